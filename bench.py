@@ -1,0 +1,268 @@
+"""Benchmark: one step = selection + sparse attention of one context-parallel shard.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step runs the whole hot path once over one synthetic batch already resident
+in HBM: ``moba_gate_topk`` then ``sparse_attn_fwd_shard`` (block mode) for the
+MoBA workloads, ``dsa_indexer_topk`` then ``sparse_attn_fwd_shard`` (token
+mode) for the DSA workload.  The default workload is the 8K-token MoBA shard
+(16 heads, D=128, last 2048 queries, blocks of 512, top-3 + own block).
+
+Printed: one JSON line.  ``value`` is effective TFLOP/s of the whole step
+(selected permitted query-key pairs x 2 x (Dqk + Dv) per second).  Extra
+fields: per-stage times (warm and with caches flushed), the roofline of the
+attention kernel, and the fp64 CPU oracle timed on a bounded sample of rows.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective sparse-attn TFLOP/s per shard (+ gate/top-k HBM GB/s), % of roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="moba_mha_8k")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-cold", action="store_true")
+    return p.parse_args()
+
+
+def permitted_bounds(w):
+    cu = w.cu_seqlens.astype(np.int64)
+    seq = w.q_seq.astype(np.int64)
+    pos = w.q_pos.astype(np.int64)
+    ok = (seq >= 0) & (seq < len(cu) - 1)
+    s = np.clip(seq, 0, len(cu) - 2)
+    lo, end = cu[s], cu[s + 1]
+    ok &= (pos >= lo) & (pos < end)
+    return lo, pos, end, ok
+
+
+def effective_pairs(w, idx):
+    """Selected permitted (query head, key) pairs of the step."""
+    lo, pos, end, ok = permitted_bounds(w)
+    idx = idx.astype(np.int64)
+    if idx.ndim == 2:
+        idx = idx[:, None, :]
+    lo_, pos_, end_ = lo[:, None, None], pos[:, None, None], end[:, None, None]
+    valid = ok[:, None, None] & (idx >= lo_) & (idx <= pos_)
+    if w.mode == "block":
+        valid &= ((idx - lo_) % w.block_size) == 0
+        n = np.minimum(np.minimum(idx + w.block_size, end_), pos_ + 1) - idx
+        pairs = np.where(valid, n, 0).sum()
+    else:
+        pairs = valid.sum()
+    if idx.shape[1] == 1:
+        pairs *= w.hq
+    return int(pairs)
+
+
+def selection_bytes(w):
+    """Algorithmic HBM bytes of the selection stage (read once, written once)."""
+    lo, pos, end, ok = permitted_bounds(w)
+    if w.mode == "block":
+        B = w.block_size
+        # blocks ending at or before the latest own-block start of each sequence
+        need = {}
+        for i in np.nonzero(ok)[0]:
+            s = int(w.q_seq[i])
+            own_start = lo[i] + ((pos[i] - lo[i]) // B) * B
+            need[s] = max(need.get(s, 0), int(own_start - lo[i]))
+        key_tokens = sum(need.values())
+        esz = 2 if w.dtype == "bf16" else 4
+        kbytes = key_tokens * w.hkv * w.dqk * esz
+        qbytes = w.n_q * w.hq * w.dqk * esz
+        ibytes = w.n_q * w.hq * (w.topk + 1) * 4
+        return {"total": kbytes + qbytes + ibytes, "keys": kbytes, "queries": qbytes,
+                "indices": ibytes}
+    n = np.where(ok, pos - lo + 1, 0)
+    logits = int(n.sum()) * 4
+    ibytes = w.n_q * w.topk * 4
+    return {"total": logits + ibytes, "logits": logits, "indices": ibytes,
+            "indexer_flops": int(n.sum()) * w.iq.shape[1] * w.iq.shape[2] * 2}
+
+
+def cpu_baseline(w, seconds):
+    """fp64 oracle on a bounded random sample of rows, one BLAS thread."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+
+    rng = np.random.default_rng(0)
+    order = rng.permutation(w.n_q)
+    done_pairs, rows_done, t_sel, t_att = 0, 0, 0.0, 0.0
+    with threadpool_limits(limits=1):
+        t_start = time.perf_counter()
+        for start in range(0, w.n_q, 8):
+            rows = np.sort(order[start:start + 8])
+            t0 = time.perf_counter()
+            if w.mode == "block":
+                gate = oracle.gate_scores(w.q[rows], w.k, w.q_pos[rows], w.q_seq[rows],
+                                          w.cu_seqlens, w.block_size)
+                idx = oracle.select_blocks(gate, w.topk)
+            else:
+                idx, _, _ = oracle.indexer_topk(w.iq[rows], w.ik, w.w[rows], w.q_pos[rows],
+                                                w.q_seq[rows], w.cu_seqlens, w.topk)
+                idx = idx[:, None, :]
+            t1 = time.perf_counter()
+            oracle.shard_forward(w.q[rows], w.k, w.value, w.q_pos[rows], w.q_seq[rows],
+                                 w.cu_seqlens, w.mode, idx, w.scale, w.block_size)
+            t2 = time.perf_counter()
+            t_sel += t1 - t0
+            t_att += t2 - t1
+            sub = _SubRows(w, rows)
+            done_pairs += effective_pairs(sub, idx)
+            rows_done += len(rows)
+            if time.perf_counter() - t_start > seconds:
+                break
+    flops = done_pairs * 2.0 * (w.dqk + w.dv)
+    return {"value": flops / (t_sel + t_att) / 1e12, "unit": "TFLOP/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{rows_done} of {w.n_q} query rows (all heads), seeded random; "
+                      f"selection {t_sel:.2f}s + attention {t_att:.2f}s in fp64 numpy",
+            "seconds": t_sel + t_att}
+
+
+class _SubRows:
+    """A view of a workload restricted to some rows (for effective_pairs)."""
+
+    def __init__(self, w, rows):
+        self.cu_seqlens, self.block_size, self.mode = w.cu_seqlens, w.block_size, w.mode
+        self.q_seq, self.q_pos, self.hq = w.q_seq[rows], w.q_pos[rows], w.hq
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each context-parallel rank's shard is independent once K/V are gathered). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import context_sparse_attention_amd as csa
+    from csa_inputs import make_workload
+
+    torch.cuda.set_device(0)
+    w = make_workload(args.workload)
+    dev = "cuda"
+
+    def up(x):
+        t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        return t.to(torch.bfloat16) if w.dtype == "bf16" else t
+
+    q, k = up(w.q), up(w.k)
+    v = k[..., : w.dv] if w.v_alias else up(w.v)
+    lay = csa.Layout(w.q_pos, w.q_seq, w.cu_seqlens)
+    if w.mode == "token":
+        iq, ik, wt = up(w.iq), up(w.ik), torch.from_numpy(w.w).to(dev)
+    out_dtype = q.dtype
+
+    def select():
+        if w.mode == "block":
+            return csa.moba_gate_topk(q, k, lay, w.block_size, w.topk)
+        return csa.dsa_indexer_topk(iq, ik, wt, lay, w.topk)
+
+    mode = csa.CSA_SEL_BLOCK if w.mode == "block" else csa.CSA_SEL_TOKEN
+
+    def attend(idx):
+        return csa.sparse_attn_fwd_shard(q, k, v, lay, mode, idx, block_size=w.block_size,
+                                         softmax_scale=w.scale, out_dtype=out_dtype)
+
+    for _ in range(args.warmup):
+        attend(select())
+    torch.cuda.synchronize()
+    idx_np = select().cpu().numpy()
+    pairs = effective_pairs(w, idx_np)
+    flops = pairs * 2.0 * (w.dqk + w.dv)
+    sel_bytes = selection_bytes(w)
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        idx = select()
+        ev[s][1].record(stream)
+        attend(idx)
+        ev[s][2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    sel_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(args.steps)]
+    att_ms = [ev[s][1].elapsed_time(ev[s][2]) for s in range(args.steps)]
+
+    cold = None
+    if not args.no_cold:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        c_sel, c_att = [], []
+        for s in range(max(5, min(args.steps, 10))):
+            flush.fill_(s & 0xFF)  # 1 GiB write evicts the 256 MB MALL and the L2s
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            idx = select()
+            e[1].record(stream)
+            attend(idx)
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            c_sel.append(e[0].elapsed_time(e[1]))
+            c_att.append(e[1].elapsed_time(e[2]))
+        del flush
+        cold = {"select_ms_median": float(np.median(c_sel)),
+                "attention_ms_median": float(np.median(c_att)),
+                "select_GBs": sel_bytes["total"] / (np.median(c_sel) * 1e-3) / 1e9,
+                "attention_TFLOPs": flops / (np.median(c_att) * 1e-3) / 1e12}
+
+    att_med = float(np.median(att_ms))
+    sel_med = float(np.median(sel_ms))
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    achieved = flops / (att_med * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": flops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) bf16 inputs of the workload's shapes)",
+        "config": {"workload": w.name, "n_q": w.n_q, "n_kv": w.n_kv, "hq": w.hq,
+                   "hkv": w.hkv, "dqk": w.dqk, "dv": w.dv, "mode": w.mode,
+                   "block_size": w.block_size, "topk": w.topk,
+                   "effective_pairs": pairs, "effective_gflop": flops / 1e9},
+        "roofline": {"kernel": "sparse_attn_fwd_shard", "bound": "mfma",
+                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None},
+        "stages": {"select_ms_median": sel_med, "attention_ms_median": att_med,
+                   "select_alg_bytes": sel_bytes["total"],
+                   "select_GBs": sel_bytes["total"] / (sel_med * 1e-3) / 1e9,
+                   "select_frac_hbm": sel_bytes["total"] / (sel_med * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                   "cold": cold},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,32 @@
+// Sparse shard attention: picks the kernel family for a request.
+#include "attention.hpp"
+
+namespace csa {
+
+size_t attn_ws_bytes(int n_q, int n_seq, int n_blocks, int mode, int hq, int hkv, int dv,
+                     int idx_width) {
+  (void)n_q; (void)n_seq; (void)n_blocks; (void)mode; (void)hq; (void)hkv; (void)dv;
+  (void)idx_width;
+  return 256;
+}
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
+  AttnKernelArgs k;
+  k.q = a.q;
+  k.k = a.k;
+  k.v = a.v;
+  k.L = a.L;
+  k.mode = a.mode;
+  k.idx_heads = a.idx_heads;
+  k.idx_width = a.idx_width;
+  k.block_size = a.block_size;
+  k.dtype = a.dtype;
+  k.out_dtype = a.out_dtype;
+  k.idx = a.idx;
+  k.scale_log2 = a.scale * 1.4426950408889634f;
+  k.out = a.out;
+  k.lse = a.lse;
+  return launch_attn_generic(k, stream);
+}
+
+}  // namespace csa

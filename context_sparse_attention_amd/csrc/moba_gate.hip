@@ -1,0 +1,296 @@
+// MoBA block gating and top-k block selection.
+//
+// MoBA issue #34 ("Question on Implementing Context Parallelism with MoBA
+// Efficient Attention", opening question): each query ranks key blocks by a
+// gating score computed from Q x K^T and keeps its top-k blocks; under context
+// parallelism the local queries rank blocks of the gathered keys.  The score
+// of a block is the query's dot product with the block's mean key (the plain
+// reading of "Q x K^T" at block granularity: q . mean(k) = mean(q . k)).
+//
+// Three kernels:
+//   k_moba_need  - per packed sequence, the highest own block of any local row
+//                  (blocks at or after it are never candidates, so they are
+//                  not pooled);
+//   k_moba_pool  - fp32 block means, one workgroup per (block, 32-key chunk),
+//                  coalesced 16-byte key loads; the last chunk to finish
+//                  reduces the chunk sums in fixed order (deterministic);
+//   k_moba_gate  - one thread per (row, query head): fp32 scores over the
+//                  row's candidate blocks, register top-k (score desc, ties to
+//                  the lower block), own block appended, ascending output.
+#include <float.h>
+
+#include "common.hpp"
+
+namespace csa {
+
+namespace {
+
+constexpr int kPoolThreads = 256;
+constexpr int kPoolChunk = 32;  // keys per pooling workgroup
+constexpr int kGateThreads = 256;
+
+struct MobaWs {
+  BlockTable bt;
+  int32_t* need;    // [n_seq]
+  int32_t* arrive;  // [n_blocks]
+  float* partial;   // [n_blocks, n_chunks, hkv*d]
+  float* mu;        // [n_blocks, hkv*d]
+};
+
+MobaWs carve_moba(void* base, int n_seq, int n_blocks, int hkv, int d, int block_size) {
+  Carver c(base);
+  MobaWs w;
+  w.bt.blk_off = c.take<int32_t>(n_seq + 1);
+  w.bt.blocks = c.take<int2>(n_blocks);
+  w.bt.blk_seq = c.take<int32_t>(n_blocks);
+  // need[] and arrive[] are adjacent so one fill clears both
+  w.need = c.take<int32_t>((size_t)n_seq + n_blocks);
+  w.arrive = w.need + n_seq;
+  const int n_chunks = (block_size + kPoolChunk - 1) / kPoolChunk;
+  w.partial = c.take<float>((size_t)n_blocks * n_chunks * hkv * d);
+  w.mu = c.take<float>((size_t)n_blocks * hkv * d);
+  return w;
+}
+
+size_t carve_bytes(int n_seq, int n_blocks, int hkv, int d, int block_size) {
+  Carver c(nullptr);
+  const int n_chunks = (block_size + kPoolChunk - 1) / kPoolChunk;
+  c.take<int32_t>(n_seq + 1);
+  c.take<int2>(n_blocks);
+  c.take<int32_t>(n_blocks);
+  c.take<int32_t>((size_t)n_seq + n_blocks);
+  c.take<float>((size_t)n_blocks * n_chunks * hkv * d);
+  c.take<float>((size_t)n_blocks * hkv * d);
+  return align_up(c.used, 256);
+}
+
+__global__ void k_moba_need(DevLayout L, int block_size, const int32_t* __restrict__ blk_off,
+                            int32_t* __restrict__ need) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= L.n_q) return;
+  const RowKeys r = row_keys(L, i);
+  if (!r.valid) return;
+  const int own = blk_off[r.seq] + (r.hi - r.lo) / block_size;
+  atomicMax(&need[r.seq], own);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kPoolThreads) void k_moba_pool(View k, BlockTable bt,
+                                                            const int32_t* __restrict__ need,
+                                                            int32_t* __restrict__ arrive,
+                                                            float* __restrict__ partial,
+                                                            float* __restrict__ mu,
+                                                            int n_chunks) {
+  const int b = blockIdx.x / n_chunks;
+  const int chunk = blockIdx.x % n_chunks;
+  const int seq = bt.blk_seq[b];
+  if (b >= need[seq]) return;  // never a candidate of any local row
+  const int2 blk = bt.blocks[b];
+  const int n_my_chunks = (blk.y + kPoolChunk - 1) / kPoolChunk;
+  if (chunk >= n_my_chunks) return;
+
+  const int hd = k.h * k.d;  // elements of one key row
+  const int groups = hd / 8;
+  const int lanes_k = groups >= kPoolThreads ? 1 : kPoolThreads / groups;
+  const int t0 = blk.x + chunk * kPoolChunk;
+  const int t1 = min(blk.x + blk.y, t0 + kPoolChunk);
+
+  __shared__ float s_red[kPoolThreads * 8];
+  __shared__ int s_last;
+  for (int base = 0; base < groups; base += kPoolThreads / lanes_k) {
+    const int span = min(groups - base, kPoolThreads / lanes_k);
+    const int tid = threadIdx.x;
+    const int eg = base + tid % span;
+    const int kl = tid / span;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (kl < lanes_k) {
+      const int e = eg * 8;
+      const int hh = e / k.d, dd = e % k.d;
+      for (int t = t0 + kl; t < t1; t += lanes_k) {
+        float x[8];
+        load8(elem_ptr<T>(k, t, hh) + dd, x);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += x[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s_red[(kl * span + tid % span) * 8 + j] = acc[j];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < span * 8; e += kPoolThreads) {
+      float s = 0.f;
+      for (int l = 0; l < lanes_k; ++l) s += s_red[(l * span) * 8 + e];
+      partial[((size_t)b * n_chunks + chunk) * hd + base * 8 + e] = s;
+    }
+    __syncthreads();
+  }
+
+  // the last chunk of this block to arrive reduces the chunk sums in order
+  __threadfence();
+  if (threadIdx.x == 0) s_last = (atomicAdd(&arrive[b], 1) == n_my_chunks - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const float inv = 1.0f / (float)blk.y;
+  for (int e = threadIdx.x; e < hd; e += kPoolThreads) {
+    float s = 0.f;
+    for (int c = 0; c < n_my_chunks; ++c)
+      s += partial[((size_t)b * n_chunks + c) * hd + e];
+    mu[(size_t)b * hd + e] = s * inv;
+  }
+}
+
+// Bitonic sort of (key, val) pairs ascending by key; N a power of two, fully unrolled.
+template <int N>
+__device__ inline void sort_pairs_asc(int* key, float* val) {
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool up = ((i & size) == 0);
+          const bool swap = up ? (key[i] > key[j]) : (key[i] < key[j]);
+          if (swap) {
+            const int tk = key[i]; key[i] = key[j]; key[j] = tk;
+            const float tv = val[i]; val[i] = val[j]; val[j] = tv;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int KMAX>
+__global__ __launch_bounds__(kGateThreads) void k_moba_gate(View q, DevLayout L, int hkv,
+                                                            int block_size, int topk,
+                                                            BlockTable bt,
+                                                            const float* __restrict__ mu,
+                                                            int32_t* __restrict__ idx,
+                                                            float* __restrict__ score) {
+  const int64_t pair = (int64_t)blockIdx.x * kGateThreads + threadIdx.x;
+  const int hq = q.h;
+  if (pair >= (int64_t)L.n_q * hq) return;
+  const int i = (int)(pair / hq);
+  const int h = (int)(pair % hq);
+  const int g = h / (hq / hkv);
+  const int width = topk + 1;
+  int32_t* out = idx + pair * width;
+  float* out_s = score ? score + pair * width : nullptr;
+
+  const RowKeys r = row_keys(L, i);
+  if (!r.valid) {
+    for (int t = 0; t < width; ++t) {
+      out[t] = -1;
+      if (out_s) out_s[t] = -INFINITY;
+    }
+    return;
+  }
+  const int j_own = (r.hi - r.lo) / block_size;
+  const int first = bt.blk_off[r.seq];
+  const int own = first + j_own;
+
+  float best_s[KMAX];
+  int best_b[KMAX];
+#pragma unroll
+  for (int t = 0; t < KMAX; ++t) {
+    best_s[t] = -INFINITY;
+    best_b[t] = INT32_MAX;
+  }
+  const int d = q.d;
+  const T* qp = elem_ptr<T>(q, i, h);
+  const int hd = hkv * d;
+  for (int c = 0; c < j_own; ++c) {
+    const float* m = mu + (size_t)(first + c) * hd + (size_t)g * d;
+    float s = 0.f;
+    for (int d8 = 0; d8 < d; d8 += 8) {
+      float x[8];
+      load8(qp + d8, x);
+      const float4 m0 = *reinterpret_cast<const float4*>(m + d8);
+      const float4 m1 = *reinterpret_cast<const float4*>(m + d8 + 4);
+      s = fmaf(x[0], m0.x, s); s = fmaf(x[1], m0.y, s);
+      s = fmaf(x[2], m0.z, s); s = fmaf(x[3], m0.w, s);
+      s = fmaf(x[4], m1.x, s); s = fmaf(x[5], m1.y, s);
+      s = fmaf(x[6], m1.z, s); s = fmaf(x[7], m1.w, s);
+    }
+    // insert: strictly greater moves ahead, so an equal score keeps the earlier block
+    float cs = s;
+    int cb = first + c;
+#pragma unroll
+    for (int t = 0; t < KMAX; ++t) {
+      if (t < topk && cs > best_s[t]) {
+        const float ts = best_s[t];
+        const int tb = best_b[t];
+        best_s[t] = cs;
+        best_b[t] = cb;
+        cs = ts;
+        cb = tb;
+      }
+    }
+  }
+  // unfilled entries keep the INT32_MAX sentinel and sort last (a NaN score,
+  // possible only for non-finite inputs, is never inserted)
+  sort_pairs_asc<KMAX>(best_b, best_s);
+  int kept = 0;
+#pragma unroll
+  for (int u = 0; u < KMAX; ++u) {
+    if (best_b[u] != INT32_MAX) {
+      out[u] = bt.blocks[best_b[u]].x;
+      if (out_s) out_s[u] = best_s[u];
+      ++kept;
+    }
+  }
+  int t = kept;
+  out[t] = bt.blocks[own].x;
+  if (out_s) out_s[t] = INFINITY;
+  for (++t; t < width; ++t) {
+    out[t] = -1;
+    if (out_s) out_s[t] = -INFINITY;
+  }
+}
+
+template <typename T, int KMAX>
+hipError_t launch_gate_k(const MobaGateArgs& a, const MobaWs& w, hipStream_t stream) {
+  const int64_t pairs = (int64_t)a.L.n_q * a.q.h;
+  const int grid = (int)((pairs + kGateThreads - 1) / kGateThreads);
+  hipLaunchKernelGGL((k_moba_gate<T, KMAX>), dim3(grid), dim3(kGateThreads), 0, stream, a.q,
+                     a.L, a.k.h, a.block_size, a.topk, w.bt, w.mu, a.idx, a.score);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_typed(const MobaGateArgs& a, hipStream_t stream) {
+  const int n_seq = a.L.n_seq;
+  MobaWs w = carve_moba(a.ws, n_seq, a.n_blocks, a.k.h, a.k.d, a.block_size);
+  hipError_t e = launch_block_table(a.L.cu, n_seq, a.block_size, a.n_blocks, w.bt, w.need,
+                                    (int64_t)n_seq + a.n_blocks, stream);
+  if (e != hipSuccess) return e;
+  if (a.L.n_q == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_moba_need, dim3((a.L.n_q + 255) / 256), dim3(256), 0, stream, a.L,
+                     a.block_size, w.bt.blk_off, w.need);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int n_chunks = (a.block_size + kPoolChunk - 1) / kPoolChunk;
+  if (a.n_blocks > 0) {
+    hipLaunchKernelGGL((k_moba_pool<T>), dim3(a.n_blocks * n_chunks), dim3(kPoolThreads), 0,
+                       stream, a.k, w.bt, w.need, w.arrive, w.partial, w.mu, n_chunks);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (a.topk <= 4) return launch_gate_k<T, 4>(a, w, stream);
+  if (a.topk <= 8) return launch_gate_k<T, 8>(a, w, stream);
+  if (a.topk <= 16) return launch_gate_k<T, 16>(a, w, stream);
+  return launch_gate_k<T, 32>(a, w, stream);
+}
+
+}  // namespace
+
+size_t moba_gate_ws_bytes(int n_seq, int n_blocks, int hkv, int d, int block_size) {
+  return carve_bytes(n_seq, n_blocks, hkv, d, block_size);
+}
+
+hipError_t launch_moba_gate(const MobaGateArgs& a, hipStream_t stream) {
+  if (a.dtype == CSA_BF16) return launch_typed<__bf16>(a, stream);
+  return launch_typed<float>(a, stream);
+}
+
+}  // namespace csa

@@ -1,0 +1,216 @@
+/*
+ * csa.h - C ABI of the context-parallel sparse-attention shard library (libcsa.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * One call computes one step of the attention forward of one context-parallel
+ * rank's shard: local queries at their global token positions attend to the
+ * full gathered key/value stream, over key chunks picked per query either by
+ * MoBA-style block gating or by a DSA-style token indexer, and per-chunk
+ * softmax summaries (m, l, z) are merged by rescaling to the larger maximum.
+ *
+ * Sources (pages, by title and section):
+ *  [MoBA#34]  MoBA issue #34 "Question on Implementing Context Parallelism with
+ *             MoBA Efficient Attention", opening question: top-k key blocks per
+ *             query from gating scores Q x K^T, local Q against gathered K.
+ *  [CPA]      "Context parallel attention: exchange keys and merge softmax
+ *             globally": global positions decide masks; packed sequences keep
+ *             their boundaries; chunk summary (m, l, z) and its rescaled merge;
+ *             neutral summary for all-masked chunks; explicit convention for a
+ *             query with no permitted key; zigzag layouts keep global positions.
+ *  [MLM#4878] Megatron-LM issue #4878 "[Feature-request] Context Parallel
+ *             support for DSAttention", "Strategy: allgather CP mode": local Q
+ *             against gathered K/V with the causal diagonal shifted by the
+ *             rank's offset; top-k indices in global-sequence coordinates; a
+ *             sparse kernel that iterates only over the top-k indices.
+ *  [MLM#3674] Megatron-LM PR #3674 "[1/2] Enable DSA CP, THD with absorbed
+ *             MLA", Description and sequence diagram: an indexer picks the
+ *             top-k key tokens of each query; packed THD masking from sequence
+ *             metadata; absorbed MLA (value = latent part of the key).
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer is DEVICE memory owned by the caller unless marked (host).
+ *    The library allocates nothing, keeps no pointer after return, and never
+ *    writes an input.  Work is enqueued on `stream` (a hipStream_t; NULL is the
+ *    default stream) and the call returns without synchronising.
+ *  - All argument checks run on the host before anything is enqueued.  A
+ *    failed check returns a non-OK status, enqueues nothing and sets the text
+ *    returned by csa_last_error() (per thread).  A failed HIP launch returns
+ *    CSA_ERR_HIP.  No C++ exception crosses this interface.
+ *  - Row i of the shard has global position q_pos[i] inside packed sequence
+ *    q_seq[i] = [cu_seqlens[s], cu_seqlens[s+1]).  It may attend to the keys
+ *    [lo_i, pos_i] with lo_i = cu_seqlens[q_seq[i]] [CPA, MLM#4878].  A row
+ *    whose sequence id is out of range or whose position lies outside its
+ *    sequence has no permitted key: it selects nothing, its output is 0 and
+ *    its log-sum-exp is -inf [CPA].  Such rows are not an error.
+ *  - Index values are int32 global key positions [MLM#4878], ascending within
+ *    a row, padded with -1 at the end.  An index slot whose chunk has no
+ *    permitted key of the row (including -1) is neutral; it is never read.
+ *  - Query head h reads key/value head h / (Hq / Hkv) (grouped-query
+ *    attention); Hq must be a multiple of Hkv.
+ *  - Results are bitwise reproducible run to run (no floating-point atomics).
+ *  - Tensors: element (t, h, e) lives at data + t*stride_n + h*stride_h + e
+ *    (strides in elements).  The last dimension is contiguous, `data` is
+ *    16-byte aligned and both strides are multiples of 16 bytes.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_INVALID_ARG = 1, /* a shape, dtype, stride, pointer or range check failed */
+  CSA_ERR_UNSUPPORTED = 2, /* a valid request outside what the kernels implement   */
+  CSA_ERR_WORKSPACE = 3,   /* workspace pointer missing, misaligned or too small  */
+  CSA_ERR_HIP = 4          /* the HIP runtime rejected a launch                    */
+} csa_status;
+
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
+
+typedef enum {
+  CSA_SEL_BLOCK = 0, /* index slots are block starts (MoBA) */
+  CSA_SEL_TOKEN = 1  /* index slots are key tokens (DSA)    */
+} csa_sel_mode;
+
+/* A [n, h, d] tensor view.  `data` is device memory; the struct itself is host memory. */
+typedef struct {
+  const void* data;
+  int32_t dtype; /* csa_dtype */
+  int64_t n;
+  int32_t h;
+  int32_t d;
+  int64_t stride_n; /* elements */
+  int64_t stride_h; /* elements */
+} csa_tensor3;
+
+/* Shard layout.  The struct is host memory. */
+typedef struct {
+  int32_t n_q;                    /* local query rows                                  */
+  int32_t n_kv;                   /* tokens in the gathered key/value stream           */
+  const int32_t* q_pos;           /* [n_q] global position of each row (device)        */
+  const int32_t* q_seq;           /* [n_q] packed-sequence id of each row (device)     */
+  int32_t n_seq;                  /* packed sequences (1 for an unpacked stream)       */
+  const int32_t* cu_seqlens;      /* [n_seq+1] sequence starts, last = n_kv (device)   */
+  const int32_t* cu_seqlens_host; /* (host) the same values; used to size and check    */
+} csa_layout;
+
+/* ---------------------------------------------------------------------------------
+ * moba_gate_topk - MoBA block gating and top-k block selection [MoBA#34].
+ *
+ * Blocks are cut per packed sequence from its first token, block_size tokens
+ * each (the last block of a sequence may be shorter) [CPA: packed boundaries].
+ * The score of block b for row i, query head h is q[i,h] . mean(k[t, kv(h)] for
+ * t in b), in fp32 from an fp32 block mean.  Candidates of row i are the blocks
+ * of its sequence that end at or before the start of the row's own block (the
+ * block holding pos_i).  Each (row, head) keeps the min(topk, #candidates)
+ * best candidates (score descending, ties to the lower block) and then its own
+ * block.
+ *
+ *  q   [n_q, Hq, D]  bf16 or f32;  k [n_kv, Hkv, D] same dtype;  D <= 256.
+ *  idx [n_q, Hq, topk+1] int32 out (contiguous): global start position of each
+ *      selected block, ascending (so the own block is last), -1 padded.
+ *  score [n_q, Hq, topk+1] f32 out, nullable: the gate score of each selected
+ *      block; +inf for the own block, -inf for padding.
+ *  topk in [0, 32].  ws: at least moba_gate_topk_workspace_size() bytes,
+ *  256-byte aligned.
+ * ------------------------------------------------------------------------------- */
+size_t moba_gate_topk_workspace_size(const csa_layout* L, int32_t hkv, int32_t d,
+                                     int32_t block_size);
+csa_status moba_gate_topk(const csa_tensor3* q, const csa_tensor3* k, const csa_layout* L,
+                          int32_t block_size, int32_t topk, int32_t* idx, float* score,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * dsa_indexer_topk - DSA-style token indexer and top-k token selection
+ * [MLM#3674 Description, MLM#4878 Strategy].
+ *
+ * Logit of key j for row i: L[i,j] = sum_h w[i,h] * max(0, iq[i,h] . ik[j]),
+ * products and sums in fp32, over the permitted keys j in [lo_i, pos_i].
+ * Each row keeps the min(topk, pos_i - lo_i + 1) largest logits, ties to the
+ * lower key index.
+ *
+ *  iq [n_q, H_I, D_I] bf16 or f32;  ik [n_kv, 1, D_I] same dtype;  D_I <= 128,
+ *     a multiple of 8.
+ *  w  [n_q, H_I] f32 (row stride w_stride_n elements, H_I contiguous).
+ *  idx [n_q, topk] int32 out (contiguous): selected global key positions,
+ *     ascending, -1 padded.
+ *  score [n_q, topk] f32 out, nullable: the logit of each selected key, -inf
+ *     for padding.
+ *  topk >= 1.  ws: at least dsa_indexer_topk_workspace_size() bytes (it holds
+ *  the fp32 logits of the permitted keys), 256-byte aligned.
+ * ------------------------------------------------------------------------------- */
+size_t dsa_indexer_topk_workspace_size(const csa_layout* L, int32_t topk);
+csa_status dsa_indexer_topk(const csa_tensor3* iq, const csa_tensor3* ik, const float* w,
+                            int64_t w_stride_n, const csa_layout* L, int32_t topk,
+                            int32_t* idx, float* score, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * sparse_attn_fwd_shard - attention of the shard's rows over their selected
+ * key chunks [MLM#4878 "iterate only over topk indices", CPA summary merge].
+ *
+ * For row i, query head h, the selected keys are the multiset union over the
+ * slots of idx row (i, h) (or (i, 0) when idx_heads == 1) of each slot's
+ * permitted keys:
+ *   CSA_SEL_TOKEN: slot j selects key j when lo_i <= j <= pos_i;
+ *   CSA_SEL_BLOCK: slot s selects the block of the row's sequence starting at
+ *     s when lo_i <= s <= pos_i and (s - lo_i) is a multiple of block_size;
+ *     its keys are [s, min(s + block_size, sequence end)) cut to [lo_i, pos_i].
+ * Slots are expected to be distinct; a repeated slot counts its keys again.
+ * With logits x = softmax_scale * q . k, the output is
+ *   out[i,h] = sum_j exp(x_j - M) v_j / sum_j exp(x_j - M),  lse = M + ln(sum),
+ * computed as a merge of per-chunk (m, l, z) summaries in fp32 with bf16
+ * products for bf16 inputs.  No selected key: out = 0, lse = -inf [CPA].
+ *
+ *  q [n_q, Hq, Dqk], k [n_kv, Hkv, Dqk], v [n_kv, Hkv, Dv]: same dtype.  v may
+ *     alias k (absorbed MLA: v.data = k.data, v.d = 512 < k.d = 576).
+ *     Dqk <= 576, Dv <= 512.
+ *  idx [n_q, idx_heads, idx_width] int32 (contiguous); idx_heads is 1 or Hq.
+ *  out [n_q, Hq, Dv] (contiguous) in out_dtype (CSA_F32 or CSA_BF16, rounded
+ *     to nearest even); lse [n_q, Hq] f32, nullable (natural-log units).
+ *  ws: at least sparse_attn_fwd_shard_workspace_size() bytes, 256-byte aligned.
+ * ------------------------------------------------------------------------------- */
+size_t sparse_attn_fwd_shard_workspace_size(const csa_layout* L, int32_t mode, int32_t hq,
+                                            int32_t hkv, int32_t dv, int32_t idx_width,
+                                            int32_t block_size);
+csa_status sparse_attn_fwd_shard(const csa_tensor3* q, const csa_tensor3* k,
+                                 const csa_tensor3* v, const csa_layout* L, int32_t mode,
+                                 const int32_t* idx, int32_t idx_heads, int32_t idx_width,
+                                 int32_t block_size, float softmax_scale, void* out,
+                                 int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * summary_merge - merge P chunk summaries per row [CPA, summary paragraph].
+ *
+ * Part p of row r is (m[p,r], l[p,r], z[p,r,:]) with m in natural-log units.
+ * Parts merge in ascending p: m = max(m_a, m_b); each side is scaled by
+ * exp(m_side - m), a side with m = -inf by 0.  The neutral summary is
+ * (-inf, 0, 0); merging two neutral summaries gives the neutral summary
+ * without NaN [CPA, neutral-summary paragraph].
+ *
+ *  m, l [n_parts, n_rows] f32;  z [n_parts, n_rows, dv] f32 (all contiguous).
+ *  m_out, l_out [n_rows], z_out [n_rows, dv]: merged summary, f32 (nullable
+ *     together).
+ *  o_out [n_rows, dv] in o_dtype and lse_out [n_rows] f32: finalized output
+ *     o = z / l and lse = m + ln l; o = 0 and lse = -inf when l = 0 (nullable
+ *     together).
+ * ------------------------------------------------------------------------------- */
+csa_status summary_merge(int32_t n_parts, int64_t n_rows, int32_t dv, const float* m,
+                         const float* l, const float* z, float* m_out, float* l_out,
+                         float* z_out, void* o_out, int32_t o_dtype, float* lse_out,
+                         void* stream);
+
+/* Text of the last non-OK status on the calling thread ("" if none). */
+const char* csa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H */

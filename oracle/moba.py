@@ -99,9 +99,8 @@ def gate_scores(q, k, q_pos, q_seq, cu_seqlens, block_size):
         own[i], first[i], n_cand[i] = c
         if n_cand[i] == 0:
             continue
-        cand_mu = mu[first[i]:first[i] + n_cand[i]]  # [nc, Hkv, D]
-        for h in range(hq):
-            scores[i, h, :n_cand[i]] = cand_mu[:, kv_of_head[h], :] @ q64[i, h]
+        cand_mu = mu[first[i]:first[i] + n_cand[i]][:, kv_of_head, :]  # [nc, Hq, D]
+        scores[i, :, :n_cand[i]] = np.einsum("chd,hd->hc", cand_mu, q64[i])
     return {"scores": scores, "n_cand": n_cand, "first": first, "own": own,
             "starts": starts}
 
@@ -119,13 +118,10 @@ def select_blocks(gate, topk):
         nc = int(n_cand[i])
         if nc < 0:
             continue
-        for h in range(hq):
-            if nc > 0:
-                # stable sort on the negated score: equal scores keep block order
-                order = np.argsort(-scores[i, h, :nc], kind="stable")[:min(topk, nc)]
-                blocks = np.sort(order) + gate["first"][i]
-            else:
-                blocks = np.zeros(0, np.int64)
-            blocks = np.append(blocks, gate["own"][i])
-            idx[i, h, :len(blocks)] = starts[blocks]
+        kept = min(topk, nc)
+        # stable sort on the negated score: equal scores keep block order
+        order = np.argsort(-scores[i, :, :nc], axis=-1, kind="stable")[:, :kept]
+        blocks = np.sort(order, axis=-1) + gate["first"][i]  # [Hq, kept]
+        idx[i, :, :kept] = starts[blocks]
+        idx[i, :, kept] = starts[gate["own"][i]]
     return idx
