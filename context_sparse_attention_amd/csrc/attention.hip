@@ -5,8 +5,8 @@ namespace csa {
 
 size_t attn_ws_bytes(int n_q, int n_seq, int n_blocks, int mode, int hq, int hkv, int dv,
                      int idx_width) {
-  (void)n_q; (void)n_seq; (void)n_blocks; (void)mode; (void)hq; (void)hkv; (void)dv;
-  (void)idx_width;
+  if (mode == CSA_SEL_BLOCK)
+    return attn_block_mfma_ws_bytes(n_q, n_seq, n_blocks, hq, hkv, dv, idx_width);
   return 256;
 }
 
@@ -26,6 +26,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
   k.scale_log2 = a.scale * 1.4426950408889634f;
   k.out = a.out;
   k.lse = a.lse;
+  if (attn_block_mfma_supported(k)) return launch_attn_block_mfma(k, a.n_blocks, a.ws, stream);
   return launch_attn_generic(k, stream);
 }
 

@@ -1,0 +1,657 @@
+// Block-mode sparse shard attention on the matrix cores (bf16 MFMA, gfx950).
+//
+// MoBA issue #34 (opening question): every query attends only to its own
+// top-k key blocks.  With independent per-query, per-head choices a
+// query-tile-centric kernel would visit the union of its rows' blocks, so the
+// selection is inverted instead: every fully permitted block slot of every
+// (row, head) is appended to the list of its (key head, block); each list is
+// cut into tiles of 128 gathered queries that share the block's keys, and the
+// tile kernel computes one (m, l, z) chunk summary per slot ("Context parallel
+// attention: exchange keys and merge softmax globally", chunk summary).  The
+// own block, partially masked by the causal diagonal at the row's global
+// position (Megatron-LM issue #4878, shifted causal diagonal), is computed by a
+// diagonal kernel over tiles of consecutive rows, which then merges the slot
+// summaries of each (row, head) by rescaling to the larger maximum and
+// finalizes the output (neutral summary and zero-output convention for rows
+// with no permitted key: same article, masking paragraph).
+//
+// Kernels (in stream order):
+//   k_block_table  (layout.hip) block table + zeroed list counters
+//   k_bm_count     per (row, head): count full block slots per list, own multiplicity
+//   k_bm_scan      one workgroup: list offsets, query tiles, diagonal row tiles
+//   k_bm_fill      per (row, head): scatter slot ids into the lists
+//   k_bm_tiles     persistent: per query tile, S^T = K Q^T and O^T = V^T P^T on
+//                  LDS-staged key/value tiles (32x32x16 bf16 MFMA), fp32 online
+//                  softmax in registers, one fp32 summary per slot
+//   k_bm_diag      persistent: own-block attention with the causal mask, merge
+//                  with the slot summaries in slot order, finalize
+//
+// Layout of the math: the MFMA computes S^T (keys x queries) so that a lane
+// owns one query and its scores sit in that lane's registers; the softmax row
+// reduction is then in-lane plus one cross-half exchange, and P^T is already
+// in the B-operand layout of the O^T = V^T P^T product (the contraction index
+// is permuted consistently on both operands).  V is stored transposed in LDS.
+#include "attention.hpp"
+
+namespace csa {
+
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr int kTN = 64;                  // keys per LDS tile
+constexpr int kQW = 32;                  // queries per wave
+constexpr int kWaves = 4;
+constexpr int kTM = kQW * kWaves;        // queries per workgroup tile
+constexpr int kThreads = kWaves * kWave;
+constexpr int kScanThreads = 1024;
+constexpr float kLn2 = 0.69314718055994531f;
+
+struct BmWs {
+  BlockTable bt;
+  int32_t* counts;    // [n_lists]
+  int32_t* fill;      // [n_lists], adjacent to counts (zeroed together)
+  int32_t* list_off;  // [n_lists + 1]
+  int2* tiles;        // [max_tiles]  (list, first entry)
+  int32_t* totals;    // [4]  query tiles, diagonal tiles
+  int2* diag;         // [n_q + 1]  (first row, own block or -1)
+  int32_t* own_mult;  // [n_q * hq]
+  int32_t* entries;   // [n_q * hq * W]  flat slot ids
+  float2* part_ml;    // [n_q * hq * W]  (m in log2 units, l)
+  float* part_z;      // [n_q * hq * W * D]
+};
+
+int64_t max_query_tiles(int64_t slots, int64_t n_lists) { return slots / kTM + n_lists + 1; }
+
+template <bool CARVE>
+size_t carve_bm(void* base, int n_q, int n_seq, int n_blocks, int hq, int hkv, int dv, int W,
+                BmWs* w) {
+  Carver c(base);
+  const int64_t n_lists = (int64_t)hkv * n_blocks;
+  const int64_t slots = (int64_t)n_q * hq * W;
+  BmWs t;
+  t.bt.blk_off = c.take<int32_t>(n_seq + 1);
+  t.bt.blocks = c.take<int2>(n_blocks);
+  t.bt.blk_seq = c.take<int32_t>(n_blocks);
+  t.counts = c.take<int32_t>(2 * n_lists);
+  t.fill = t.counts + n_lists;
+  t.list_off = c.take<int32_t>(n_lists + 1);
+  t.tiles = c.take<int2>(max_query_tiles(slots, n_lists));
+  t.totals = c.take<int32_t>(4);
+  t.diag = c.take<int2>(n_q + 1);
+  t.own_mult = c.take<int32_t>((size_t)n_q * hq);
+  t.entries = c.take<int32_t>(slots);
+  t.part_ml = c.take<float2>(slots);
+  t.part_z = c.take<float>(slots * dv);
+  if (CARVE) *w = t;
+  return align_up(c.used, 256);
+}
+
+__device__ inline const int32_t* slot_row(const AttnKernelArgs& a, int i, int h) {
+  return a.idx + ((int64_t)i * a.idx_heads + (a.idx_heads == 1 ? 0 : h)) * a.idx_width;
+}
+
+// Slot classes: 0 = no permitted key, 1 = full block strictly before pos_i, 2 = own block.
+__device__ inline int slot_class(int s, const RowKeys& r, int B) {
+  if (s < r.lo || s > r.hi || (s - r.lo) % B) return 0;
+  return (s + B - 1 < r.hi) ? 1 : 2;
+}
+
+__global__ void k_bm_count(AttnKernelArgs a, BlockTable bt, int n_blocks,
+                           int32_t* __restrict__ counts, int32_t* __restrict__ own_mult) {
+  const int64_t pair = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int hq = a.q.h;
+  if (pair >= (int64_t)a.L.n_q * hq) return;
+  const int i = (int)(pair / hq), h = (int)(pair % hq);
+  const int g = h / (hq / a.k.h);
+  const RowKeys r = row_keys(a.L, i);
+  int mult = 0;
+  if (r.valid) {
+    const int32_t* slots = slot_row(a, i, h);
+    const int base = g * n_blocks + bt.blk_off[r.seq];
+    for (int s = 0; s < a.idx_width; ++s) {
+      const int st = slots[s];
+      const int c = slot_class(st, r, a.block_size);
+      if (c == 1) atomicAdd(&counts[base + (st - r.lo) / a.block_size], 1);
+      else if (c == 2) ++mult;
+    }
+  }
+  own_mult[pair] = mult;
+}
+
+__global__ void k_bm_fill(AttnKernelArgs a, BlockTable bt, int n_blocks,
+                          const int32_t* __restrict__ list_off, int32_t* __restrict__ fill,
+                          int32_t* __restrict__ entries) {
+  const int64_t pair = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int hq = a.q.h;
+  if (pair >= (int64_t)a.L.n_q * hq) return;
+  const int i = (int)(pair / hq), h = (int)(pair % hq);
+  const int g = h / (hq / a.k.h);
+  const RowKeys r = row_keys(a.L, i);
+  if (!r.valid) return;
+  const int32_t* slots = slot_row(a, i, h);
+  const int base = g * n_blocks + bt.blk_off[r.seq];
+  for (int s = 0; s < a.idx_width; ++s) {
+    const int st = slots[s];
+    if (slot_class(st, r, a.block_size) != 1) continue;
+    const int list = base + (st - r.lo) / a.block_size;
+    const int at = atomicAdd(&fill[list], 1);
+    entries[list_off[list] + at] = (int32_t)(pair * a.idx_width + s);
+  }
+}
+
+// Workgroup-wide inclusive scan (kScanThreads threads).
+__device__ int scan_incl(int x, int* s_wave, int* s_total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  if (lane == kWave - 1) s_wave[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < kScanThreads / kWave; ++w) {
+    if (w < wave) before += s_wave[w];
+    all += s_wave[w];
+  }
+  __syncthreads();
+  *s_total = all;
+  return x + before;
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_bm_scan(AttnKernelArgs a, BlockTable bt,
+                                                          int n_lists, int rows_per_diag,
+                                                          const int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ list_off,
+                                                          int2* __restrict__ tiles,
+                                                          int32_t* __restrict__ totals,
+                                                          int2* __restrict__ diag) {
+  __shared__ int s_wave[kScanThreads / kWave];
+  int carry = 0, tcarry = 0, tot = 0;
+  for (int base = 0; base < n_lists; base += kScanThreads) {
+    const int l = base + threadIdx.x;
+    const int c = l < n_lists ? counts[l] : 0;
+    const int incl = scan_incl(c, s_wave, &tot);
+    const int ctot = tot;
+    const int nt = (c + kTM - 1) / kTM;
+    const int tincl = scan_incl(nt, s_wave, &tot);
+    if (l < n_lists) {
+      list_off[l] = carry + incl - c;
+      const int first = tcarry + tincl - nt;
+      for (int j = 0; j < nt; ++j) tiles[first + j] = make_int2(l, j * kTM);
+    }
+    carry += ctot;
+    tcarry += tot;
+  }
+  if (threadIdx.x == 0) {
+    list_off[n_lists] = carry;
+    totals[0] = tcarry;
+  }
+  // diagonal row tiles: split at own-block changes and every rows_per_diag rows
+  int dcarry = 0;
+  const int B = a.block_size;
+  for (int base = 0; base < a.L.n_q; base += kScanThreads) {
+    const int i = base + threadIdx.x;
+    int key = -1, prev = -1;
+    bool flag = false;
+    if (i < a.L.n_q) {
+      const RowKeys r = row_keys(a.L, i);
+      key = r.valid ? bt.blk_off[r.seq] + (r.hi - r.lo) / B : -1;
+      if (i > 0) {
+        const RowKeys rp = row_keys(a.L, i - 1);
+        prev = rp.valid ? bt.blk_off[rp.seq] + (rp.hi - rp.lo) / B : -1;
+      }
+      flag = (i == 0) || (key != prev) || (i % rows_per_diag == 0);
+    }
+    const int incl = scan_incl(flag ? 1 : 0, s_wave, &tot);
+    if (flag) diag[dcarry + incl - 1] = make_int2(i, key);
+    dcarry += tot;
+  }
+  if (threadIdx.x == 0) {
+    diag[dcarry] = make_int2(a.L.n_q, -1);
+    totals[1] = dcarry;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA tile machinery
+// ---------------------------------------------------------------------------
+
+// K tile [kTN][D] bf16 in 16-byte units, unit u of row r stored at u ^ (r & 7):
+// eight consecutive rows read at one column hit eight distinct bank groups.
+template <int D>
+__device__ inline int k_off(int r, int u) {
+  return r * D + ((u ^ (r & 7)) << 3);
+}
+// V^T tile [D][kTN] bf16 in 4-key groups, group q of row r stored at
+// q ^ ((r + (r >> 4)) & 15): conflict-free both for the transposing writes
+// (rows 8 apart) and for the operand reads (16 consecutive rows).
+__device__ inline int vt_off(int r, int q) {
+  return r * kTN + ((q ^ ((r + (r >> 4)) & 15)) << 2);
+}
+
+template <int D>
+struct Lds {
+  __bf16 k[2][kTN * D];
+  __bf16 vt[2][D * kTN];
+};
+
+// Global -> register staging of one key/value tile (all threads).  The staging
+// registers are ext-vector values so that they stay in VGPRs.
+template <int D>
+struct Stage {
+  static constexpr int kUnits = D / 8;                  // 16-byte units per row
+  static constexpr int kRowsPerPass = kThreads / kUnits;
+  static constexpr int kPasses = kTN / kRowsPerPass;
+  static constexpr int kVThreads = kTN * D / 32;        // 4 keys x 8 values each
+  typedef uint32_t KVec __attribute__((ext_vector_type(4 * kPasses)));
+  typedef uint32_t VVec __attribute__((ext_vector_type(16)));
+  KVec kr;
+  VVec vr;  // 4 keys x 8 bf16: key kk in words 4kk .. 4kk+3
+
+  // keys key0 + [0, kTN); rows at or beyond `last` repeat row `last` (masked later)
+  __device__ __forceinline__ void load(const View& K, const View& V, int g, int key0, int last) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int row = p * kRowsPerPass + t / kUnits;
+      const int key = min(key0 + row, last);
+      const uint4 x =
+          *reinterpret_cast<const uint4*>(elem_ptr<__bf16>(K, key, g) + (t % kUnits) * 8);
+      kr[4 * p] = x.x;
+      kr[4 * p + 1] = x.y;
+      kr[4 * p + 2] = x.z;
+      kr[4 * p + 3] = x.w;
+    }
+    if (t < kVThreads) {
+      const int dv8 = (t % kUnits) * 8;
+      const int k0 = (t / kUnits) * 4;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int key = min(key0 + k0 + kk, last);
+        const uint4 x = *reinterpret_cast<const uint4*>(elem_ptr<__bf16>(V, key, g) + dv8);
+        vr[4 * kk] = x.x;
+        vr[4 * kk + 1] = x.y;
+        vr[4 * kk + 2] = x.z;
+        vr[4 * kk + 3] = x.w;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(Lds<D>& s, int buf) const {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int row = p * kRowsPerPass + t / kUnits;
+      *reinterpret_cast<uint4*>(&s.k[buf][k_off<D>(row, t % kUnits)]) =
+          make_uint4(kr[4 * p], kr[4 * p + 1], kr[4 * p + 2], kr[4 * p + 3]);
+    }
+    if (t < kVThreads) {
+      const int dv8 = (t % kUnits) * 8;
+      const int q = t / kUnits;  // 4-key group
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // value columns dv8 + 2w (low halves) and dv8 + 2w + 1 (high halves)
+        const uint32_t a0 = vr[w], a1 = vr[4 + w], a2 = vr[8 + w], a3 = vr[12 + w];
+        const uint2 even = make_uint2((a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16));
+        const uint2 odd = make_uint2((a0 >> 16) | (a1 & 0xffff0000u),
+                                     (a2 >> 16) | (a3 & 0xffff0000u));
+        *reinterpret_cast<uint2*>(&s.vt[buf][vt_off(dv8 + 2 * w, q)]) = even;
+        *reinterpret_cast<uint2*>(&s.vt[buf][vt_off(dv8 + 2 * w + 1, q)]) = odd;
+      }
+    }
+  }
+};
+
+// Per-wave online-softmax state for 32 queries (one per lane pair).
+template <int D>
+struct WaveState {
+  f32x16 o[D / 32];  // O^T: rows = value columns, columns = queries
+  float m, l;        // running max (log2 units) and denominator of this lane's query
+};
+
+// One key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+// kvalid: number of valid keys in the tile; qpos: mask keys > qpos (MASK only).
+template <int D, bool MASK>
+__device__ __forceinline__ void wave_tile(const Lds<D>& s, int buf, const bf16x8* qf, float c,
+                                 WaveState<D>& st, int tile_key0, int kvalid, int qpos) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int half = lane >> 5;
+  f32x16 sc[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    sc[m] = f32x16{};
+    const int row = m * 32 + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.k[buf][k_off<D>(row, 2 * ks + half)]);
+      sc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sc[m], 0, 0, 0);
+    }
+  }
+  // lane holds keys m*32 + 8*(j/4) + 4*half + (j%4) of its query (column lane&31)
+  float mx = -INFINITY;
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (MASK) {
+        const int kl = m * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+        if (kl >= kvalid || tile_key0 + kl > qpos) sc[m][j] = -INFINITY;
+      }
+      mx = fmaxf(mx, sc[m][j]);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  const float m_new = fmaxf(st.m, mx * c);
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = (st.m == -INFINITY) ? 0.f : exp2f(st.m - m_use);
+  float rs = 0.f;
+  bf16x8 pb[4];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float p = exp2f(fmaf(sc[m][j], c, -m_use));
+      rs += p;
+      pb[2 * m + (j >> 3)][j & 7] = (__bf16)p;
+    }
+  rs += __shfl_xor(rs, 32, kWave);
+  st.l = st.l * alpha + rs;
+  st.m = m_new;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) st.o[dt][j] *= alpha;
+  // P^T for key step s: keys 16s + 4*half + (0..3) and 16s + 8 + 4*half + (0..3)
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int r = dt * 32 + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x4 lo = *reinterpret_cast<const bf16x4*>(&s.vt[buf][vt_off(r, 4 * ks + half)]);
+      const bf16x4 hi = *reinterpret_cast<const bf16x4*>(&s.vt[buf][vt_off(r, 4 * ks + 2 + half)]);
+      const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], st.o[dt], 0, 0, 0);
+    }
+  }
+}
+
+// Runs every key tile of [key0, key0 + nkeys) through the workgroup.  Tile kt
+// is staged into LDS buffer kt & 1 and consumed after one barrier; the barrier
+// of tile kt + 1 also orders every read of buffer kt & 1 before its reuse by
+// tile kt + 2.  The staging registers are dead during the MFMA work, and the
+// second workgroup on the CU hides the load latency.
+// active: this wave has work; wave_max_pos: skip tiles entirely past it (MASK).
+template <int D, bool MASK>
+__device__ __forceinline__ void run_keys(Lds<D>& s, const View& K, const View& V, int g,
+                                         int key0, int nkeys, bool active, const bf16x8* qf,
+                                         float c, WaveState<D>& st, int qpos,
+                                         int wave_max_pos) {
+  const int n_kt = (nkeys + kTN - 1) / kTN;
+  const int last = key0 + nkeys - 1;
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    const int tk0 = key0 + kt * kTN;
+    {
+      Stage<D> stage;
+      stage.load(K, V, g, tk0, last);
+      stage.store(s, buf);
+    }
+    __syncthreads();
+    if (active && (!MASK || tk0 <= wave_max_pos))
+      wave_tile<D, MASK>(s, buf, qf, c, st, tk0, min(kTN, nkeys - kt * kTN), qpos);
+  }
+  __syncthreads();  // the caller may restage buffer 0 right away
+}
+
+template <int D>
+__device__ __forceinline__ void load_q(const View& Q, int row, int head, bf16x8* qf) {
+  const int half = (threadIdx.x & (kWave - 1)) >> 5;
+  const __bf16* qp = elem_ptr<__bf16>(Q, row, head);
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * half);
+}
+
+// Persistent walk over `total` work items with an XCD-aware order: workgroup b
+// runs on XCD b % 8 and takes items from that XCD's contiguous eighth, so the
+// tiles of one key block share one L2.
+struct XcdWalk {
+  int begin, end, step;
+  __device__ XcdWalk(int total) {
+    const int nx = 8;
+    const int x = blockIdx.x % nx;
+    const int per = (total + nx - 1) / nx;
+    const int wg_in_x = (gridDim.x + nx - 1 - x) / nx;  // workgroups on this XCD
+    begin = x * per + (int)(blockIdx.x / nx);
+    end = min(total, (x + 1) * per);
+    step = max(wg_in_x, 1);
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void k_bm_tiles(AttnKernelArgs a, BmWs w,
+                                                          int n_blocks) {
+  __shared__ Lds<D> s;
+  const int total = w.totals[0];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int half = lane >> 5;
+  const int hq = a.q.h;
+  const int W = a.idx_width;
+  const XcdWalk walk(total);
+  for (int t = walk.begin; t < walk.end; t += walk.step) {
+    const int2 tl = w.tiles[t];
+    const int list = tl.x;
+    const int g = list / n_blocks;
+    const int blk = list % n_blocks;
+    const int cnt = min(kTM, w.counts[list] - tl.y);
+    const int32_t* ent = w.entries + w.list_off[list] + tl.y;
+    const int n = wave * kQW + (lane & 31);
+    const bool valid = n < cnt;
+    const int p = ent[valid ? n : 0];
+    const int row = p / (hq * W);
+    const int head = (p / W) % hq;
+    bf16x8 qf[D / 16];
+    load_q<D>(a.q, row, head, qf);
+    WaveState<D> st;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) st.o[dt] = f32x16{};
+    st.m = -INFINITY;
+    st.l = 0.f;
+    const int2 b = w.bt.blocks[blk];
+    run_keys<D, false>(s, a.k, a.v, g, b.x, b.y, wave * kQW < cnt, qf, a.scale_log2, st, 0, 0);
+    if (valid) {
+      if (half == 0) w.part_ml[p] = make_float2(st.m, st.l);
+      float* z = w.part_z + (int64_t)p * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *reinterpret_cast<float4*>(z + dt * 32 + 8 * jj + 4 * half) =
+              make_float4(st.o[dt][4 * jj], st.o[dt][4 * jj + 1], st.o[dt][4 * jj + 2],
+                          st.o[dt][4 * jj + 3]);
+    }
+  }
+}
+
+__device__ inline void store4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+__device__ inline void store4(__bf16* p, float a, float b, float c, float d) {
+  bf16x4 x = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+  *reinterpret_cast<bf16x4*>(p) = x;
+}
+
+template <int D, typename TO>
+__global__ __launch_bounds__(kThreads, 2) void k_bm_diag(AttnKernelArgs a, BmWs w) {
+  __shared__ Lds<D> s;
+  __shared__ int s_maxpos;
+  const int n_tiles = w.totals[1];
+  const int hkv = a.k.h;
+  const int G = a.q.h / hkv;
+  const int TR = kTM / G;  // rows per diagonal tile
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int half = lane >> 5;
+  const int hq = a.q.h;
+  const int W = a.idx_width;
+  const XcdWalk walk(n_tiles * hkv);
+  for (int item = walk.begin; item < walk.end; item += walk.step) {
+    const int tile = item / hkv;
+    const int g = item % hkv;
+    const int2 d0 = w.diag[tile];
+    const int r0 = d0.x;
+    const int nrows = w.diag[tile + 1].x - r0;
+    const int own = d0.y;
+    const int n = wave * kQW + (lane & 31);
+    const int row = r0 + n % TR;
+    const int head = g * G + n / TR;
+    const bool valid = (n % TR) < nrows;
+    const int rowc = valid ? row : r0;
+    const int qpos = (own >= 0 && valid) ? a.L.q_pos[rowc] : -1;
+
+    WaveState<D> st;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) st.o[dt] = f32x16{};
+    st.m = -INFINITY;
+    st.l = 0.f;
+    if (own >= 0) {
+      if (threadIdx.x == 0) s_maxpos = -1;
+      __syncthreads();
+      if (threadIdx.x < nrows) atomicMax(&s_maxpos, a.L.q_pos[r0 + threadIdx.x]);
+      __syncthreads();
+      const int maxpos = s_maxpos;
+      int wmax = qpos;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) wmax = max(wmax, __shfl_xor(wmax, off, kWave));
+      bf16x8 qf[D / 16];
+      load_q<D>(a.q, rowc, head, qf);
+      const int own_start = w.bt.blocks[own].x;
+      run_keys<D, true>(s, a.k, a.v, g, own_start, maxpos - own_start + 1, wmax >= own_start,
+                        qf, a.scale_log2, st, qpos, wmax);
+    }
+    if (!valid) continue;
+    // own-block multiplicity, then the full-block summaries in slot order
+    const int pair = rowc * hq + head;
+    const int mult = w.own_mult[pair];
+    if (mult == 0) {
+      st.m = -INFINITY;
+      st.l = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) st.o[dt] = f32x16{};
+    } else if (mult > 1) {
+      st.l *= (float)mult;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) st.o[dt][j] *= (float)mult;
+    }
+    const RowKeys r = row_keys(a.L, rowc);
+    if (r.valid) {
+      const int32_t* slots = slot_row(a, rowc, head);
+      for (int sl = 0; sl < W; ++sl) {
+        if (slot_class(slots[sl], r, a.block_size) != 1) continue;
+        const int64_t p = (int64_t)pair * W + sl;
+        const float2 ml = w.part_ml[p];
+        const float mn = fmaxf(st.m, ml.x);
+        const float al = (st.m == -INFINITY) ? 0.f : exp2f(st.m - mn);
+        const float be = exp2f(ml.x - mn);
+        st.l = st.l * al + ml.y * be;
+        st.m = mn;
+        const float* z = w.part_z + p * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float4 zz = *reinterpret_cast<const float4*>(z + dt * 32 + 8 * jj + 4 * half);
+            st.o[dt][4 * jj] = st.o[dt][4 * jj] * al + zz.x * be;
+            st.o[dt][4 * jj + 1] = st.o[dt][4 * jj + 1] * al + zz.y * be;
+            st.o[dt][4 * jj + 2] = st.o[dt][4 * jj + 2] * al + zz.z * be;
+            st.o[dt][4 * jj + 3] = st.o[dt][4 * jj + 3] * al + zz.w * be;
+          }
+      }
+    }
+    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+    TO* out = reinterpret_cast<TO*>(a.out) + (int64_t)pair * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        store4(out + dt * 32 + 8 * jj + 4 * half, st.o[dt][4 * jj] * inv,
+               st.o[dt][4 * jj + 1] * inv, st.o[dt][4 * jj + 2] * inv,
+               st.o[dt][4 * jj + 3] * inv);
+    if (a.lse && half == 0)
+      a.lse[pair] = st.l > 0.f ? (st.m + log2f(st.l)) * kLn2 : -INFINITY;
+  }
+}
+
+int device_cus() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+  }
+  return cus;
+}
+
+template <int D>
+hipError_t launch_d(const AttnKernelArgs& a, int n_blocks, void* ws, hipStream_t stream) {
+  BmWs w;
+  const int n_seq = a.L.n_seq;
+  const int hq = a.q.h, hkv = a.k.h;
+  carve_bm<true>(ws, a.L.n_q, n_seq, n_blocks, hq, hkv, D, a.idx_width, &w);
+  const int n_lists = hkv * n_blocks;
+  hipError_t e = launch_block_table(a.L.cu, n_seq, a.block_size, n_blocks, w.bt, w.counts,
+                                    2 * (int64_t)n_lists, stream);
+  if (e != hipSuccess) return e;
+  const int64_t pairs = (int64_t)a.L.n_q * hq;
+  const int pgrid = (int)((pairs + 255) / 256);
+  hipLaunchKernelGGL(k_bm_count, dim3(pgrid), dim3(256), 0, stream, a, w.bt, n_blocks,
+                     w.counts, w.own_mult);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int rows_per_diag = kTM / (hq / hkv);
+  hipLaunchKernelGGL(k_bm_scan, dim3(1), dim3(kScanThreads), 0, stream, a, w.bt, n_lists,
+                     rows_per_diag, w.counts, w.list_off, w.tiles, w.totals, w.diag);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_bm_fill, dim3(pgrid), dim3(256), 0, stream, a, w.bt, n_blocks,
+                     w.list_off, w.fill, w.entries);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int grid = 2 * device_cus();
+  hipLaunchKernelGGL((k_bm_tiles<D>), dim3(grid), dim3(kThreads), 0, stream, a, w, n_blocks);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.out_dtype == CSA_BF16)
+    hipLaunchKernelGGL((k_bm_diag<D, __bf16>), dim3(grid), dim3(kThreads), 0, stream, a, w);
+  else
+    hipLaunchKernelGGL((k_bm_diag<D, float>), dim3(grid), dim3(kThreads), 0, stream, a, w);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attn_block_mfma_ws_bytes(int n_q, int n_seq, int n_blocks, int hq, int hkv, int dv,
+                                int idx_width) {
+  return carve_bm<false>(nullptr, n_q, n_seq, n_blocks, hq, hkv, dv, idx_width, nullptr);
+}
+
+bool attn_block_mfma_supported(const AttnKernelArgs& a) {
+  const int G = a.q.h / a.k.h;
+  const int D = a.q.d;
+  return a.mode == CSA_SEL_BLOCK && a.dtype == CSA_BF16 && (D == 64 || D == 128) &&
+         a.v.d == D && a.block_size % kTN == 0 && G >= 1 && G <= kTM && (G & (G - 1)) == 0 &&
+         a.scale_log2 > 0.f;
+}
+
+hipError_t launch_attn_block_mfma(const AttnKernelArgs& a, int n_blocks, void* ws,
+                                  hipStream_t stream) {
+  if (a.L.n_q == 0) return hipSuccess;
+  if (a.q.d == 64) return launch_d<64>(a, n_blocks, ws, stream);
+  return launch_d<128>(a, n_blocks, ws, stream);
+}
+
+}  // namespace csa

@@ -67,11 +67,24 @@ size_t carve_bytes(int n_seq, int n_blocks, int hkv, int d, int block_size) {
 __global__ void k_moba_need(DevLayout L, int block_size, const int32_t* __restrict__ blk_off,
                             int32_t* __restrict__ need) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= L.n_q) return;
-  const RowKeys r = row_keys(L, i);
-  if (!r.valid) return;
-  const int own = blk_off[r.seq] + (r.hi - r.lo) / block_size;
-  atomicMax(&need[r.seq], own);
+  int seq = -1, own = -1;
+  if (i < L.n_q) {
+    const RowKeys r = row_keys(L, i);
+    if (r.valid) {
+      seq = r.seq;
+      own = blk_off[r.seq] + (r.hi - r.lo) / block_size;
+    }
+  }
+  // rows of one wave are usually in one sequence: one atomic per wave then
+  const int seq0 = __shfl(seq, 0, kWave);
+  if (__all(seq == seq0)) {
+    int m = own;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = max(m, __shfl_xor(m, off, kWave));
+    if ((threadIdx.x & (kWave - 1)) == 0 && seq0 >= 0) atomicMax(&need[seq0], m);
+  } else if (seq >= 0) {
+    atomicMax(&need[seq], own);
+  }
 }
 
 template <typename T>

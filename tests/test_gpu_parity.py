@@ -51,15 +51,20 @@ def _check_out(w, idx_np, out, lse, rows, tol):
     return err
 
 
+# bf16 cases with D in {64, 128} and blocks of a multiple of 64 run the MFMA path;
+# the others (and every fp32 case) run the general-shape path.
 TINY_BLOCK = [
     dict(seed=0, lengths=(200, 120), layout="contiguous", cp=2, rank=1, hq=4, hkv=2, d=64,
-         block=32, topk=2),
+         block=64, topk=2),
     dict(seed=1, lengths=(512,), layout="zigzag", cp=4, rank=1, hq=8, hkv=2, d=128, block=64,
          topk=3),
-    dict(seed=2, lengths=(77, 300, 19, 116), layout="all", hq=4, hkv=4, d=128, block=32,
+    dict(seed=2, lengths=(77, 300, 19, 116), layout="all", hq=4, hkv=4, d=128, block=64,
          topk=4),
     dict(seed=3, lengths=(640,), layout="contiguous", cp=4, rank=3, hq=2, hkv=1, d=64,
          block=64, topk=1),
+    dict(seed=5, lengths=(333, 700, 91), layout="all", hq=16, hkv=2, d=128, block=128,
+         topk=2),
+    dict(seed=6, lengths=(300, 212), layout="all", hq=4, hkv=2, d=64, block=48, topk=3),
 ]
 
 
@@ -80,12 +85,12 @@ def test_tiny_block_gate_and_attention(case, dtype):
         _check_out(w, idx_np, out, lse, list(range(w.n_q)), tol)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_tiny_block_arbitrary_slots(dtype):
+@pytest.mark.parametrize("dtype,block", [("f32", 16), ("bf16", 16), ("bf16", 64)])
+def test_tiny_block_arbitrary_slots(dtype, block):
     """Caller-made index rows: pads, misaligned, out-of-range, future and repeated slots."""
-    w = tiny_block_workload(seed=4, layout="all", lengths=(100, 140, 60), hq=4, hkv=2, d=64,
-                            block=16, topk=2, dtype=dtype)
-    _say("arbitrary slots", dtype)
+    w = tiny_block_workload(seed=4, layout="all", lengths=(300, 420, 180), hq=4, hkv=2, d=64,
+                            block=block, topk=2, dtype=dtype)
+    _say("arbitrary slots", dtype, block)
     rng = np.random.default_rng(4)
     W = 7
     idx = rng.integers(-3, w.n_kv + 3, size=(w.n_q, w.hq, W)).astype(np.int32)
@@ -162,14 +167,14 @@ def test_summary_merge_matches_oracle():
 
 
 def test_rows_without_keys_and_all_masked_rows():
-    w = tiny_block_workload(seed=10, layout="all", lengths=(128, 128), hq=4, hkv=2, d=64,
-                            block=32, topk=2, dtype="bf16")
+    w = tiny_block_workload(seed=10, layout="all", lengths=(256, 256), hq=4, hkv=2, d=64,
+                            block=64, topk=2, dtype="bf16")
     _say("no-key rows")
     q_seq = w.q_seq.copy()
     q_pos = w.q_pos.copy()
     q_seq[5] = 1        # sequence 1 starts after position 5
     q_seq[200] = 9      # no such sequence
-    q_pos[201] = 999    # beyond the stream
+    q_pos[201] = 9999   # beyond the stream
     w.q_seq, w.q_pos = q_seq, q_pos
     d = upload(w)
     idx = csa.moba_gate_topk(d["q"], d["k"], d["layout"], w.block_size, w.topk)
