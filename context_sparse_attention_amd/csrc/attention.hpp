@@ -18,8 +18,9 @@ struct AttnKernelArgs {
 hipError_t launch_attn_generic(const AttnKernelArgs& a, hipStream_t stream);
 
 // bf16 block mode with D = Dqk = Dv in {64, 128}, block size a multiple of 64,
-// a power-of-two GQA group of at most 128 and a positive scale.
-bool attn_block_mfma_supported(const AttnKernelArgs& a);
+// a power-of-two GQA group of at most 128, at most 16384 (key head, block)
+// lists and a positive scale.
+bool attn_block_mfma_supported(const AttnKernelArgs& a, int n_blocks);
 size_t attn_block_mfma_ws_bytes(int n_q, int n_seq, int n_blocks, int hq, int hkv, int dv,
                                 int idx_width);
 hipError_t launch_attn_block_mfma(const AttnKernelArgs& a, int n_blocks, void* ws,

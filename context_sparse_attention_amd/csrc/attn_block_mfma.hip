@@ -17,9 +17,10 @@
 //
 // Kernels (in stream order):
 //   k_block_table  (layout.hip) block table + zeroed list counters
-//   k_bm_count     per (row, head): count full block slots per list, own multiplicity
+//   k_bm_hist      64 workgroups: LDS histogram of full block slots per list,
+//                  own-block multiplicity per (row, head)
 //   k_bm_scan      one workgroup: list offsets, query tiles, diagonal row tiles
-//   k_bm_fill      per (row, head): scatter slot ids into the lists
+//   k_bm_fill      64 workgroups: place slot ids into the lists (counting sort)
 //   k_bm_tiles     persistent: per query tile, S^T = K Q^T and O^T = V^T P^T on
 //                  LDS-staged key/value tiles (32x32x16 bf16 MFMA), fp32 online
 //                  softmax in registers, one fp32 summary per slot
@@ -47,12 +48,15 @@ constexpr int kWaves = 4;
 constexpr int kTM = kQW * kWaves;        // queries per workgroup tile
 constexpr int kThreads = kWaves * kWave;
 constexpr int kScanThreads = 1024;
+constexpr int kHistWgs = 64;          // workgroups that bucket the slots into lists
+constexpr int kHistThreads = 256;
+constexpr int kMaxLists = 16384;      // LDS histogram bins (64 KiB)
 constexpr float kLn2 = 0.69314718055994531f;
 
 struct BmWs {
   BlockTable bt;
-  int32_t* counts;    // [n_lists]
-  int32_t* fill;      // [n_lists], adjacent to counts (zeroed together)
+  int32_t* counts;    // [n_lists]  slots per list
+  int32_t* hist;      // [n_hist_wg, n_lists]  per-workgroup counts, then prefixes
   int32_t* list_off;  // [n_lists + 1]
   int2* tiles;        // [max_tiles]  (list, first entry)
   int32_t* totals;    // [4]  query tiles, diagonal tiles
@@ -75,8 +79,8 @@ size_t carve_bm(void* base, int n_q, int n_seq, int n_blocks, int hq, int hkv, i
   t.bt.blk_off = c.take<int32_t>(n_seq + 1);
   t.bt.blocks = c.take<int2>(n_blocks);
   t.bt.blk_seq = c.take<int32_t>(n_blocks);
-  t.counts = c.take<int32_t>(2 * n_lists);
-  t.fill = t.counts + n_lists;
+  t.counts = c.take<int32_t>(n_lists);
+  t.hist = c.take<int32_t>((size_t)kHistWgs * n_lists);
   t.list_off = c.take<int32_t>(n_lists + 1);
   t.tiles = c.take<int2>(max_query_tiles(slots, n_lists));
   t.totals = c.take<int32_t>(4);
@@ -99,46 +103,74 @@ __device__ inline int slot_class(int s, const RowKeys& r, int B) {
   return (s + B - 1 < r.hi) ? 1 : 2;
 }
 
-__global__ void k_bm_count(AttnKernelArgs a, BlockTable bt, int n_blocks,
-                           int32_t* __restrict__ counts, int32_t* __restrict__ own_mult) {
-  const int64_t pair = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// The (row, head) pairs are cut into kHistWgs contiguous ranges.  Each range
+// is bucketed by one workgroup with an LDS histogram (no global atomics), so
+// list building is a counting sort: hist[w][list] counts, a scan turns the
+// matrix into per-list offsets, and the fill pass places each slot at
+// list_off[list] + prefix[w][list] + its LDS-local rank.
+__device__ inline void pair_range(int64_t pairs, int64_t* b, int64_t* e) {
+  const int64_t per = (pairs + kHistWgs - 1) / kHistWgs;
+  *b = min(pairs, (int64_t)blockIdx.x * per);
+  *e = min(pairs, *b + per);
+}
+
+__global__ __launch_bounds__(kHistThreads) void k_bm_hist(AttnKernelArgs a, BlockTable bt,
+                                                          int n_blocks, int n_lists,
+                                                          int32_t* __restrict__ hist,
+                                                          int32_t* __restrict__ own_mult) {
+  extern __shared__ int s_bins[];
+  for (int l = threadIdx.x; l < n_lists; l += kHistThreads) s_bins[l] = 0;
+  __syncthreads();
   const int hq = a.q.h;
-  if (pair >= (int64_t)a.L.n_q * hq) return;
-  const int i = (int)(pair / hq), h = (int)(pair % hq);
-  const int g = h / (hq / a.k.h);
-  const RowKeys r = row_keys(a.L, i);
-  int mult = 0;
-  if (r.valid) {
+  int64_t b, e;
+  pair_range((int64_t)a.L.n_q * hq, &b, &e);
+  for (int64_t pair = b + threadIdx.x; pair < e; pair += kHistThreads) {
+    const int i = (int)(pair / hq), h = (int)(pair % hq);
+    const int g = h / (hq / a.k.h);
+    const RowKeys r = row_keys(a.L, i);
+    int mult = 0;
+    if (r.valid) {
+      const int32_t* slots = slot_row(a, i, h);
+      const int base = g * n_blocks + bt.blk_off[r.seq];
+      for (int s = 0; s < a.idx_width; ++s) {
+        const int st = slots[s];
+        const int c = slot_class(st, r, a.block_size);
+        if (c == 1) atomicAdd(&s_bins[base + (st - r.lo) / a.block_size], 1);
+        else if (c == 2) ++mult;
+      }
+    }
+    own_mult[pair] = mult;
+  }
+  __syncthreads();
+  for (int l = threadIdx.x; l < n_lists; l += kHistThreads)
+    hist[(int64_t)blockIdx.x * n_lists + l] = s_bins[l];
+}
+
+__global__ __launch_bounds__(kHistThreads) void k_bm_fill(AttnKernelArgs a, BlockTable bt,
+                                                          int n_blocks, int n_lists,
+                                                          const int32_t* __restrict__ list_off,
+                                                          const int32_t* __restrict__ hist,
+                                                          int32_t* __restrict__ entries) {
+  extern __shared__ int s_bins[];
+  for (int l = threadIdx.x; l < n_lists; l += kHistThreads)
+    s_bins[l] = list_off[l] + hist[(int64_t)blockIdx.x * n_lists + l];
+  __syncthreads();
+  const int hq = a.q.h;
+  int64_t b, e;
+  pair_range((int64_t)a.L.n_q * hq, &b, &e);
+  for (int64_t pair = b + threadIdx.x; pair < e; pair += kHistThreads) {
+    const int i = (int)(pair / hq), h = (int)(pair % hq);
+    const int g = h / (hq / a.k.h);
+    const RowKeys r = row_keys(a.L, i);
+    if (!r.valid) continue;
     const int32_t* slots = slot_row(a, i, h);
     const int base = g * n_blocks + bt.blk_off[r.seq];
     for (int s = 0; s < a.idx_width; ++s) {
       const int st = slots[s];
-      const int c = slot_class(st, r, a.block_size);
-      if (c == 1) atomicAdd(&counts[base + (st - r.lo) / a.block_size], 1);
-      else if (c == 2) ++mult;
+      if (slot_class(st, r, a.block_size) != 1) continue;
+      const int at = atomicAdd(&s_bins[base + (st - r.lo) / a.block_size], 1);
+      entries[at] = (int32_t)(pair * a.idx_width + s);
     }
-  }
-  own_mult[pair] = mult;
-}
-
-__global__ void k_bm_fill(AttnKernelArgs a, BlockTable bt, int n_blocks,
-                          const int32_t* __restrict__ list_off, int32_t* __restrict__ fill,
-                          int32_t* __restrict__ entries) {
-  const int64_t pair = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int hq = a.q.h;
-  if (pair >= (int64_t)a.L.n_q * hq) return;
-  const int i = (int)(pair / hq), h = (int)(pair % hq);
-  const int g = h / (hq / a.k.h);
-  const RowKeys r = row_keys(a.L, i);
-  if (!r.valid) return;
-  const int32_t* slots = slot_row(a, i, h);
-  const int base = g * n_blocks + bt.blk_off[r.seq];
-  for (int s = 0; s < a.idx_width; ++s) {
-    const int st = slots[s];
-    if (slot_class(st, r, a.block_size) != 1) continue;
-    const int list = base + (st - r.lo) / a.block_size;
-    const int at = atomicAdd(&fill[list], 1);
-    entries[list_off[list] + at] = (int32_t)(pair * a.idx_width + s);
   }
 }
 
@@ -164,12 +196,25 @@ __device__ int scan_incl(int x, int* s_wave, int* s_total) {
 
 __global__ __launch_bounds__(kScanThreads) void k_bm_scan(AttnKernelArgs a, BlockTable bt,
                                                           int n_lists, int rows_per_diag,
-                                                          const int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ hist,
                                                           int32_t* __restrict__ list_off,
                                                           int2* __restrict__ tiles,
                                                           int32_t* __restrict__ totals,
                                                           int2* __restrict__ diag) {
   __shared__ int s_wave[kScanThreads / kWave];
+  // per list: exclusive prefix over the bucketing workgroups, and the total
+  for (int l = threadIdx.x; l < n_lists; l += kScanThreads) {
+    int run = 0;
+    for (int w = 0; w < kHistWgs; ++w) {
+      const int64_t at = (int64_t)w * n_lists + l;
+      const int c = hist[at];
+      hist[at] = run;
+      run += c;
+    }
+    counts[l] = run;
+  }
+  __syncthreads();
   int carry = 0, tcarry = 0, tot = 0;
   for (int base = 0; base < n_lists; base += kScanThreads) {
     const int l = base + threadIdx.x;
@@ -607,20 +652,19 @@ hipError_t launch_d(const AttnKernelArgs& a, int n_blocks, void* ws, hipStream_t
   const int hq = a.q.h, hkv = a.k.h;
   carve_bm<true>(ws, a.L.n_q, n_seq, n_blocks, hq, hkv, D, a.idx_width, &w);
   const int n_lists = hkv * n_blocks;
-  hipError_t e = launch_block_table(a.L.cu, n_seq, a.block_size, n_blocks, w.bt, w.counts,
-                                    2 * (int64_t)n_lists, stream);
+  hipError_t e = launch_block_table(a.L.cu, n_seq, a.block_size, n_blocks, w.bt, nullptr, 0,
+                                    stream);
   if (e != hipSuccess) return e;
-  const int64_t pairs = (int64_t)a.L.n_q * hq;
-  const int pgrid = (int)((pairs + 255) / 256);
-  hipLaunchKernelGGL(k_bm_count, dim3(pgrid), dim3(256), 0, stream, a, w.bt, n_blocks,
-                     w.counts, w.own_mult);
+  const size_t bins = (size_t)n_lists * sizeof(int);
+  hipLaunchKernelGGL(k_bm_hist, dim3(kHistWgs), dim3(kHistThreads), bins, stream, a, w.bt,
+                     n_blocks, n_lists, w.hist, w.own_mult);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int rows_per_diag = kTM / (hq / hkv);
   hipLaunchKernelGGL(k_bm_scan, dim3(1), dim3(kScanThreads), 0, stream, a, w.bt, n_lists,
-                     rows_per_diag, w.counts, w.list_off, w.tiles, w.totals, w.diag);
+                     rows_per_diag, w.counts, w.hist, w.list_off, w.tiles, w.totals, w.diag);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_bm_fill, dim3(pgrid), dim3(256), 0, stream, a, w.bt, n_blocks,
-                     w.list_off, w.fill, w.entries);
+  hipLaunchKernelGGL(k_bm_fill, dim3(kHistWgs), dim3(kHistThreads), bins, stream, a, w.bt,
+                     n_blocks, n_lists, w.list_off, w.hist, w.entries);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int grid = 2 * device_cus();
   hipLaunchKernelGGL((k_bm_tiles<D>), dim3(grid), dim3(kThreads), 0, stream, a, w, n_blocks);
@@ -639,10 +683,11 @@ size_t attn_block_mfma_ws_bytes(int n_q, int n_seq, int n_blocks, int hq, int hk
   return carve_bm<false>(nullptr, n_q, n_seq, n_blocks, hq, hkv, dv, idx_width, nullptr);
 }
 
-bool attn_block_mfma_supported(const AttnKernelArgs& a) {
+bool attn_block_mfma_supported(const AttnKernelArgs& a, int n_blocks) {
   const int G = a.q.h / a.k.h;
   const int D = a.q.d;
   return a.mode == CSA_SEL_BLOCK && a.dtype == CSA_BF16 && (D == 64 || D == 128) &&
+         (int64_t)a.k.h * n_blocks <= kMaxLists &&
          a.v.d == D && a.block_size % kTN == 0 && G >= 1 && G <= kTM && (G & (G - 1)) == 0 &&
          a.scale_log2 > 0.f;
 }

@@ -35,6 +35,8 @@ struct MobaWs {
   int32_t* arrive;  // [n_blocks]
   float* partial;   // [n_blocks, n_chunks, hkv*d]
   float* mu;        // [n_blocks, hkv*d]
+  __bf16* mu_hi;    // [n_blocks, hkv*d]  bf16 split of mu (high part)
+  __bf16* mu_lo;    // [n_blocks, hkv*d]  (low part)
 };
 
 MobaWs carve_moba(void* base, int n_seq, int n_blocks, int hkv, int d, int block_size) {
@@ -49,6 +51,8 @@ MobaWs carve_moba(void* base, int n_seq, int n_blocks, int hkv, int d, int block
   const int n_chunks = (block_size + kPoolChunk - 1) / kPoolChunk;
   w.partial = c.take<float>((size_t)n_blocks * n_chunks * hkv * d);
   w.mu = c.take<float>((size_t)n_blocks * hkv * d);
+  w.mu_hi = c.take<__bf16>((size_t)n_blocks * hkv * d);
+  w.mu_lo = c.take<__bf16>((size_t)n_blocks * hkv * d);
   return w;
 }
 
@@ -61,6 +65,8 @@ size_t carve_bytes(int n_seq, int n_blocks, int hkv, int d, int block_size) {
   c.take<int32_t>((size_t)n_seq + n_blocks);
   c.take<float>((size_t)n_blocks * n_chunks * hkv * d);
   c.take<float>((size_t)n_blocks * hkv * d);
+  c.take<__bf16>((size_t)n_blocks * hkv * d);
+  c.take<__bf16>((size_t)n_blocks * hkv * d);
   return align_up(c.used, 256);
 }
 
@@ -93,6 +99,8 @@ __global__ __launch_bounds__(kPoolThreads) void k_moba_pool(View k, BlockTable b
                                                             int32_t* __restrict__ arrive,
                                                             float* __restrict__ partial,
                                                             float* __restrict__ mu,
+                                                            __bf16* __restrict__ mu_hi,
+                                                            __bf16* __restrict__ mu_lo,
                                                             int n_chunks) {
   const int b = blockIdx.x / n_chunks;
   const int chunk = blockIdx.x % n_chunks;
@@ -119,6 +127,7 @@ __global__ __launch_bounds__(kPoolThreads) void k_moba_pool(View k, BlockTable b
     if (kl < lanes_k) {
       const int e = eg * 8;
       const int hh = e / k.d, dd = e % k.d;
+#pragma unroll 4
       for (int t = t0 + kl; t < t1; t += lanes_k) {
         float x[8];
         load8(elem_ptr<T>(k, t, hh) + dd, x);
@@ -148,7 +157,14 @@ __global__ __launch_bounds__(kPoolThreads) void k_moba_pool(View k, BlockTable b
     float s = 0.f;
     for (int c = 0; c < n_my_chunks; ++c)
       s += partial[((size_t)b * n_chunks + c) * hd + e];
-    mu[(size_t)b * hd + e] = s * inv;
+    const float m = s * inv;
+    mu[(size_t)b * hd + e] = m;
+    if (mu_hi) {
+      // bf16 pair whose sum carries the fp32 mean to ~2^-17 relative
+      const __bf16 hi = (__bf16)m;
+      mu_hi[(size_t)b * hd + e] = hi;
+      mu_lo[(size_t)b * hd + e] = (__bf16)(m - (float)hi);
+    }
   }
 }
 
@@ -263,6 +279,161 @@ __global__ __launch_bounds__(kGateThreads) void k_moba_gate(View q, DevLayout L,
   }
 }
 
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int kGateCols = 64;  // block columns scored per pass
+
+// bf16 gate on the matrix cores.  One wave scores 16 consecutive rows of one
+// query head against 16-block column tiles with 16x16x32 bf16 MFMA: the A
+// operand is the rows' queries, the B operand the block means split into a
+// bf16 high and low part (two products per step, so the score keeps the fp32
+// mean to ~2^-17 relative).  The 16 x 64 score chunk goes through LDS and lanes
+// 0..15 each keep the register top-k of their row over its own candidates
+// (blocks of its sequence before its own block), in ascending block order so
+// that ties keep the lower block.
+template <int D, int KMAX>
+__global__ __launch_bounds__(kGateThreads) void k_moba_gate_mfma(
+    View q, DevLayout L, int hkv, int block_size, int topk, int n_blocks, BlockTable bt,
+    const __bf16* __restrict__ mu_hi, const __bf16* __restrict__ mu_lo,
+    int32_t* __restrict__ idx, float* __restrict__ score) {
+  __shared__ float s_sc[kGateThreads / kWave][16][kGateCols + 1];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int hq = q.h;
+  const int n_rg = (L.n_q + 15) / 16;
+  const int wg = blockIdx.x * (kGateThreads / kWave) + wave;
+  if (wg >= n_rg * hq) return;  // whole wave
+  const int h = wg % hq;
+  const int rg = wg / hq;
+  const int g = h / (hq / hkv);
+  const int rl = lane & 15;
+  const int quad = lane >> 4;
+  const int row = rg * 16 + rl;
+
+  int first = 0, own = -1;
+  if (row < L.n_q) {
+    const RowKeys r = row_keys(L, row);
+    if (r.valid) {
+      first = bt.blk_off[r.seq];
+      own = first + (r.hi - r.lo) / block_size;
+    }
+  }
+  int col_lo = own >= 0 ? first : INT32_MAX;
+  int col_hi = own;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    col_lo = min(col_lo, __shfl_xor(col_lo, off, kWave));
+    col_hi = max(col_hi, __shfl_xor(col_hi, off, kWave));
+  }
+
+  bf16x8 a[D / 32];
+  const __bf16* qp = elem_ptr<__bf16>(q, row < L.n_q ? row : 0, h);
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+    a[ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks + 8 * quad);
+
+  float best_s[KMAX];
+  int best_b[KMAX];
+#pragma unroll
+  for (int t = 0; t < KMAX; ++t) {
+    best_s[t] = -INFINITY;
+    best_b[t] = INT32_MAX;
+  }
+  const int hd = hkv * D;
+  for (int cb = col_lo; cb < col_hi; cb += kGateCols) {
+#pragma unroll
+    for (int t = 0; t < kGateCols / 16; ++t) {
+      const int c0 = cb + 16 * t;
+      if (c0 >= col_hi) break;  // uniform across the wave
+      const int blk = min(c0 + rl, n_blocks - 1);
+      const __bf16* ph = mu_hi + (size_t)blk * hd + (size_t)g * D + 8 * quad;
+      const __bf16* pl = mu_lo + (size_t)blk * hd + (size_t)g * D + 8 * quad;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(ph + 32 * ks);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(pl + 32 * ks);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bl, acc, 0, 0, 0);
+      }
+      // lane holds block c0 + rl for rows 4*quad .. 4*quad + 3
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s_sc[wave][4 * quad + j][16 * t + rl] = acc[j];
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    if (lane < 16) {
+      const int n = min(kGateCols, col_hi - cb);
+      for (int c = 0; c < n; ++c) {
+        const int b = cb + c;
+        if (b < first || b >= own) continue;
+        float cs = s_sc[wave][lane][c];
+        int cbk = b;
+#pragma unroll
+        for (int t = 0; t < KMAX; ++t) {
+          if (t < topk && cs > best_s[t]) {
+            const float ts = best_s[t];
+            const int tb = best_b[t];
+            best_s[t] = cs;
+            best_b[t] = cbk;
+            cs = ts;
+            cbk = tb;
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (lane >= 16 || row >= L.n_q) return;
+  const int width = topk + 1;
+  int32_t* out = idx + ((int64_t)row * hq + h) * width;
+  float* out_s = score ? score + ((int64_t)row * hq + h) * width : nullptr;
+  if (own < 0) {
+    for (int t = 0; t < width; ++t) {
+      out[t] = -1;
+      if (out_s) out_s[t] = -INFINITY;
+    }
+    return;
+  }
+  sort_pairs_asc<KMAX>(best_b, best_s);
+  int kept = 0;
+#pragma unroll
+  for (int u = 0; u < KMAX; ++u) {
+    if (best_b[u] != INT32_MAX) {
+      out[u] = bt.blocks[best_b[u]].x;
+      if (out_s) out_s[u] = best_s[u];
+      ++kept;
+    }
+  }
+  int t = kept;
+  out[t] = bt.blocks[own].x;
+  if (out_s) out_s[t] = INFINITY;
+  for (++t; t < width; ++t) {
+    out[t] = -1;
+    if (out_s) out_s[t] = -INFINITY;
+  }
+}
+
+template <int D, int KMAX>
+hipError_t launch_gate_mfma(const MobaGateArgs& a, const MobaWs& w, hipStream_t stream) {
+  const int64_t waves = (int64_t)((a.L.n_q + 15) / 16) * a.q.h;
+  const int per_wg = kGateThreads / kWave;
+  const int grid = (int)((waves + per_wg - 1) / per_wg);
+  hipLaunchKernelGGL((k_moba_gate_mfma<D, KMAX>), dim3(grid), dim3(kGateThreads), 0, stream,
+                     a.q, a.L, a.k.h, a.block_size, a.topk, a.n_blocks, w.bt, w.mu_hi,
+                     w.mu_lo, a.idx, a.score);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_gate_mfma_k(const MobaGateArgs& a, const MobaWs& w, hipStream_t stream) {
+  if (a.topk <= 4) return launch_gate_mfma<D, 4>(a, w, stream);
+  if (a.topk <= 8) return launch_gate_mfma<D, 8>(a, w, stream);
+  if (a.topk <= 16) return launch_gate_mfma<D, 16>(a, w, stream);
+  return launch_gate_mfma<D, 32>(a, w, stream);
+}
+
 template <typename T, int KMAX>
 hipError_t launch_gate_k(const MobaGateArgs& a, const MobaWs& w, hipStream_t stream) {
   const int64_t pairs = (int64_t)a.L.n_q * a.q.h;
@@ -284,10 +455,17 @@ hipError_t launch_typed(const MobaGateArgs& a, hipStream_t stream) {
                      a.block_size, w.bt.blk_off, w.need);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int n_chunks = (a.block_size + kPoolChunk - 1) / kPoolChunk;
+  const bool use_mfma = a.dtype == CSA_BF16 && (a.q.d == 64 || a.q.d == 128 || a.q.d == 256);
   if (a.n_blocks > 0) {
     hipLaunchKernelGGL((k_moba_pool<T>), dim3(a.n_blocks * n_chunks), dim3(kPoolThreads), 0,
-                       stream, a.k, w.bt, w.need, w.arrive, w.partial, w.mu, n_chunks);
+                       stream, a.k, w.bt, w.need, w.arrive, w.partial, w.mu,
+                       use_mfma ? w.mu_hi : nullptr, use_mfma ? w.mu_lo : nullptr, n_chunks);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (use_mfma) {
+    if (a.q.d == 64) return launch_gate_mfma_k<64>(a, w, stream);
+    if (a.q.d == 128) return launch_gate_mfma_k<128>(a, w, stream);
+    return launch_gate_mfma_k<256>(a, w, stream);
   }
   if (a.topk <= 4) return launch_gate_k<T, 4>(a, w, stream);
   if (a.topk <= 8) return launch_gate_k<T, 8>(a, w, stream);
