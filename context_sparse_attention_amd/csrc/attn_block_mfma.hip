@@ -19,13 +19,13 @@
 //   k_block_table  (layout.hip) block table + zeroed list counters
 //   k_bm_hist      64 workgroups: LDS histogram of full block slots per list,
 //                  own-block multiplicity per (row, head)
-//   k_bm_scan      one workgroup: list offsets, query tiles, diagonal row tiles
+//   k_bm_scan      one workgroup: list offsets and the query-tile table
 //   k_bm_fill      64 workgroups: place slot ids into the lists (counting sort)
 //   k_bm_tiles     persistent: per query tile, S^T = K Q^T and O^T = V^T P^T on
 //                  LDS-staged key/value tiles (32x32x16 bf16 MFMA), fp32 online
 //                  softmax in registers, one fp32 summary per slot
-//   k_bm_diag      persistent: own-block attention with the causal mask, merge
-//                  with the slot summaries in slot order, finalize
+//   k_bm_diag      persistent over fixed row tiles: own-block attention with the
+//                  causal mask, merge with the slot summaries in slot order, finalize
 //
 // Layout of the math: the MFMA computes S^T (keys x queries) so that a lane
 // owns one query and its scores sit in that lane's registers; the softmax row
@@ -59,8 +59,7 @@ struct BmWs {
   int32_t* hist;      // [n_hist_wg, n_lists]  per-workgroup counts, then prefixes
   int32_t* list_off;  // [n_lists + 1]
   int2* tiles;        // [max_tiles]  (list, first entry)
-  int32_t* totals;    // [4]  query tiles, diagonal tiles
-  int2* diag;         // [n_q + 1]  (first row, own block or -1)
+  int32_t* totals;    // [4]  query tiles
   int32_t* own_mult;  // [n_q * hq]
   int32_t* entries;   // [n_q * hq * W]  flat slot ids
   float2* part_ml;    // [n_q * hq * W]  (m in log2 units, l)
@@ -84,7 +83,6 @@ size_t carve_bm(void* base, int n_q, int n_seq, int n_blocks, int hq, int hkv, i
   t.list_off = c.take<int32_t>(n_lists + 1);
   t.tiles = c.take<int2>(max_query_tiles(slots, n_lists));
   t.totals = c.take<int32_t>(4);
-  t.diag = c.take<int2>(n_q + 1);
   t.own_mult = c.take<int32_t>((size_t)n_q * hq);
   t.entries = c.take<int32_t>(slots);
   t.part_ml = c.take<float2>(slots);
@@ -194,23 +192,23 @@ __device__ int scan_incl(int x, int* s_wave, int* s_total) {
   return x + before;
 }
 
-__global__ __launch_bounds__(kScanThreads) void k_bm_scan(AttnKernelArgs a, BlockTable bt,
-                                                          int n_lists, int rows_per_diag,
+__global__ __launch_bounds__(kScanThreads) void k_bm_scan(int n_lists,
                                                           int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ hist,
                                                           int32_t* __restrict__ list_off,
                                                           int2* __restrict__ tiles,
-                                                          int32_t* __restrict__ totals,
-                                                          int2* __restrict__ diag) {
+                                                          int32_t* __restrict__ totals) {
   __shared__ int s_wave[kScanThreads / kWave];
   // per list: exclusive prefix over the bucketing workgroups, and the total
   for (int l = threadIdx.x; l < n_lists; l += kScanThreads) {
+    int c[kHistWgs];
+#pragma unroll
+    for (int w = 0; w < kHistWgs; ++w) c[w] = hist[(int64_t)w * n_lists + l];
     int run = 0;
+#pragma unroll
     for (int w = 0; w < kHistWgs; ++w) {
-      const int64_t at = (int64_t)w * n_lists + l;
-      const int c = hist[at];
-      hist[at] = run;
-      run += c;
+      hist[(int64_t)w * n_lists + l] = run;
+      run += c[w];
     }
     counts[l] = run;
   }
@@ -234,30 +232,6 @@ __global__ __launch_bounds__(kScanThreads) void k_bm_scan(AttnKernelArgs a, Bloc
   if (threadIdx.x == 0) {
     list_off[n_lists] = carry;
     totals[0] = tcarry;
-  }
-  // diagonal row tiles: split at own-block changes and every rows_per_diag rows
-  int dcarry = 0;
-  const int B = a.block_size;
-  for (int base = 0; base < a.L.n_q; base += kScanThreads) {
-    const int i = base + threadIdx.x;
-    int key = -1, prev = -1;
-    bool flag = false;
-    if (i < a.L.n_q) {
-      const RowKeys r = row_keys(a.L, i);
-      key = r.valid ? bt.blk_off[r.seq] + (r.hi - r.lo) / B : -1;
-      if (i > 0) {
-        const RowKeys rp = row_keys(a.L, i - 1);
-        prev = rp.valid ? bt.blk_off[rp.seq] + (rp.hi - rp.lo) / B : -1;
-      }
-      flag = (i == 0) || (key != prev) || (i % rows_per_diag == 0);
-    }
-    const int incl = scan_incl(flag ? 1 : 0, s_wave, &tot);
-    if (flag) diag[dcarry + incl - 1] = make_int2(i, key);
-    dcarry += tot;
-  }
-  if (threadIdx.x == 0) {
-    diag[dcarry] = make_int2(a.L.n_q, -1);
-    totals[1] = dcarry;
   }
 }
 
@@ -530,54 +504,69 @@ __device__ inline void store4(__bf16* p, float a, float b, float c, float d) {
   *reinterpret_cast<bf16x4*>(p) = x;
 }
 
+// Diagonal tiles are fixed runs of TR = 128 / G consecutive rows (all G query
+// heads of one key head).  Rows of a tile whose own blocks differ (sequence or
+// zigzag-chunk boundaries) are handled run by run: each lane only takes keys in
+// the pass of its own row's block.
 template <int D, typename TO>
 __global__ __launch_bounds__(kThreads, 2) void k_bm_diag(AttnKernelArgs a, BmWs w) {
   __shared__ Lds<D> s;
-  __shared__ int s_maxpos;
-  const int n_tiles = w.totals[1];
+  __shared__ int s_own[kTM];
+  __shared__ int s_pos[kTM];
   const int hkv = a.k.h;
-  const int G = a.q.h / hkv;
+  const int hq = a.q.h;
+  const int G = hq / hkv;
   const int TR = kTM / G;  // rows per diagonal tile
+  const int n_tiles = (a.L.n_q + TR - 1) / TR;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int half = lane >> 5;
-  const int hq = a.q.h;
   const int W = a.idx_width;
+  const int B = a.block_size;
   const XcdWalk walk(n_tiles * hkv);
   for (int item = walk.begin; item < walk.end; item += walk.step) {
     const int tile = item / hkv;
     const int g = item % hkv;
-    const int2 d0 = w.diag[tile];
-    const int r0 = d0.x;
-    const int nrows = w.diag[tile + 1].x - r0;
-    const int own = d0.y;
+    const int r0 = tile * TR;
+    const int nrows = min(TR, a.L.n_q - r0);
+    if (threadIdx.x < nrows) {
+      const RowKeys r = row_keys(a.L, r0 + threadIdx.x);
+      s_own[threadIdx.x] = r.valid ? w.bt.blk_off[r.seq] + (r.hi - r.lo) / B : -1;
+      s_pos[threadIdx.x] = r.hi;
+    }
+    __syncthreads();
     const int n = wave * kQW + (lane & 31);
-    const int row = r0 + n % TR;
+    const int rl = n % TR;
     const int head = g * G + n / TR;
-    const bool valid = (n % TR) < nrows;
-    const int rowc = valid ? row : r0;
-    const int qpos = (own >= 0 && valid) ? a.L.q_pos[rowc] : -1;
+    const bool valid = rl < nrows;
+    const int rowc = r0 + (valid ? rl : 0);
+    const int my_pos = valid ? s_pos[rl] : -1;
 
     WaveState<D> st;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) st.o[dt] = f32x16{};
     st.m = -INFINITY;
     st.l = 0.f;
-    if (own >= 0) {
-      if (threadIdx.x == 0) s_maxpos = -1;
-      __syncthreads();
-      if (threadIdx.x < nrows) atomicMax(&s_maxpos, a.L.q_pos[r0 + threadIdx.x]);
-      __syncthreads();
-      const int maxpos = s_maxpos;
-      int wmax = qpos;
+    bf16x8 qf[D / 16];
+    load_q<D>(a.q, rowc, head, qf);
+    for (int start = 0; start < nrows;) {
+      const int ob = s_own[start];
+      int end = start + 1, maxpos = s_pos[start];
+      while (end < nrows && s_own[end] == ob) maxpos = max(maxpos, s_pos[end++]);
+      if (ob >= 0) {
+        // a lane joins only the run that holds its row: two runs may share a
+        // block when rows without keys sit between them
+        const int qpos = (valid && rl >= start && rl < end) ? my_pos : -1;
+        int wmax = qpos;
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) wmax = max(wmax, __shfl_xor(wmax, off, kWave));
-      bf16x8 qf[D / 16];
-      load_q<D>(a.q, rowc, head, qf);
-      const int own_start = w.bt.blocks[own].x;
-      run_keys<D, true>(s, a.k, a.v, g, own_start, maxpos - own_start + 1, wmax >= own_start,
-                        qf, a.scale_log2, st, qpos, wmax);
+        for (int off = 32; off >= 1; off >>= 1) wmax = max(wmax, __shfl_xor(wmax, off, kWave));
+        const int own_start = w.bt.blocks[ob].x;
+        run_keys<D, true>(s, a.k, a.v, g, own_start, maxpos - own_start + 1,
+                          wmax >= own_start, qf, a.scale_log2, st, qpos, wmax);
+      }
+      start = end;
     }
+    __syncthreads();  // s_own / s_pos are rewritten by the next item
     if (!valid) continue;
     // own-block multiplicity, then the full-block summaries in slot order
     const int pair = rowc * hq + head;
@@ -598,7 +587,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bm_diag(AttnKernelArgs a, BmWs 
     if (r.valid) {
       const int32_t* slots = slot_row(a, rowc, head);
       for (int sl = 0; sl < W; ++sl) {
-        if (slot_class(slots[sl], r, a.block_size) != 1) continue;
+        if (slot_class(slots[sl], r, B) != 1) continue;
         const int64_t p = (int64_t)pair * W + sl;
         const float2 ml = w.part_ml[p];
         const float mn = fmaxf(st.m, ml.x);
@@ -659,9 +648,8 @@ hipError_t launch_d(const AttnKernelArgs& a, int n_blocks, void* ws, hipStream_t
   hipLaunchKernelGGL(k_bm_hist, dim3(kHistWgs), dim3(kHistThreads), bins, stream, a, w.bt,
                      n_blocks, n_lists, w.hist, w.own_mult);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int rows_per_diag = kTM / (hq / hkv);
-  hipLaunchKernelGGL(k_bm_scan, dim3(1), dim3(kScanThreads), 0, stream, a, w.bt, n_lists,
-                     rows_per_diag, w.counts, w.hist, w.list_off, w.tiles, w.totals, w.diag);
+  hipLaunchKernelGGL(k_bm_scan, dim3(1), dim3(kScanThreads), 0, stream, n_lists, w.counts,
+                     w.hist, w.list_off, w.tiles, w.totals);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_bm_fill, dim3(kHistWgs), dim3(kHistThreads), bins, stream, a, w.bt,
                      n_blocks, n_lists, w.list_off, w.hist, w.entries);

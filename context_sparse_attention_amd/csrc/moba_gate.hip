@@ -11,12 +11,13 @@
 //   k_moba_need  - per packed sequence, the highest own block of any local row
 //                  (blocks at or after it are never candidates, so they are
 //                  not pooled);
-//   k_moba_pool  - fp32 block means, one workgroup per (block, 32-key chunk),
-//                  coalesced 16-byte key loads; the last chunk to finish
-//                  reduces the chunk sums in fixed order (deterministic);
-//   k_moba_gate  - one thread per (row, query head): fp32 scores over the
-//                  row's candidate blocks, register top-k (score desc, ties to
-//                  the lower block), own block appended, ascending output.
+//   k_moba_pool  - fp32 block means (and their bf16 high/low split), one
+//                  workgroup per (block, key head), coalesced 16-byte loads,
+//                  fixed-order LDS reduction (deterministic);
+//   k_moba_gate_mfma - bf16: 16 rows x 16 blocks per MFMA, per-row register
+//                  top-k (score desc, ties to the lower block), own block
+//                  appended, ascending output;
+//   k_moba_gate  - fp32 and other shapes: one thread per (row, query head).
 #include <float.h>
 
 #include "common.hpp"
@@ -26,14 +27,11 @@ namespace csa {
 namespace {
 
 constexpr int kPoolThreads = 256;
-constexpr int kPoolChunk = 32;  // keys per pooling workgroup
 constexpr int kGateThreads = 256;
 
 struct MobaWs {
   BlockTable bt;
   int32_t* need;    // [n_seq]
-  int32_t* arrive;  // [n_blocks]
-  float* partial;   // [n_blocks, n_chunks, hkv*d]
   float* mu;        // [n_blocks, hkv*d]
   __bf16* mu_hi;    // [n_blocks, hkv*d]  bf16 split of mu (high part)
   __bf16* mu_lo;    // [n_blocks, hkv*d]  (low part)
@@ -45,11 +43,7 @@ MobaWs carve_moba(void* base, int n_seq, int n_blocks, int hkv, int d, int block
   w.bt.blk_off = c.take<int32_t>(n_seq + 1);
   w.bt.blocks = c.take<int2>(n_blocks);
   w.bt.blk_seq = c.take<int32_t>(n_blocks);
-  // need[] and arrive[] are adjacent so one fill clears both
-  w.need = c.take<int32_t>((size_t)n_seq + n_blocks);
-  w.arrive = w.need + n_seq;
-  const int n_chunks = (block_size + kPoolChunk - 1) / kPoolChunk;
-  w.partial = c.take<float>((size_t)n_blocks * n_chunks * hkv * d);
+  w.need = c.take<int32_t>(n_seq);
   w.mu = c.take<float>((size_t)n_blocks * hkv * d);
   w.mu_hi = c.take<__bf16>((size_t)n_blocks * hkv * d);
   w.mu_lo = c.take<__bf16>((size_t)n_blocks * hkv * d);
@@ -58,12 +52,10 @@ MobaWs carve_moba(void* base, int n_seq, int n_blocks, int hkv, int d, int block
 
 size_t carve_bytes(int n_seq, int n_blocks, int hkv, int d, int block_size) {
   Carver c(nullptr);
-  const int n_chunks = (block_size + kPoolChunk - 1) / kPoolChunk;
   c.take<int32_t>(n_seq + 1);
   c.take<int2>(n_blocks);
   c.take<int32_t>(n_blocks);
-  c.take<int32_t>((size_t)n_seq + n_blocks);
-  c.take<float>((size_t)n_blocks * n_chunks * hkv * d);
+  c.take<int32_t>(n_seq);
   c.take<float>((size_t)n_blocks * hkv * d);
   c.take<__bf16>((size_t)n_blocks * hkv * d);
   c.take<__bf16>((size_t)n_blocks * hkv * d);
@@ -93,77 +85,50 @@ __global__ void k_moba_need(DevLayout L, int block_size, const int32_t* __restri
   }
 }
 
+// One workgroup per (block, key head): D/8 lanes cover a key row with 16-byte
+// loads, the other lanes stride over the block's keys, and the partial sums
+// are reduced through LDS in a fixed order (deterministic, no atomics, no
+// cross-workgroup fences).
 template <typename T>
 __global__ __launch_bounds__(kPoolThreads) void k_moba_pool(View k, BlockTable bt,
                                                             const int32_t* __restrict__ need,
-                                                            int32_t* __restrict__ arrive,
-                                                            float* __restrict__ partial,
                                                             float* __restrict__ mu,
                                                             __bf16* __restrict__ mu_hi,
-                                                            __bf16* __restrict__ mu_lo,
-                                                            int n_chunks) {
-  const int b = blockIdx.x / n_chunks;
-  const int chunk = blockIdx.x % n_chunks;
-  const int seq = bt.blk_seq[b];
-  if (b >= need[seq]) return;  // never a candidate of any local row
+                                                            __bf16* __restrict__ mu_lo) {
+  const int b = blockIdx.x / k.h;
+  const int g = blockIdx.x % k.h;
+  if (b >= need[bt.blk_seq[b]]) return;  // never a candidate of any local row
   const int2 blk = bt.blocks[b];
-  const int n_my_chunks = (blk.y + kPoolChunk - 1) / kPoolChunk;
-  if (chunk >= n_my_chunks) return;
-
-  const int hd = k.h * k.d;  // elements of one key row
-  const int groups = hd / 8;
-  const int lanes_k = groups >= kPoolThreads ? 1 : kPoolThreads / groups;
-  const int t0 = blk.x + chunk * kPoolChunk;
-  const int t1 = min(blk.x + blk.y, t0 + kPoolChunk);
-
-  __shared__ float s_red[kPoolThreads * 8];
-  __shared__ int s_last;
-  for (int base = 0; base < groups; base += kPoolThreads / lanes_k) {
-    const int span = min(groups - base, kPoolThreads / lanes_k);
-    const int tid = threadIdx.x;
-    const int eg = base + tid % span;
-    const int kl = tid / span;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (kl < lanes_k) {
-      const int e = eg * 8;
-      const int hh = e / k.d, dd = e % k.d;
-#pragma unroll 4
-      for (int t = t0 + kl; t < t1; t += lanes_k) {
-        float x[8];
-        load8(elem_ptr<T>(k, t, hh) + dd, x);
+  const int d = k.d;
+  const int units = d / 8;                // <= 32
+  const int lanes_k = kPoolThreads / units;
+  const int u = threadIdx.x % units;
+  const int kl = threadIdx.x / units;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int t1 = kl < lanes_k ? blk.x + blk.y : 0;  // spare threads add nothing
+#pragma unroll 8
+  for (int t = blk.x + kl; t < t1; t += lanes_k) {
+    float x[8];
+    load8(elem_ptr<T>(k, t, g) + u * 8, x);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] += x[j];
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) s_red[(kl * span + tid % span) * 8 + j] = acc[j];
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < span * 8; e += kPoolThreads) {
-      float s = 0.f;
-      for (int l = 0; l < lanes_k; ++l) s += s_red[(l * span) * 8 + e];
-      partial[((size_t)b * n_chunks + chunk) * hd + base * 8 + e] = s;
-    }
-    __syncthreads();
+    for (int j = 0; j < 8; ++j) acc[j] += x[j];
   }
-
-  // the last chunk of this block to arrive reduces the chunk sums in order
-  __threadfence();
-  if (threadIdx.x == 0) s_last = (atomicAdd(&arrive[b], 1) == n_my_chunks - 1);
+  __shared__ float s_red[kPoolThreads * 8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s_red[threadIdx.x * 8 + j] = acc[j];
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
   const float inv = 1.0f / (float)blk.y;
-  for (int e = threadIdx.x; e < hd; e += kPoolThreads) {
+  const size_t base = ((size_t)b * k.h + g) * d;
+  for (int e = threadIdx.x; e < d; e += kPoolThreads) {
     float s = 0.f;
-    for (int c = 0; c < n_my_chunks; ++c)
-      s += partial[((size_t)b * n_chunks + c) * hd + e];
+    for (int l = 0; l < lanes_k; ++l) s += s_red[(l * units + e / 8) * 8 + e % 8];
     const float m = s * inv;
-    mu[(size_t)b * hd + e] = m;
+    mu[base + e] = m;
     if (mu_hi) {
       // bf16 pair whose sum carries the fp32 mean to ~2^-17 relative
       const __bf16 hi = (__bf16)m;
-      mu_hi[(size_t)b * hd + e] = hi;
-      mu_lo[(size_t)b * hd + e] = (__bf16)(m - (float)hi);
+      mu_hi[base + e] = hi;
+      mu_lo[base + e] = (__bf16)(m - (float)hi);
     }
   }
 }
@@ -448,18 +413,17 @@ hipError_t launch_typed(const MobaGateArgs& a, hipStream_t stream) {
   const int n_seq = a.L.n_seq;
   MobaWs w = carve_moba(a.ws, n_seq, a.n_blocks, a.k.h, a.k.d, a.block_size);
   hipError_t e = launch_block_table(a.L.cu, n_seq, a.block_size, a.n_blocks, w.bt, w.need,
-                                    (int64_t)n_seq + a.n_blocks, stream);
+                                    n_seq, stream);
   if (e != hipSuccess) return e;
   if (a.L.n_q == 0) return hipSuccess;
   hipLaunchKernelGGL(k_moba_need, dim3((a.L.n_q + 255) / 256), dim3(256), 0, stream, a.L,
                      a.block_size, w.bt.blk_off, w.need);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int n_chunks = (a.block_size + kPoolChunk - 1) / kPoolChunk;
   const bool use_mfma = a.dtype == CSA_BF16 && (a.q.d == 64 || a.q.d == 128 || a.q.d == 256);
   if (a.n_blocks > 0) {
-    hipLaunchKernelGGL((k_moba_pool<T>), dim3(a.n_blocks * n_chunks), dim3(kPoolThreads), 0,
-                       stream, a.k, w.bt, w.need, w.arrive, w.partial, w.mu,
-                       use_mfma ? w.mu_hi : nullptr, use_mfma ? w.mu_lo : nullptr, n_chunks);
+    hipLaunchKernelGGL((k_moba_pool<T>), dim3(a.n_blocks * a.k.h), dim3(kPoolThreads), 0,
+                       stream, a.k, w.bt, w.need, w.mu, use_mfma ? w.mu_hi : nullptr,
+                       use_mfma ? w.mu_lo : nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (use_mfma) {
