@@ -27,6 +27,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
   k.out = a.out;
   k.lse = a.lse;
   if (attn_block_mfma_supported(k, a.n_blocks)) return launch_attn_block_mfma(k, a.n_blocks, a.ws, stream);
+  if (attn_token_mfma_supported(k)) return launch_attn_token_mfma(k, stream);
   return launch_attn_generic(k, stream);
 }
 

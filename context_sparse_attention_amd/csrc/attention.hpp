@@ -26,4 +26,9 @@ size_t attn_block_mfma_ws_bytes(int n_q, int n_seq, int n_blocks, int hq, int hk
 hipError_t launch_attn_block_mfma(const AttnKernelArgs& a, int n_blocks, void* ws,
                                   hipStream_t stream);
 
+// bf16 token mode with one index row per query token, (Dqk, Dv) in
+// {(576, 512), (128, 128), (64, 64)}, Hq / Hkv in {32, 64, 128}, positive scale.
+bool attn_token_mfma_supported(const AttnKernelArgs& a);
+hipError_t launch_attn_token_mfma(const AttnKernelArgs& a, hipStream_t stream);
+
 }  // namespace csa

@@ -1,0 +1,293 @@
+// Token-mode sparse shard attention on the matrix cores (bf16 MFMA, gfx950).
+//
+// Megatron-LM PR #3674 ("[1/2] Enable DSA CP, THD with absorbed MLA",
+// Description and sequence diagram): each query token attends to the top-k key
+// tokens its indexer picked, and with absorbed MLA all query heads share one
+// latent key head whose first columns are also the value.  Megatron-LM issue
+// #4878 ("Strategy: allgather CP mode"): the sparse kernel iterates only over
+// the top-k indices, never materialising the full score matrix.
+//
+// One workgroup per (query token, key head) with the G = Hq / Hkv query heads
+// of that key head as the 32-wide query tiles of G / 32 waves.  The token's
+// selected keys are gathered 32 at a time into a row-major LDS tile (padded
+// rows plus a one-bit unit swizzle: conflict-free for both read patterns).
+// S^T = K Q^T runs on 32x32x16 bf16 MFMA with Q^T in registers; the softmax
+// state lives in the lane of its query.  O^T = V^T P^T reads V^T straight from
+// the row-major tile with the transposing LDS read (ds_read_b64_tr_b16): in a
+// 16-lane group, lane c addressing 4 values of key kb + c/4 at value column
+// dvb + 4 (c % 4) makes lane t receive column dvb + t of keys kb .. kb + 3.
+// When the value aliases the key (absorbed MLA) no second tile exists at all.
+// The running maximum is raised only when a score exceeds it by 2^8 (scores
+// stay bounded by 2^8 in between), so the 16 x Dv/32 accumulators are rarely
+// rescaled.  Chunk summaries merge exactly as in "Context parallel attention:
+// exchange keys and merge softmax globally" (chunk summary paragraph).
+#include "attention.hpp"
+
+namespace csa {
+
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTK = 32;          // gathered keys per tile
+constexpr float kLazy = 8.0f;    // log2 headroom before the running max moves
+constexpr float kLn2 = 0.69314718055994531f;
+
+template <int DQK, int DV, bool ALIAS>
+struct TokLds {
+  static constexpr int kPitch = DQK + 16;  // bf16 elements per K row
+  static constexpr int kVPitch = DV + 16;
+  __bf16 k[2][kTK * kPitch];
+  __bf16 v[ALIAS ? 1 : 2][ALIAS ? 8 : kTK * kVPitch];
+};
+
+// byte offset of element e (a multiple of 4) of row r in a padded, swizzled tile
+template <int PITCH>
+__device__ __forceinline__ int tile_off(int r, int e) {
+  const int unit = (e >> 3) ^ ((r >> 2) & 1);
+  return r * PITCH * 2 + unit * 16 + (e & 7) * 2;
+}
+
+__device__ __forceinline__ bf16x4 read_tr(const __bf16* lds_base, int byte_off) {
+  typedef __attribute__((address_space(3))) s16x4* lds_ptr;
+  typedef __attribute__((address_space(3))) char* lds_bytes;
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_ptr)((lds_bytes)(const_cast<__bf16*>(lds_base)) + byte_off));
+  return __builtin_bit_cast(bf16x4, x);
+}
+
+// Gathers one tile straight into LDS with global_load_lds_dwordx4: an
+// instruction fills 1 KiB of LDS, lane l writing bytes [16 l, 16 l + 16) of
+// it, so each lane loads the 16 bytes that the padded, swizzled layout puts at
+// its destination (pad slots re-read unit 0 of their row).  The tile sizes are
+// whole KiBs (32 rows of 2 (D + 16) bytes).  No registers hold the data.
+// x * s for an accumulator value that stays in an accumulator register
+// (VALU instructions cannot read accumulator registers directly).
+__device__ __forceinline__ float acc_scale(float x, float s) {
+  float y, t;
+  asm volatile(
+      "v_accvgpr_read_b32 %1, %2\n\t"
+      "v_mul_f32 %1, %1, %3\n\t"
+      "v_accvgpr_write_b32 %0, %1"
+      : "=a"(y), "=&v"(t)
+      : "a"(x), "v"(s));
+  return y;
+}
+
+template <int D>
+__device__ __forceinline__ void issue_tile(const View& T, int g, const int* keys, __bf16* tile,
+                                           int wave, int nwaves) {
+  constexpr int kPitchB = 2 * (D + 16);
+  constexpr int kChunks = kTK * kPitchB / 1024;
+  static_assert(kTK * kPitchB % 1024 == 0, "tile must be whole KiBs");
+  const int lane = threadIdx.x & (kWave - 1);
+  typedef __attribute__((address_space(3))) char* lds_bytes;
+  for (int ch = wave; ch < kChunks; ch += nwaves) {
+    const int byte = ch * 1024 + lane * 16;
+    const int row = byte / kPitchB;
+    const int pu = (byte - row * kPitchB) >> 4;
+    const int u = pu < D / 8 ? (pu ^ ((row >> 2) & 1)) : 0;
+    const __bf16* src = elem_ptr<__bf16>(T, keys[row], g) + u * 8;
+    __builtin_amdgcn_global_load_lds(
+        (const void*)src, (__attribute__((address_space(3))) void*)((lds_bytes)(void*)tile + ch * 1024),
+        16, 0, 0);
+  }
+}
+
+template <int DQK, int DV, bool ALIAS, int NW, typename TO>
+__global__ __launch_bounds__(NW * kWave, 1) void k_tok_attn(AttnKernelArgs a) {
+  using Lds = TokLds<DQK, DV, ALIAS>;
+  __shared__ Lds s;
+  // slot keys of tiles kt, kt + 1 and kt + 2 live in distinct slots (kt % 3)
+  __shared__ int s_keys[3][kTK];
+  __shared__ int s_valid[3][kTK];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int half = lane >> 5;
+  const int hkv = a.k.h;
+  const int i = blockIdx.x / hkv;
+  const int g = blockIdx.x % hkv;
+  const int G = a.q.h / hkv;
+  const int head = g * G + wave * 32 + (lane & 31);
+  const RowKeys r = row_keys(a.L, i);
+  const int W = a.idx_width;
+  const int32_t* slots = a.idx + (int64_t)i * W;
+  const float c = a.scale_log2;
+
+  bf16x8 qf[DQK / 16];
+  {
+    const __bf16* qp = elem_ptr<__bf16>(a.q, i, head);
+#pragma unroll
+    for (int ks = 0; ks < DQK / 16; ++ks)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * half);
+  }
+  f32x16 o[DV / 32];
+#pragma unroll
+  for (int dt = 0; dt < DV / 32; ++dt) o[dt] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+
+  const int n_kt = r.valid ? (W + kTK - 1) / kTK : 0;
+  auto fetch_keys = [&](int kt) {
+    if (threadIdx.x < kTK) {
+      const int j = kt * kTK + threadIdx.x;
+      const int key = j < W ? slots[j] : -1;
+      const bool ok = key >= r.lo && key <= r.hi;
+      s_keys[kt % 3][threadIdx.x] = ok ? key : r.lo;  // masked slots read a valid row
+      s_valid[kt % 3][threadIdx.x] = ok;
+    }
+  };
+  auto issue = [&](int kt) {
+    issue_tile<DQK>(a.k, g, s_keys[kt % 3], s.k[kt & 1], wave, NW);
+    if constexpr (!ALIAS) issue_tile<DV>(a.v, g, s_keys[kt % 3], s.v[ALIAS ? 0 : (kt & 1)], wave, NW);
+  };
+  if (n_kt > 0) {
+    fetch_keys(0);
+    if (n_kt > 1) fetch_keys(1);
+    __syncthreads();
+    issue(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    const int ks3 = kt % 3;
+    if (kt + 1 < n_kt) issue(kt + 1);  // lands in the other buffer while this one is used
+    // S^T = K Q^T: lane holds keys 8 (j / 4) + 4 half + (j % 4) of its query
+    const char* kb = reinterpret_cast<const char*>(s.k[buf]);
+    f32x16 sc = f32x16{};
+    {
+      const int row = lane & 31;
+#pragma unroll
+      for (int ks = 0; ks < DQK / 16; ++ks) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(
+            kb + tile_off<Lds::kPitch>(row, 16 * ks + 8 * half));
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sc, 0, 0, 0);
+        if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int kl = 8 * (j >> 2) + 4 * half + (j & 3);
+      if (!s_valid[ks3][kl]) sc[j] = -INFINITY;
+      mx = fmaxf(mx, sc[j]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * c;
+    const bool need = mx > m + kLazy || (m == -INFINITY && mx > -INFINITY);
+    if (__any(need)) {
+      const float mn = need ? mx : m;
+      const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DV / 32; ++dt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[dt][j] = acc_scale(o[dt][j], alpha);
+      m = mn;
+    }
+    const float mu = (m == -INFINITY) ? 0.f : m;
+    float rs = 0.f;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float p = exp2f(fmaf(sc[j], c, -mu));
+      rs += p;
+      pb[j >> 3][j & 7] = (__bf16)p;
+    }
+    rs += __shfl_xor(rs, 32, kWave);
+    l += rs;
+    // O^T += V^T P^T with V^T read transposed from the row-major tile
+    const __bf16* vbase = ALIAS ? s.k[buf] : s.v[ALIAS ? 0 : buf];
+    constexpr int VP = ALIAS ? Lds::kPitch : Lds::kVPitch;
+    const int c16 = lane & 15;
+    const int grp = lane >> 4;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int ka = 16 * st + 4 * half + (c16 >> 2);
+      const int kb2 = ka + 8;
+#pragma unroll
+      for (int dt = 0; dt < DV / 32; ++dt) {
+        const int dv = dt * 32 + 16 * (grp & 1) + 4 * (c16 & 3);
+        const bf16x4 lo = read_tr(vbase, tile_off<VP>(ka, dv));
+        const bf16x4 hi = read_tr(vbase, tile_off<VP>(kb2, dv));
+        const bf16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[st], o[dt], 0, 0, 0);
+        if ((dt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (kt + 2 < n_kt) fetch_keys(kt + 2);
+    __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct loads have landed
+    __syncthreads();
+  }
+
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  TO* out = reinterpret_cast<TO*>(a.out) + ((int64_t)i * a.q.h + head) * DV;
+#pragma unroll
+  for (int dt = 0; dt < DV / 32; ++dt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int d = dt * 32 + 8 * jj + 4 * half;
+      if constexpr (sizeof(TO) == 4) {
+        *reinterpret_cast<float4*>(out + d) =
+            make_float4(o[dt][4 * jj] * inv, o[dt][4 * jj + 1] * inv, o[dt][4 * jj + 2] * inv,
+                        o[dt][4 * jj + 3] * inv);
+      } else {
+        bf16x4 x = {(__bf16)(o[dt][4 * jj] * inv), (__bf16)(o[dt][4 * jj + 1] * inv),
+                    (__bf16)(o[dt][4 * jj + 2] * inv), (__bf16)(o[dt][4 * jj + 3] * inv)};
+        *reinterpret_cast<bf16x4*>(out + d) = x;
+      }
+    }
+  if (a.lse && half == 0)
+    a.lse[(int64_t)i * a.q.h + head] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+}
+
+template <int DQK, int DV, bool ALIAS, typename TO>
+hipError_t launch_shape(const AttnKernelArgs& a, hipStream_t stream) {
+  const int G = a.q.h / a.k.h;
+  const dim3 grid((unsigned)a.L.n_q * a.k.h);
+  if (G == 32)
+    hipLaunchKernelGGL((k_tok_attn<DQK, DV, ALIAS, 1, TO>), grid, dim3(64), 0, stream, a);
+  else if (G == 64)
+    hipLaunchKernelGGL((k_tok_attn<DQK, DV, ALIAS, 2, TO>), grid, dim3(128), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_tok_attn<DQK, DV, ALIAS, 4, TO>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int DQK, int DV, typename TO>
+hipError_t launch_alias(const AttnKernelArgs& a, hipStream_t stream) {
+  const bool alias = a.v.data == a.k.data && a.v.stride_n == a.k.stride_n &&
+                     a.v.stride_h == a.k.stride_h;
+  if (alias) return launch_shape<DQK, DV, true, TO>(a, stream);
+  return launch_shape<DQK, DV, false, TO>(a, stream);
+}
+
+template <typename TO>
+hipError_t launch_out(const AttnKernelArgs& a, hipStream_t stream) {
+  const int dqk = a.q.d, dv = a.v.d;
+  if (dqk == 576 && dv == 512) return launch_alias<576, 512, TO>(a, stream);
+  if (dqk == 128 && dv == 128) return launch_alias<128, 128, TO>(a, stream);
+  return launch_alias<64, 64, TO>(a, stream);
+}
+
+}  // namespace
+
+bool attn_token_mfma_supported(const AttnKernelArgs& a) {
+  const int G = a.q.h / a.k.h;
+  const int dqk = a.q.d, dv = a.v.d;
+  const bool shape = (dqk == 576 && dv == 512) || (dqk == 128 && dv == 128) ||
+                     (dqk == 64 && dv == 64);
+  return a.mode == CSA_SEL_TOKEN && a.dtype == CSA_BF16 && a.idx_heads == 1 && shape &&
+         (G == 32 || G == 64 || G == 128) && a.scale_log2 > 0.f &&
+         (int64_t)a.L.n_q * a.k.h < (int64_t)1 << 31;
+}
+
+hipError_t launch_attn_token_mfma(const AttnKernelArgs& a, hipStream_t stream) {
+  if (a.L.n_q == 0) return hipSuccess;
+  if (a.out_dtype == CSA_BF16) return launch_out<__bf16>(a, stream);
+  return launch_out<float>(a, stream);
+}
+
+}  // namespace csa

@@ -8,14 +8,16 @@
 // key j for row i: sum_h w[i,h] * max(0, iq[i,h] . ik[j]) over the permitted
 // keys j in [lo_i, pos_i] only ("logits cleaning": nothing else is written).
 //
-// Two kernels:
-//   k_dsa_logits - one workgroup per (row, 256-key tile): the row's indexer
+// Kernels:
+//   k_dsa_logits_mfma - bf16, D_I in {64, 128}, H_I a multiple of 32 up to 128:
+//                  32x32x16 bf16 MFMA over LDS-staged key tiles (below);
+//   k_dsa_logits - other cases: one workgroup per (row, 256-key tile): the row's indexer
 //                  queries sit in LDS, each thread holds one key in registers
 //                  and reduces the 64 heads in fp32;
-//   k_dsa_select - one workgroup per row: 4-pass 8-bit radix select of the
-//                  k-th largest logit on order-preserving uint32 keys, then an
-//                  index-order compaction that takes every larger logit and
-//                  the lowest-index equal ones (ties to the lower index).
+//   k_dsa_select - one workgroup per row, row cached in LDS: 4-pass 8-bit radix
+//                  select of the k-th largest logit on order-preserving uint32
+//                  keys, then an index-order compaction that takes every larger
+//                  logit and the lowest-index equal ones (ties to the lower index).
 #include "common.hpp"
 
 namespace csa {
@@ -23,7 +25,6 @@ namespace csa {
 namespace {
 
 constexpr int kLogitThreads = 256;
-constexpr int kSelectThreads = 1024;
 constexpr int kMaxIndexerElems = 8192;  // H_I * D_I held in LDS as fp32
 
 template <typename T, int DI_MAX>
@@ -71,30 +72,159 @@ __global__ __launch_bounds__(kLogitThreads) void k_dsa_logits(View iq, View ik,
   logits[(int64_t)i * L.n_kv + j] = acc;
 }
 
-// Exclusive prefix count of a per-thread flag across the workgroup, plus the total.
-__device__ inline int block_excl_count(bool flag, int* s_wave, int* total) {
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr int kLgWaves = 8;                 // query tokens per workgroup (one per wave)
+constexpr int kLgThreads = kLgWaves * kWave;
+constexpr int kLgKeys = 64;                 // keys per LDS tile
+constexpr int kLgChunk = 2048;              // keys per workgroup
+
+// bf16 indexer logits on the matrix cores.  Wave w owns query token
+// t0 + w: its H_I x D_I indexer queries sit in registers as the A operand
+// (rows = heads), each 64-key ik tile is staged once in LDS for the eight
+// tokens of the workgroup and read as the B operand (columns = keys), so the
+// 32x32 accumulator gives a lane one key column and 16 heads per M tile; the
+// ReLU and head weights are applied in-lane and the two lane halves are added.
+// Only permitted keys [lo_i, pos_i] are written.
+template <int DI, int MT>
+__global__ __launch_bounds__(kLgThreads, 2) void k_dsa_logits_mfma(View iq, View ik,
+                                                                   const float* __restrict__ w,
+                                                                   int64_t w_stride, DevLayout L,
+                                                                   float* __restrict__ logits) {
+  __shared__ __bf16 s_k[2][kLgKeys * DI];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const uint64_t ballot = __ballot(flag);
-  const int before_in_wave = __popcll(ballot & ((1ull << lane) - 1ull));
-  if (lane == 0) s_wave[wave] = __popcll(ballot);
+  const int half = lane >> 5;
+  const int t0 = blockIdx.x * kLgWaves;
+  const int row = t0 + wave;
+  int lo = 0, hi = -1;
+  if (row < L.n_q) {
+    const RowKeys r = row_keys(L, row);
+    if (r.valid) {
+      lo = r.lo;
+      hi = r.hi;
+    }
+  }
+  // key range of the workgroup: the union of its tokens' ranges, cut to this chunk
+  __shared__ int s_lo, s_hi;
+  if (threadIdx.x == 0) {
+    s_lo = INT32_MAX;
+    s_hi = -1;
+  }
+  __syncthreads();
+  if (lane == 0 && hi >= lo) {
+    atomicMin(&s_lo, lo);
+    atomicMax(&s_hi, hi);
+  }
+  __syncthreads();
+  const int k_begin = max(s_lo, blockIdx.y * kLgChunk);
+  const int k_end = min(s_hi + 1, (blockIdx.y + 1) * kLgChunk);
+  if (k_begin >= k_end) return;  // whole workgroup
+
+  constexpr int KS = DI / 16;
+  bf16x8 a[MT][KS];
+  float wr[MT][16];
+  const int rowc = row < L.n_q ? row : t0;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const __bf16* qp = elem_ptr<__bf16>(iq, rowc, mt * 32 + (lane & 31));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      a[mt][ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * half);
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      wr[mt][j] = w[(int64_t)rowc * w_stride + mt * 32 + 8 * (j >> 2) + 4 * half + (j & 3)];
+  }
+
+  constexpr int kUnits = DI / 8;
+  constexpr int kRowsPerPass = kLgThreads / kUnits;
+  constexpr int kPasses = kLgKeys / kRowsPerPass;
+  const int n_kt = (k_end - k_begin + kLgKeys - 1) / kLgKeys;
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    const int key0 = k_begin + kt * kLgKeys;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int r = p * kRowsPerPass + threadIdx.x / kUnits;
+      const int u = threadIdx.x % kUnits;
+      const int key = min(key0 + r, k_end - 1);
+      const uint4 x = *reinterpret_cast<const uint4*>(elem_ptr<__bf16>(ik, key, 0) + u * 8);
+      *reinterpret_cast<uint4*>(&s_k[buf][r * DI + ((u ^ (r & 7)) << 3)]) = x;
+    }
+    __syncthreads();
+    if (hi >= lo && key0 <= hi) {
+#pragma unroll
+      for (int nt = 0; nt < kLgKeys / 32; ++nt) {
+        const int r = nt * 32 + (lane & 31);
+        f32x16 acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 b =
+              *reinterpret_cast<const bf16x8*>(&s_k[buf][r * DI + (((2 * ks + half) ^ (r & 7)) << 3)]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][ks], b, acc[mt], 0, 0, 0);
+        }
+        float v = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) v = fmaf(wr[mt][j], fmaxf(acc[mt][j], 0.f), v);
+        v += __shfl_xor(v, 32, kWave);
+        const int key = key0 + r;
+        if (half == 0 && key >= lo && key <= hi && key < k_end)
+          logits[(int64_t)row * L.n_kv + key] = v;
+      }
+    }
+    // the barrier of the next tile orders these reads before buffer reuse
+  }
+}
+
+constexpr int kSelThreads = 256;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kSelCache = 12288;  // row keys cached in LDS (48 KiB)
+constexpr int kSelPer = 8;        // elements per thread in the compaction
+
+// Exclusive prefix sum of one int per thread across the workgroup, plus the total.
+__device__ inline int sel_excl_scan(int x, int* s_wave, int* total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) s_wave[wave] = incl;
   __syncthreads();
   int before = 0, all = 0;
-  for (int w = 0; w < kSelectThreads / kWave; ++w) {
-    const int c = s_wave[w];
-    if (w < wave) before += c;
-    all += c;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    if (w < wave) before += s_wave[w];
+    all += s_wave[w];
   }
   __syncthreads();
   *total = all;
-  return before + before_in_wave;
+  return before + incl - x;
 }
 
-__global__ __launch_bounds__(kSelectThreads) void k_dsa_select(DevLayout L, int topk,
-                                                               const float* __restrict__ logits,
-                                                               int32_t* __restrict__ idx,
-                                                               float* __restrict__ score) {
+// One workgroup per row.  The row's logits become order-preserving uint32 keys
+// (cached in LDS when the row fits); four 8-bit radix passes find the key T of
+// the k-th largest logit and how many keys equal to T are taken; a compaction
+// in index order then writes every key > T and the lowest-index keys == T.
+__global__ __launch_bounds__(kSelThreads) void k_dsa_select(DevLayout L, int topk,
+                                                            const float* __restrict__ logits,
+                                                            int32_t* __restrict__ idx,
+                                                            float* __restrict__ score) {
+  __shared__ uint32_t s_key[kSelCache];
+  __shared__ int s_hist[256];
+  __shared__ int s_wave[kSelWaves];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_remaining;
   const int i = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
   const RowKeys r = row_keys(L, i);
   const int n = r.valid ? r.hi - r.lo + 1 : 0;
   const float* row = logits + (int64_t)i * L.n_kv + r.lo;
@@ -102,36 +232,76 @@ __global__ __launch_bounds__(kSelectThreads) void k_dsa_select(DevLayout L, int 
   float* out_s = score ? score + (int64_t)i * topk : nullptr;
 
   if (n <= topk) {
-    for (int t = threadIdx.x; t < topk; t += kSelectThreads) {
+    for (int t = threadIdx.x; t < topk; t += kSelThreads) {
       out[t] = t < n ? r.lo + t : -1;
       if (out_s) out_s[t] = t < n ? row[t] : -INFINITY;
     }
     return;
   }
+  const bool cached = n <= kSelCache;
+  if (cached)
+    for (int t = threadIdx.x; t < n; t += kSelThreads) s_key[t] = float_key(row[t]);
 
-  __shared__ int s_hist[256];
-  __shared__ int s_wave[kSelectThreads / kWave];
-  __shared__ uint32_t s_prefix;
-  __shared__ int s_remaining;
   uint32_t prefix = 0, mask = 0;
   int remaining = topk;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int b = threadIdx.x; b < 256; b += kSelectThreads) s_hist[b] = 0;
+    for (int b = threadIdx.x; b < 256; b += kSelThreads) s_hist[b] = 0;
     __syncthreads();
-    for (int t = threadIdx.x; t < n; t += kSelectThreads) {
-      const uint32_t u = float_key(row[t]);
-      if ((u & mask) == prefix) atomicAdd(&s_hist[(u >> shift) & 255u], 1);
+    for (int base = 0; base < n; base += kSelThreads) {
+      const int t = base + threadIdx.x;
+      bool act = false;
+      uint32_t dg = 0;
+      if (t < n) {
+        const uint32_t u = cached ? s_key[t] : float_key(row[t]);
+        act = (u & mask) == prefix;
+        dg = (u >> shift) & 255u;
+      }
+      if (shift == 24) {
+        // leading bytes of nearby logits coincide: one atomic per distinct digit per wave
+        uint64_t pending = __ballot(act);
+        while (pending) {
+          const int leader = __ffsll((unsigned long long)pending) - 1;
+          const uint32_t dl = __shfl(dg, leader, kWave);
+          const uint64_t same = __ballot(act && dg == dl);
+          if (lane == leader) atomicAdd(&s_hist[dl], __popcll(same));
+          pending &= ~same;
+          act = act && dg != dl;
+        }
+      } else if (act) {
+        atomicAdd(&s_hist[dg], 1);
+      }
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      int above = 0;
-      int digit = 255;
-      for (; digit > 0; --digit) {
-        if (above + s_hist[digit] >= remaining) break;
-        above += s_hist[digit];
+    if (threadIdx.x < kWave) {
+      // lane l owns digits 255-4l .. 252-4l; find the digit holding the remaining-th key
+      int c[4], sum = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = s_hist[255 - 4 * lane - j];
+        sum += c[j];
       }
-      s_prefix = prefix | ((uint32_t)digit << shift);
-      s_remaining = remaining - above;
+      int incl = sum;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += y;
+      }
+      int above = incl - sum;
+      int found = -1, above_found = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (found < 0 && above + c[j] >= remaining) {
+          found = 255 - 4 * lane - j;
+          above_found = above;
+        }
+        above += c[j];
+      }
+      const uint64_t hit = __ballot(found >= 0);
+      const int first = __ffsll((unsigned long long)hit) - 1;
+      if (lane == first) {
+        s_prefix = prefix | ((uint32_t)found << shift);
+        s_remaining = remaining - above_found;
+      }
     }
     __syncthreads();
     prefix = s_prefix;
@@ -139,26 +309,40 @@ __global__ __launch_bounds__(kSelectThreads) void k_dsa_select(DevLayout L, int 
     mask |= 255u << shift;
     __syncthreads();
   }
-  // prefix is the key of the k-th largest logit; `remaining` equal keys are taken
+
+  // compaction in index order: keys > prefix, then the first `remaining` keys == prefix
   int eq_carry = 0, out_carry = 0;
-  for (int base = 0; base < n; base += kSelectThreads) {
-    const int t = base + threadIdx.x;
-    uint32_t u = 0;
-    float x = 0.f;
-    if (t < n) {
-      x = row[t];
-      u = float_key(x);
+  for (int base = 0; base < n; base += kSelThreads * kSelPer) {
+    const int t0 = base + threadIdx.x * kSelPer;
+    uint32_t u[kSelPer];
+    int n_eq = 0;
+#pragma unroll
+    for (int j = 0; j < kSelPer; ++j) {
+      const int t = t0 + j;
+      u[j] = t < n ? (cached ? s_key[t] : float_key(row[t])) : 0u;
+      n_eq += (t < n && u[j] == prefix);
     }
-    const bool gt = t < n && u > prefix;
-    const bool eq = t < n && u == prefix;
     int eq_total;
-    const int eq_rank = eq_carry + block_excl_count(eq, s_wave, &eq_total);
-    const bool sel = gt || (eq && eq_rank < remaining);
+    int eq_rank = eq_carry + sel_excl_scan(n_eq, s_wave, &eq_total);
+    bool sel[kSelPer];
+    int n_sel = 0;
+#pragma unroll
+    for (int j = 0; j < kSelPer; ++j) {
+      const int t = t0 + j;
+      const bool eq = t < n && u[j] == prefix;
+      sel[j] = t < n && (u[j] > prefix || (eq && eq_rank < remaining));
+      eq_rank += eq;
+      n_sel += sel[j];
+    }
     int sel_total;
-    const int slot = out_carry + block_excl_count(sel, s_wave, &sel_total);
-    if (sel) {
-      out[slot] = r.lo + t;
-      if (out_s) out_s[slot] = x;
+    int slot = out_carry + sel_excl_scan(n_sel, s_wave, &sel_total);
+#pragma unroll
+    for (int j = 0; j < kSelPer; ++j) {
+      if (sel[j]) {
+        out[slot] = r.lo + t0 + j;
+        if (out_s) out_s[slot] = row[t0 + j];
+        ++slot;
+      }
     }
     eq_carry += eq_total;
     out_carry += sel_total;
@@ -169,14 +353,34 @@ template <typename T>
 hipError_t launch_typed(const DsaArgs& a, hipStream_t stream) {
   float* logits = static_cast<float*>(a.ws);
   if (a.L.n_q == 0) return hipSuccess;
-  const int tiles = (a.L.n_kv + kLogitThreads - 1) / kLogitThreads;
-  if (tiles > 0) {
-    hipLaunchKernelGGL((k_dsa_logits<T, 128>), dim3(tiles, a.L.n_q), dim3(kLogitThreads), 0,
-                       stream, a.iq, a.ik, a.w, a.w_stride, a.L, logits);
+  const int hi = a.iq.h, di = a.iq.d;
+  const bool mfma = a.dtype == CSA_BF16 && (di == 64 || di == 128) && hi % 32 == 0 && hi <= 128;
+  if (mfma && a.L.n_kv > 0) {
+    const dim3 grid((a.L.n_q + kLgWaves - 1) / kLgWaves, (a.L.n_kv + kLgChunk - 1) / kLgChunk);
+    const dim3 block(kLgThreads);
+#define CSA_LG(DI, MT) \
+  hipLaunchKernelGGL((k_dsa_logits_mfma<DI, MT>), grid, block, 0, stream, a.iq, a.ik, a.w, \
+                     a.w_stride, a.L, logits)
+    if (di == 64) {
+      if (hi == 32) CSA_LG(64, 1); else if (hi == 64) CSA_LG(64, 2);
+      else if (hi == 96) CSA_LG(64, 3); else CSA_LG(64, 4);
+    } else {
+      if (hi == 32) CSA_LG(128, 1); else if (hi == 64) CSA_LG(128, 2);
+      else if (hi == 96) CSA_LG(128, 3); else CSA_LG(128, 4);
+    }
+#undef CSA_LG
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  } else {
+    const int tiles = (a.L.n_kv + kLogitThreads - 1) / kLogitThreads;
+    if (tiles > 0) {
+      hipLaunchKernelGGL((k_dsa_logits<T, 128>), dim3(tiles, a.L.n_q), dim3(kLogitThreads), 0,
+                         stream, a.iq, a.ik, a.w, a.w_stride, a.L, logits);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
-  hipLaunchKernelGGL(k_dsa_select, dim3(a.L.n_q), dim3(kSelectThreads), 0, stream, a.L,
+  hipLaunchKernelGGL(k_dsa_select, dim3(a.L.n_q), dim3(kSelThreads), 0, stream, a.L,
                      a.topk, logits, a.idx, a.score);
   return hipGetLastError();
 }
