@@ -54,23 +54,30 @@ def permitted_bounds(w):
     return lo, pos, end, ok
 
 
-def effective_pairs(w, idx):
-    """Selected permitted (query head, key) pairs of the step."""
+def effective_pairs(w, idx, split=False):
+    """Selected permitted (query head, key) pairs of the step.
+
+    With split=True (block mode) also returns the pairs of full blocks lying
+    strictly before the row's position, the work of the query-tile kernel.
+    """
     lo, pos, end, ok = permitted_bounds(w)
     idx = idx.astype(np.int64)
     if idx.ndim == 2:
         idx = idx[:, None, :]
     lo_, pos_, end_ = lo[:, None, None], pos[:, None, None], end[:, None, None]
     valid = ok[:, None, None] & (idx >= lo_) & (idx <= pos_)
+    full = 0
     if w.mode == "block":
         valid &= ((idx - lo_) % w.block_size) == 0
         n = np.minimum(np.minimum(idx + w.block_size, end_), pos_ + 1) - idx
         pairs = np.where(valid, n, 0).sum()
+        full = np.where(valid & (idx + w.block_size - 1 < pos_), n, 0).sum()
     else:
         pairs = valid.sum()
     if idx.shape[1] == 1:
         pairs *= w.hq
-    return int(pairs)
+        full *= w.hq
+    return (int(pairs), int(full)) if split else int(pairs)
 
 
 def selection_bytes(w):
@@ -188,12 +195,13 @@ def main():
         attend(select())
     torch.cuda.synchronize()
     idx_np = select().cpu().numpy()
-    pairs = effective_pairs(w, idx_np)
+    pairs, full_pairs = effective_pairs(w, idx_np, split=True)
     flops = pairs * 2.0 * (w.dqk + w.dv)
     sel_bytes = selection_bytes(w)
 
     stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    csa.trace_begin(4 * args.steps + 8)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -204,9 +212,14 @@ def main():
         ev[s][2].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    traced = csa.trace_collect()
+    csa.trace_begin(0)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     sel_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(args.steps)]
     att_ms = [ev[s][1].elapsed_time(ev[s][2]) for s in range(args.steps)]
+    kern = {}
+    for name, ms in traced:
+        kern.setdefault(name, []).append(ms)
 
     cold = None
     if not args.no_cold:
@@ -232,7 +245,27 @@ def main():
     att_med = float(np.median(att_ms))
     sel_med = float(np.median(sel_ms))
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-    achieved = flops / (att_med * 1e-3) / 1e12
+    # dominant attention kernel and the algorithmic flops of one launch
+    if "k_bm_tiles" in kern:
+        dom, dom_flops = "k_bm_tiles", full_pairs * 2.0 * (w.dqk + w.dv)
+    elif "k_tok_attn" in kern:
+        dom, dom_flops = "k_tok_attn", flops
+    else:
+        dom, dom_flops = "k_attn_generic", flops
+    dom_ms = float(np.mean(kern[dom])) if dom in kern else att_med
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    # dominant selection kernel
+    if w.mode == "block":
+        sk = "k_moba_gate_mfma" if "k_moba_gate_mfma" in kern else "k_moba_gate"
+        esz = 2 if w.dtype == "bf16" else 4
+        sk_work = w.n_q * w.hq * w.dqk * esz + w.n_q * w.hq * (w.topk + 1) * 4
+        sk_unit, sk_peak = "GB/s", PEAK_HBM_GBS
+    else:
+        sk = "k_dsa_logits_mfma" if "k_dsa_logits_mfma" in kern else "k_dsa_logits"
+        sk_work = sel_bytes["indexer_flops"]
+        sk_unit, sk_peak = "TFLOP/s", peak
+    sk_ms = float(np.mean(kern[sk])) if sk in kern else float("nan")
+    sk_rate = sk_work / (sk_ms * 1e-3) / (1e9 if sk_unit == "GB/s" else 1e12)
     result = {
         "metric": METRIC,
         "value": flops / (ms_per_step * 1e-3) / 1e12,
@@ -250,13 +283,18 @@ def main():
                    "hkv": w.hkv, "dqk": w.dqk, "dv": w.dv, "mode": w.mode,
                    "block_size": w.block_size, "topk": w.topk,
                    "effective_pairs": pairs, "effective_gflop": flops / 1e9},
-        "roofline": {"kernel": "sparse_attn_fwd_shard", "bound": "mfma",
-                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "kernel_ms": dom_ms, "kernel_gflop": dom_flops / 1e9},
         "stages": {"select_ms_median": sel_med, "attention_ms_median": att_med,
+                   "attention_TFLOPs": flops / (att_med * 1e-3) / 1e12,
+                   "attention_frac_peak": flops / (att_med * 1e-3) / 1e12 / peak,
                    "select_alg_bytes": sel_bytes["total"],
                    "select_GBs": sel_bytes["total"] / (sel_med * 1e-3) / 1e9,
                    "select_frac_hbm": sel_bytes["total"] / (sel_med * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                   "select_kernel": {"kernel": sk, "ms": sk_ms, "rate": sk_rate,
+                                     "unit": sk_unit, "frac": sk_rate / sk_peak},
+                   "kernels_ms": {k: float(np.mean(v)) for k, v in kern.items()},
                    "cold": cold},
     }
     if not args.no_cpu_baseline:

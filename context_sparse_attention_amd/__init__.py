@@ -15,6 +15,8 @@ from ._binding import (
     dsa_indexer_topk,
     sparse_attn_fwd_shard,
     summary_merge,
+    trace_begin,
+    trace_collect,
     library_path,
     lib,
     CSA_SEL_BLOCK,
@@ -28,6 +30,8 @@ __all__ = [
     "dsa_indexer_topk",
     "sparse_attn_fwd_shard",
     "summary_merge",
+    "trace_begin",
+    "trace_collect",
     "library_path",
     "lib",
     "CSA_SEL_BLOCK",

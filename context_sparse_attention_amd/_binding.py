@@ -12,7 +12,7 @@ library_path = os.path.join(_HERE, "libcsa.so")
 
 if not os.path.exists(library_path):
     raise ImportError(
-        f"{library_path} is not built; run `python -m context_sparse_attention_amd.build` "
+        f"{library_path} is not built; run `python context_sparse_attention_amd/build.py` "
         "(or __graft_entry__.build()) first. There is no fallback path.")
 
 lib = ctypes.CDLL(library_path)
@@ -62,6 +62,11 @@ lib.sparse_attn_fwd_shard_workspace_size.argtypes = [_LP, _i32, _i32, _i32, _i32
 lib.sparse_attn_fwd_shard.restype = ctypes.c_int
 lib.sparse_attn_fwd_shard.argtypes = [_T3, _T3, _T3, _LP, _i32, _P, _i32, _i32, _i32, _f32,
                                       _P, _i32, _P, _P, _sz, _P]
+lib.csa_trace_begin.restype = ctypes.c_int
+lib.csa_trace_begin.argtypes = [ctypes.c_int]
+lib.csa_trace_collect.restype = ctypes.c_int
+lib.csa_trace_collect.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                  ctypes.POINTER(ctypes.c_char_p), ctypes.c_int]
 lib.summary_merge.restype = ctypes.c_int
 lib.summary_merge.argtypes = [_i32, _i64, _i32, _P, _P, _P, _P, _P, _P, _P, _i32, _P, _P]
 
@@ -203,3 +208,16 @@ def summary_merge(m, l, z, finalize=True, merged=False, o_dtype=torch.float32):
                              CSA_BF16 if o_dtype == torch.bfloat16 else CSA_F32, _ptr(lse),
                              _stream()))
     return res
+
+
+def trace_begin(max_records):
+    """Record HIP event pairs around each call's dominant kernel (see csa.h)."""
+    _check(lib.csa_trace_begin(int(max_records)))
+
+
+def trace_collect(max_records=4096):
+    """[(kernel name, elapsed ms)] of the recorded launches, in order; rewinds the ring."""
+    ms = (ctypes.c_float * max_records)()
+    names = (ctypes.c_char_p * max_records)()
+    n = lib.csa_trace_collect(ms, names, max_records)
+    return [(names[i].decode(), float(ms[i])) for i in range(n)]

@@ -1,6 +1,7 @@
 """Build libcsa.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: ``python -m context_sparse_attention_amd.build`` (or ``build()`` from Python).
+Usage: ``python context_sparse_attention_amd/build.py`` (or ``__graft_entry__.build()``);
+run it by path: importing the package first would load the library being rebuilt.
 Objects go to ``_build/`` at the repository root; the shared library is written
 next to this file so that the Python binding finds it.
 """

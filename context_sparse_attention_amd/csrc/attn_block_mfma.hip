@@ -655,7 +655,10 @@ hipError_t launch_d(const AttnKernelArgs& a, int n_blocks, void* ws, hipStream_t
                      n_blocks, n_lists, w.list_off, w.hist, w.entries);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int grid = 2 * device_cus();
+  int slot;
+  trace_begin(stream, "k_bm_tiles", &slot);
   hipLaunchKernelGGL((k_bm_tiles<D>), dim3(grid), dim3(kThreads), 0, stream, a, w, n_blocks);
+  trace_end(stream, slot);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.out_dtype == CSA_BF16)
     hipLaunchKernelGGL((k_bm_diag<D, __bf16>), dim3(grid), dim3(kThreads), 0, stream, a, w);

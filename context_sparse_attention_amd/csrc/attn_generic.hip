@@ -126,6 +126,8 @@ hipError_t launch_dv(const AttnKernelArgs& a, hipStream_t stream) {
   const int64_t pairs = (int64_t)a.L.n_q * a.q.h;
   const int grid = (int)((pairs + kWavesPerBlock - 1) / kWavesPerBlock);
   const dim3 block(kWavesPerBlock * kWave);
+  int slot;
+  trace_begin(stream, "k_attn_generic", &slot);
   if (a.v.d <= 64)
     hipLaunchKernelGGL((k_attn_generic<T, TO, 1>), dim3(grid), block, 0, stream, a);
   else if (a.v.d <= 128)
@@ -134,6 +136,7 @@ hipError_t launch_dv(const AttnKernelArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((k_attn_generic<T, TO, 4>), dim3(grid), block, 0, stream, a);
   else
     hipLaunchKernelGGL((k_attn_generic<T, TO, 8>), dim3(grid), block, 0, stream, a);
+  trace_end(stream, slot);
   return hipGetLastError();
 }
 

@@ -247,12 +247,15 @@ template <int DQK, int DV, bool ALIAS, typename TO>
 hipError_t launch_shape(const AttnKernelArgs& a, hipStream_t stream) {
   const int G = a.q.h / a.k.h;
   const dim3 grid((unsigned)a.L.n_q * a.k.h);
+  int slot;
+  trace_begin(stream, "k_tok_attn", &slot);
   if (G == 32)
     hipLaunchKernelGGL((k_tok_attn<DQK, DV, ALIAS, 1, TO>), grid, dim3(64), 0, stream, a);
   else if (G == 64)
     hipLaunchKernelGGL((k_tok_attn<DQK, DV, ALIAS, 2, TO>), grid, dim3(128), 0, stream, a);
   else
     hipLaunchKernelGGL((k_tok_attn<DQK, DV, ALIAS, 4, TO>), grid, dim3(256), 0, stream, a);
+  trace_end(stream, slot);
   return hipGetLastError();
 }
 

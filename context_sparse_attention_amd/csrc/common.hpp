@@ -127,6 +127,10 @@ struct Carver {
   }
 };
 
+// ---- tracing (trace.hip) ----------------------------------------------------
+void trace_begin(hipStream_t stream, const char* kernel, int* slot);
+void trace_end(hipStream_t stream, int slot);
+
 // ---- block table of a packed stream ----------------------------------------
 struct BlockTable {
   int32_t* blk_off;  // [n_seq + 1] first global block of each sequence

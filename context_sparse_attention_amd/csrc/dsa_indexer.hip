@@ -355,6 +355,8 @@ hipError_t launch_typed(const DsaArgs& a, hipStream_t stream) {
   if (a.L.n_q == 0) return hipSuccess;
   const int hi = a.iq.h, di = a.iq.d;
   const bool mfma = a.dtype == CSA_BF16 && (di == 64 || di == 128) && hi % 32 == 0 && hi <= 128;
+  int slot;
+  trace_begin(stream, mfma ? "k_dsa_logits_mfma" : "k_dsa_logits", &slot);
   if (mfma && a.L.n_kv > 0) {
     const dim3 grid((a.L.n_q + kLgWaves - 1) / kLgWaves, (a.L.n_kv + kLgChunk - 1) / kLgChunk);
     const dim3 block(kLgThreads);
@@ -380,6 +382,7 @@ hipError_t launch_typed(const DsaArgs& a, hipStream_t stream) {
       if (e != hipSuccess) return e;
     }
   }
+  trace_end(stream, slot);
   hipLaunchKernelGGL(k_dsa_select, dim3(a.L.n_q), dim3(kSelThreads), 0, stream, a.L,
                      a.topk, logits, a.idx, a.score);
   return hipGetLastError();

@@ -426,15 +426,23 @@ hipError_t launch_typed(const MobaGateArgs& a, hipStream_t stream) {
                        use_mfma ? w.mu_lo : nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  int slot;
+  trace_begin(stream, use_mfma ? "k_moba_gate_mfma" : "k_moba_gate", &slot);
   if (use_mfma) {
-    if (a.q.d == 64) return launch_gate_mfma_k<64>(a, w, stream);
-    if (a.q.d == 128) return launch_gate_mfma_k<128>(a, w, stream);
-    return launch_gate_mfma_k<256>(a, w, stream);
+    if (a.q.d == 64) e = launch_gate_mfma_k<64>(a, w, stream);
+    else if (a.q.d == 128) e = launch_gate_mfma_k<128>(a, w, stream);
+    else e = launch_gate_mfma_k<256>(a, w, stream);
+  } else if (a.topk <= 4) {
+    e = launch_gate_k<T, 4>(a, w, stream);
+  } else if (a.topk <= 8) {
+    e = launch_gate_k<T, 8>(a, w, stream);
+  } else if (a.topk <= 16) {
+    e = launch_gate_k<T, 16>(a, w, stream);
+  } else {
+    e = launch_gate_k<T, 32>(a, w, stream);
   }
-  if (a.topk <= 4) return launch_gate_k<T, 4>(a, w, stream);
-  if (a.topk <= 8) return launch_gate_k<T, 8>(a, w, stream);
-  if (a.topk <= 16) return launch_gate_k<T, 16>(a, w, stream);
-  return launch_gate_k<T, 32>(a, w, stream);
+  trace_end(stream, slot);
+  return e;
 }
 
 }  // namespace

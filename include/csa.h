@@ -206,6 +206,20 @@ csa_status summary_merge(int32_t n_parts, int64_t n_rows, int32_t dv, const floa
                          float* z_out, void* o_out, int32_t o_dtype, float* lse_out,
                          void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * Tracing (host-side, for profiling; not needed for computing).
+ *
+ * csa_trace_begin(n) allocates n HIP event pairs and turns tracing on
+ * (n <= 0 turns it off and frees them).  While on, each call records one pair
+ * on its stream around its dominant kernel until the n pairs are used.
+ * csa_trace_collect waits for the recorded pairs, writes up to `max` elapsed
+ * times (ms) and kernel names (static strings; either array nullable), returns
+ * how many it wrote and rewinds the ring.  Returns CSA_ERR_HIP if event
+ * creation fails.
+ * ------------------------------------------------------------------------------- */
+int csa_trace_begin(int max_records);
+int csa_trace_collect(float* ms, const char** kernels, int max);
+
 /* Text of the last non-OK status on the calling thread ("" if none). */
 const char* csa_last_error(void);
 
