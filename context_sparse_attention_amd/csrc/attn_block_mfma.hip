@@ -239,27 +239,32 @@ __global__ __launch_bounds__(kScanThreads) void k_bm_scan(int n_lists,
 // MFMA tile machinery
 // ---------------------------------------------------------------------------
 
-// K tile [kTN][D] bf16 in 16-byte units, unit u of row r stored at u ^ (r & 7):
-// eight consecutive rows read at one column hit eight distinct bank groups.
-template <int D>
-__device__ inline int k_off(int r, int u) {
-  return r * D + ((u ^ (r & 7)) << 3);
-}
-// V^T tile [D][kTN] bf16 in 4-key groups, group q of row r stored at
-// q ^ ((r + (r >> 4)) & 15): conflict-free both for the transposing writes
-// (rows 8 apart) and for the operand reads (16 consecutive rows).
-__device__ inline int vt_off(int r, int q) {
-  return r * kTN + ((q ^ ((r + (r >> 4)) & 15)) << 2);
-}
-
+// LDS tiles use padded row pitches rather than swizzles, so that every
+// fragment read is one per-lane base address plus a compile-time offset.  Both
+// pitches are 4 mod 32 banks: eight consecutive rows read at one column cover
+// all 32 banks once.
+//   K   [kTN][D + 8]: row-major key tile.
+//   V^T [D][kTN + 8]: value column x key.  The 4-key groups of a row sit at
+//       permuted positions (vt_pos) so that the two groups one MFMA operand
+//       needs (keys 16s + 4h + 0..3 and 16s + 8 + 4h + 0..3) are adjacent.
 template <int D>
 struct Lds {
-  __bf16 k[2][kTN * D];
-  __bf16 vt[2][D * kTN];
+  static constexpr int kKP = D + 8;
+  static constexpr int kVP = kTN + 8;
+  __bf16 k[2][kTN * kKP];
+  __bf16 vt[2][D * kVP];
 };
 
+// position of 4-key group q in a V^T row: groups 4s, 4s + 2, 4s + 1, 4s + 3
+__device__ inline int vt_pos(int q) { return (q & ~3) | ((q & 1) << 1) | ((q >> 1) & 1); }
+
 // Global -> register staging of one key/value tile (all threads).  The staging
-// registers are ext-vector values so that they stay in VGPRs.
+// registers are ext-vector values so that they stay in VGPRs.  Addresses are a
+// uniform tile base plus per-thread byte offsets that do not change from tile
+// to tile, so a load costs no address arithmetic.
+//   K: thread t loads 16-byte unit t % kUnits of rows t / kUnits + kRowsPerPass * p.
+//   V: thread t < kVThreads loads 4-key group t % 16, value columns 8 (t / 16) .. +7,
+//      so that the 16 threads of a store phase write one V^T row.
 template <int D>
 struct Stage {
   static constexpr int kUnits = D / 8;                  // 16-byte units per row
@@ -271,27 +276,44 @@ struct Stage {
   KVec kr;
   VVec vr;  // 4 keys x 8 bf16: key kk in words 4kk .. 4kk+3
 
-  // keys key0 + [0, kTN); rows at or beyond `last` repeat row `last` (masked later)
-  __device__ __forceinline__ void load(const View& K, const View& V, int g, int key0, int last) {
+  struct Offs {
+    uint32_t k[kPasses];
+    uint32_t v[4];
+  };
+
+  // Byte offsets of this thread's rows from the tile base; rows at or beyond
+  // `rows` repeat row `rows - 1` (their scores are masked later).
+  static __device__ __forceinline__ void offsets(const View& K, const View& V, int rows,
+                                                 Offs& o) {
+    const int t = threadIdx.x;
+    const int ku8 = (t % kUnits) * 8;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int row = min(p * kRowsPerPass + t / kUnits, rows - 1);
+      o.k[p] = (uint32_t)((row * K.stride_n + ku8) * (int64_t)sizeof(__bf16));
+    }
+    const int vu8 = (t / 16) * 8;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int key = min((t % 16) * 4 + kk, rows - 1);
+      o.v[kk] = (uint32_t)((key * V.stride_n + vu8) * (int64_t)sizeof(__bf16));
+    }
+  }
+
+  __device__ __forceinline__ void load(const char* kb, const char* vb, const Offs& o) {
     const int t = threadIdx.x;
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
-      const int row = p * kRowsPerPass + t / kUnits;
-      const int key = min(key0 + row, last);
-      const uint4 x =
-          *reinterpret_cast<const uint4*>(elem_ptr<__bf16>(K, key, g) + (t % kUnits) * 8);
+      const uint4 x = *reinterpret_cast<const uint4*>(kb + o.k[p]);
       kr[4 * p] = x.x;
       kr[4 * p + 1] = x.y;
       kr[4 * p + 2] = x.z;
       kr[4 * p + 3] = x.w;
     }
     if (t < kVThreads) {
-      const int dv8 = (t % kUnits) * 8;
-      const int k0 = (t / kUnits) * 4;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const int key = min(key0 + k0 + kk, last);
-        const uint4 x = *reinterpret_cast<const uint4*>(elem_ptr<__bf16>(V, key, g) + dv8);
+        const uint4 x = *reinterpret_cast<const uint4*>(vb + o.v[kk]);
         vr[4 * kk] = x.x;
         vr[4 * kk + 1] = x.y;
         vr[4 * kk + 2] = x.z;
@@ -302,54 +324,89 @@ struct Stage {
 
   __device__ __forceinline__ void store(Lds<D>& s, int buf) const {
     const int t = threadIdx.x;
+    __bf16* kd = &s.k[buf][(t / kUnits) * Lds<D>::kKP + (t % kUnits) * 8];
 #pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      const int row = p * kRowsPerPass + t / kUnits;
-      *reinterpret_cast<uint4*>(&s.k[buf][k_off<D>(row, t % kUnits)]) =
+    for (int p = 0; p < kPasses; ++p)
+      *reinterpret_cast<uint4*>(kd + p * kRowsPerPass * Lds<D>::kKP) =
           make_uint4(kr[4 * p], kr[4 * p + 1], kr[4 * p + 2], kr[4 * p + 3]);
-    }
     if (t < kVThreads) {
-      const int dv8 = (t % kUnits) * 8;
-      const int q = t / kUnits;  // 4-key group
+      __bf16* vd = &s.vt[buf][(t / 16) * 8 * Lds<D>::kVP + vt_pos(t % 16) * 4];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        // value columns dv8 + 2w (low halves) and dv8 + 2w + 1 (high halves)
+        // value columns 2w (low halves) and 2w + 1 (high halves) of this thread's eight
         const uint32_t a0 = vr[w], a1 = vr[4 + w], a2 = vr[8 + w], a3 = vr[12 + w];
         const uint2 even = make_uint2((a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16));
         const uint2 odd = make_uint2((a0 >> 16) | (a1 & 0xffff0000u),
                                      (a2 >> 16) | (a3 & 0xffff0000u));
-        *reinterpret_cast<uint2*>(&s.vt[buf][vt_off(dv8 + 2 * w, q)]) = even;
-        *reinterpret_cast<uint2*>(&s.vt[buf][vt_off(dv8 + 2 * w + 1, q)]) = odd;
+        *reinterpret_cast<uint2*>(vd + (2 * w) * Lds<D>::kVP) = even;
+        *reinterpret_cast<uint2*>(vd + (2 * w + 1) * Lds<D>::kVP) = odd;
       }
     }
   }
 };
 
-// Per-wave online-softmax state for 32 queries (one per lane pair).
+// Per-wave online-softmax state for 32 queries (one per lane pair).  m is the
+// reference maximum the exponentials are taken against (log2 units); it is
+// raised only when a tile's maximum exceeds it by more than kLazy, so the
+// probabilities stay below 2^kLazy and the accumulators are rescaled rarely.
 template <int D>
 struct WaveState {
   f32x16 o[D / 32];  // O^T: rows = value columns, columns = queries
-  float m, l;        // running max (log2 units) and denominator of this lane's query
+  float m, l;        // reference max (log2 units) and denominator of this lane's query
 };
+
+constexpr float kLazy = 8.f;
+
+// lane l and lane l ^ 32 hold the two key halves of one query
+__device__ inline float halves_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float halves_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // One key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
 // kvalid: number of valid keys in the tile; qpos: mask keys > qpos (MASK only).
+// Fragment reads run three MFMAs ahead of their use, and the probabilities of
+// key step ks + 1 are computed while the MFMAs of key step ks run.
 template <int D, bool MASK>
 __device__ __forceinline__ void wave_tile(const Lds<D>& s, int buf, const bf16x8* qf, float c,
-                                 WaveState<D>& st, int tile_key0, int kvalid, int qpos) {
+                                          WaveState<D>& st, int tile_key0, int kvalid,
+                                          int qpos) {
+  constexpr int KP = Lds<D>::kKP, VP = Lds<D>::kVP;
+  constexpr int NS = 2 * (D / 16);  // S^T MFMAs: MFMA i takes key block i & 1, step i >> 1
+  constexpr int NDT = D / 32;       // value blocks
+  constexpr int NO = 4 * NDT;       // O^T MFMAs: MFMA i takes value block i % NDT, step i / NDT
   const int lane = threadIdx.x & (kWave - 1);
   const int half = lane >> 5;
-  f32x16 sc[2];
+  const __bf16* kp = &s.k[buf][(lane & 31) * KP + 8 * half];
+  const __bf16* vp = &s.vt[buf][(lane & 31) * VP + 8 * half];
+  auto kfrag = [&](int i) {
+    return *reinterpret_cast<const bf16x8*>(kp + (i & 1) * 32 * KP + (i >> 1) * 16);
+  };
+  auto vfrag = [&](int i) {
+    return *reinterpret_cast<const bf16x8*>(vp + (i % NDT) * 32 * VP + (i / NDT) * 16);
+  };
+
+  f32x16 sc[2] = {f32x16{}, f32x16{}};
+  bf16x8 ka[4];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    sc[m] = f32x16{};
-    const int row = m * 32 + (lane & 31);
+  for (int i = 0; i < 3; ++i) ka[i] = kfrag(i);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.k[buf][k_off<D>(row, 2 * ks + half)]);
-      sc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sc[m], 0, 0, 0);
-    }
+  for (int i = 0; i < NS; ++i) {
+    if (i + 3 < NS) ka[(i + 3) & 3] = kfrag(i + 3);
+    sc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i & 3], qf[i >> 1], sc[i & 1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  // the first value fragments load while the softmax runs
+  bf16x8 va[4];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) va[i] = vfrag(i);
+
   // lane holds keys m*32 + 8*(j/4) + 4*half + (j%4) of its query (column lane&31)
   float mx = -INFINITY;
 #pragma unroll
@@ -362,63 +419,88 @@ __device__ __forceinline__ void wave_tile(const Lds<D>& s, int buf, const bf16x8
       }
       mx = fmaxf(mx, sc[m][j]);
     }
-  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-  const float m_new = fmaxf(st.m, mx * c);
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = (st.m == -INFINITY) ? 0.f : exp2f(st.m - m_use);
-  float rs = 0.f;
-  bf16x8 pb[4];
+  mx = halves_max(mx) * c;
+  // wave-uniform branch: some query's maximum moved past the reference
+  if (__builtin_amdgcn_ballot_w64(mx > st.m + kLazy)) {
+    const float m_new = fmaxf(st.m, mx);
+    // equal references (both -inf included) need no rescale
+    const float alpha = (m_new == st.m) ? 1.f : __builtin_amdgcn_exp2f(st.m - m_new);
+    st.l *= alpha;
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float p = exp2f(fmaf(sc[m][j], c, -m_use));
-      rs += p;
-      pb[2 * m + (j >> 3)][j & 7] = (__bf16)p;
-    }
-  rs += __shfl_xor(rs, 32, kWave);
-  st.l = st.l * alpha + rs;
-  st.m = m_new;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) st.o[dt][j] *= alpha;
-  // P^T for key step s: keys 16s + 4*half + (0..3) and 16s + 8 + 4*half + (0..3)
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    const int r = dt * 32 + (lane & 31);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x4 lo = *reinterpret_cast<const bf16x4*>(&s.vt[buf][vt_off(r, 4 * ks + half)]);
-      const bf16x4 hi = *reinterpret_cast<const bf16x4*>(&s.vt[buf][vt_off(r, 4 * ks + 2 + half)]);
-      const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], st.o[dt], 0, 0, 0);
-    }
+      for (int j = 0; j < 16; ++j) st.o[dt][j] *= alpha;
+    st.m = m_new;
   }
+  const float m_use = (st.m == -INFINITY) ? 0.f : st.m;
+
+  // P^T for key step ks: pb[ks] holds keys 16ks + 4*half + (0..3) and
+  // 16ks + 8 + 4*half + (0..3), i.e. elements (ks & 1) * 8 .. + 7 of sc[ks >> 1]
+  bf16x8 pb[4];
+  float rs = 0.f;
+  auto probs = [&](int ks, int e0, int e1) {
+#pragma unroll
+    for (int e = e0; e < e1; ++e) {
+      const float p =
+          __builtin_amdgcn_exp2f(fmaf(sc[ks >> 1][(ks & 1) * 8 + e], c, -m_use));
+      rs += p;
+      pb[ks][e] = (__bf16)p;
+    }
+  };
+  probs(0, 0, 8);
+  constexpr int kSlice = 8 / NDT;
+#pragma unroll
+  for (int i = 0; i < NO; ++i) {
+    if (i + 3 < NO) va[(i + 3) & 3] = vfrag(i + 3);
+    const int dt = i % NDT, ks = i / NDT;
+    st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 3], pb[ks], st.o[dt], 0, 0, 0);
+    if (ks + 1 < 4) probs(ks + 1, dt * kSlice, (dt + 1) * kSlice);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  st.l += halves_sum(rs);
 }
 
 // Runs every key tile of [key0, key0 + nkeys) through the workgroup.  Tile kt
-// is staged into LDS buffer kt & 1 and consumed after one barrier; the barrier
+// is stored into LDS buffer kt & 1 and consumed after one barrier; the barrier
 // of tile kt + 1 also orders every read of buffer kt & 1 before its reuse by
-// tile kt + 2.  The staging registers are dead during the MFMA work, and the
-// second workgroup on the CU hides the load latency.
+// tile kt + 2.  The global loads of tile kt + 1 are issued before the math of
+// tile kt, so their latency hides behind it.  Without MASK every tile is full
+// (nkeys is a multiple of kTN).
 // active: this wave has work; wave_max_pos: skip tiles entirely past it (MASK).
 template <int D, bool MASK>
 __device__ __forceinline__ void run_keys(Lds<D>& s, const View& K, const View& V, int g,
                                          int key0, int nkeys, bool active, const bf16x8* qf,
                                          float c, WaveState<D>& st, int qpos,
                                          int wave_max_pos) {
+  key0 = __builtin_amdgcn_readfirstlane(key0);
+  nkeys = __builtin_amdgcn_readfirstlane(nkeys);
   const int n_kt = (nkeys + kTN - 1) / kTN;
-  const int last = key0 + nkeys - 1;
+  typename Stage<D>::Offs full;
+  Stage<D>::offsets(K, V, kTN, full);
+  const char* kb = reinterpret_cast<const char*>(elem_ptr<__bf16>(K, key0, g));
+  const char* vb = reinterpret_cast<const char*>(elem_ptr<__bf16>(V, key0, g));
+  const int64_t kstep = kTN * K.stride_n * (int64_t)sizeof(__bf16);
+  const int64_t vstep = kTN * V.stride_n * (int64_t)sizeof(__bf16);
+  Stage<D> stage;
+  auto load_tile = [&](int kt) {
+    const int rows = nkeys - kt * kTN;
+    if (MASK && rows < kTN) {
+      typename Stage<D>::Offs part;
+      Stage<D>::offsets(K, V, rows, part);
+      stage.load(kb, vb, part);
+    } else {
+      stage.load(kb, vb, full);
+    }
+    kb += kstep;
+    vb += vstep;
+  };
+  if (n_kt > 0) load_tile(0);
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
     const int tk0 = key0 + kt * kTN;
-    {
-      Stage<D> stage;
-      stage.load(K, V, g, tk0, last);
-      stage.store(s, buf);
-    }
+    stage.store(s, buf);
     __syncthreads();
+    if (kt + 1 < n_kt) load_tile(kt + 1);
     if (active && (!MASK || tk0 <= wave_max_pos))
       wave_tile<D, MASK>(s, buf, qf, c, st, tk0, min(kTN, nkeys - kt * kTN), qpos);
   }
