@@ -195,7 +195,7 @@ def main():
         attend(select())
     torch.cuda.synchronize()
     idx_np = select().cpu().numpy()
-    pairs, full_pairs = effective_pairs(w, idx_np, split=True)
+    pairs = effective_pairs(w, idx_np)
     flops = pairs * 2.0 * (w.dqk + w.dv)
     sel_bytes = selection_bytes(w)
 
@@ -246,8 +246,9 @@ def main():
     sel_med = float(np.median(sel_ms))
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     # dominant attention kernel and the algorithmic flops of one launch
-    if "k_bm_tiles" in kern:
-        dom, dom_flops = "k_bm_tiles", full_pairs * 2.0 * (w.dqk + w.dv)
+    if "k_bm_attn" in kern:
+        # full-block and own-block (causal) chunks are both computed there
+        dom, dom_flops = "k_bm_attn", flops
     elif "k_tok_attn" in kern:
         dom, dom_flops = "k_tok_attn", flops
     else:

@@ -5,27 +5,28 @@
 // query-tile-centric kernel would visit the union of its rows' blocks, so the
 // selection is inverted instead: every fully permitted block slot of every
 // (row, head) is appended to the list of its (key head, block); each list is
-// cut into tiles of 128 gathered queries that share the block's keys, and the
-// tile kernel computes one (m, l, z) chunk summary per slot ("Context parallel
+// cut into tiles of 128 gathered queries that share the block's keys, and each
+// tile yields one (m, l, z) chunk summary per slot ("Context parallel
 // attention: exchange keys and merge softmax globally", chunk summary).  The
 // own block, partially masked by the causal diagonal at the row's global
-// position (Megatron-LM issue #4878, shifted causal diagonal), is computed by a
-// diagonal kernel over tiles of consecutive rows, which then merges the slot
-// summaries of each (row, head) by rescaling to the larger maximum and
-// finalizes the output (neutral summary and zero-output convention for rows
-// with no permitted key: same article, masking paragraph).
+// position (Megatron-LM issue #4878, shifted causal diagonal), is computed in
+// the same persistent kernel over diagonal tiles of consecutive rows.  A merge
+// kernel then combines the summaries of each (row, head) by rescaling to the
+// larger maximum and finalizes the output (neutral summary and zero-output
+// convention for rows with no permitted key: same article, masking paragraph).
 //
 // Kernels (in stream order):
 //   k_block_table  (layout.hip) block table + zeroed list counters
-//   k_bm_hist      64 workgroups: LDS histogram of full block slots per list,
-//                  own-block multiplicity per (row, head)
+//   k_bm_hist      LDS histogram of full block slots per list for each range of
+//                  (row, head) pairs, own-block multiplicity per (row, head)
+//   k_bm_colscan   one wave per list: prefix of the histogram over the ranges
 //   k_bm_scan      one workgroup: list offsets and the query-tile table
-//   k_bm_fill      64 workgroups: place slot ids into the lists (counting sort)
-//   k_bm_tiles     persistent: per query tile, S^T = K Q^T and O^T = V^T P^T on
-//                  LDS-staged key/value tiles (32x32x16 bf16 MFMA), fp32 online
-//                  softmax in registers, one fp32 summary per slot
-//   k_bm_diag      persistent over fixed row tiles: own-block attention with the
-//                  causal mask, merge with the slot summaries in slot order, finalize
+//   k_bm_fill      place slot ids into the lists (counting sort)
+//   k_bm_attn      persistent, per-XCD work queues: list tiles, then diagonal
+//                  tiles; S^T = K Q^T and O^T = V^T P^T on LDS-staged key/value
+//                  tiles (32x32x16 bf16 MFMA), fp32 online softmax in registers,
+//                  one summary per chunk (fp32 m, l; bf16 z / l)
+//   k_bm_merge     per (row, head): merge the summaries in slot order, finalize
 //
 // Layout of the math: the MFMA computes S^T (keys x queries) so that a lane
 // owns one query and its scores sit in that lane's registers; the softmax row
@@ -48,25 +49,38 @@ constexpr int kWaves = 4;
 constexpr int kTM = kQW * kWaves;        // queries per workgroup tile
 constexpr int kThreads = kWaves * kWave;
 constexpr int kScanThreads = 1024;
-constexpr int kHistWgs = 64;          // workgroups that bucket the slots into lists
 constexpr int kHistThreads = 256;
+constexpr int kHistPairs = 512;        // (row, head) pairs per bucketing workgroup
+constexpr int kMaxHistWgs = 512;
+constexpr int64_t kHistCells = 1 << 21;  // bound on workgroups x lists
 constexpr int kMaxLists = 16384;      // LDS histogram bins (64 KiB)
+constexpr int kXcds = 8;              // accelerator complex dies; workgroup b runs on b % 8
+constexpr int kQueue0 = 8;            // totals[kQueue0 + x]: work-queue counter of XCD x
 constexpr float kLn2 = 0.69314718055994531f;
 
 struct BmWs {
   BlockTable bt;
   int32_t* counts;    // [n_lists]  slots per list
-  int32_t* hist;      // [n_hist_wg, n_lists]  per-workgroup counts, then prefixes
+  int32_t* hist;      // [n_lists, n_hist]  per-range counts, then prefixes
   int32_t* list_off;  // [n_lists + 1]
   int2* tiles;        // [max_tiles]  (list, first entry)
-  int32_t* totals;    // [4]  query tiles
-  int32_t* own_mult;  // [n_q * hq]
+  int32_t* totals;    // [16]  [0] list tiles, [kQueue0 + x] work-queue counter of XCD x
+  int4* pinfo;        // [n_q * hq]  own-block multiplicity, full-block slot mask (lo, hi),
+                      //             first own-block slot (-1 if none)
   int32_t* entries;   // [n_q * hq * W]  flat slot ids
   float2* part_ml;    // [n_q * hq * W]  (m in log2 units, l)
-  float* part_z;      // [n_q * hq * W * D]
+  __bf16* part_o;     // [n_q * hq * W * D]  normalized partial output z / l
 };
 
 int64_t max_query_tiles(int64_t slots, int64_t n_lists) { return slots / kTM + n_lists + 1; }
+
+// Number of bucketing workgroups (ranges of (row, head) pairs).
+int hist_wgs(int64_t pairs, int64_t n_lists) {
+  int64_t w = (pairs + kHistPairs - 1) / kHistPairs;
+  w = std::min<int64_t>(w, kMaxHistWgs);
+  w = std::min<int64_t>(w, std::max<int64_t>(16, kHistCells / std::max<int64_t>(n_lists, 1)));
+  return (int)std::max<int64_t>(w, 1);
+}
 
 template <bool CARVE>
 size_t carve_bm(void* base, int n_q, int n_seq, int n_blocks, int hq, int hkv, int dv, int W,
@@ -79,14 +93,14 @@ size_t carve_bm(void* base, int n_q, int n_seq, int n_blocks, int hq, int hkv, i
   t.bt.blocks = c.take<int2>(n_blocks);
   t.bt.blk_seq = c.take<int32_t>(n_blocks);
   t.counts = c.take<int32_t>(n_lists);
-  t.hist = c.take<int32_t>((size_t)kHistWgs * n_lists);
+  t.hist = c.take<int32_t>((size_t)hist_wgs((int64_t)n_q * hq, n_lists) * n_lists);
   t.list_off = c.take<int32_t>(n_lists + 1);
   t.tiles = c.take<int2>(max_query_tiles(slots, n_lists));
-  t.totals = c.take<int32_t>(4);
-  t.own_mult = c.take<int32_t>((size_t)n_q * hq);
+  t.totals = c.take<int32_t>(16);
+  t.pinfo = c.take<int4>((size_t)n_q * hq);
   t.entries = c.take<int32_t>(slots);
   t.part_ml = c.take<float2>(slots);
-  t.part_z = c.take<float>(slots * dv);
+  t.part_o = c.take<__bf16>(slots * dv);
   if (CARVE) *w = t;
   return align_up(c.used, 256);
 }
@@ -101,13 +115,13 @@ __device__ inline int slot_class(int s, const RowKeys& r, int B) {
   return (s + B - 1 < r.hi) ? 1 : 2;
 }
 
-// The (row, head) pairs are cut into kHistWgs contiguous ranges.  Each range
+// The (row, head) pairs are cut into gridDim.x contiguous ranges.  Each range
 // is bucketed by one workgroup with an LDS histogram (no global atomics), so
-// list building is a counting sort: hist[w][list] counts, a scan turns the
+// list building is a counting sort: hist[list][w] counts, a scan turns the
 // matrix into per-list offsets, and the fill pass places each slot at
-// list_off[list] + prefix[w][list] + its LDS-local rank.
+// list_off[list] + prefix[list][w] + its LDS-local rank.
 __device__ inline void pair_range(int64_t pairs, int64_t* b, int64_t* e) {
-  const int64_t per = (pairs + kHistWgs - 1) / kHistWgs;
+  const int64_t per = (pairs + gridDim.x - 1) / gridDim.x;
   *b = min(pairs, (int64_t)blockIdx.x * per);
   *e = min(pairs, *b + per);
 }
@@ -115,7 +129,7 @@ __device__ inline void pair_range(int64_t pairs, int64_t* b, int64_t* e) {
 __global__ __launch_bounds__(kHistThreads) void k_bm_hist(AttnKernelArgs a, BlockTable bt,
                                                           int n_blocks, int n_lists,
                                                           int32_t* __restrict__ hist,
-                                                          int32_t* __restrict__ own_mult) {
+                                                          int4* __restrict__ pinfo) {
   extern __shared__ int s_bins[];
   for (int l = threadIdx.x; l < n_lists; l += kHistThreads) s_bins[l] = 0;
   __syncthreads();
@@ -126,22 +140,27 @@ __global__ __launch_bounds__(kHistThreads) void k_bm_hist(AttnKernelArgs a, Bloc
     const int i = (int)(pair / hq), h = (int)(pair % hq);
     const int g = h / (hq / a.k.h);
     const RowKeys r = row_keys(a.L, i);
-    int mult = 0;
+    int mult = 0, own_slot = -1;
+    uint64_t full = 0;
     if (r.valid) {
       const int32_t* slots = slot_row(a, i, h);
       const int base = g * n_blocks + bt.blk_off[r.seq];
       for (int s = 0; s < a.idx_width; ++s) {
         const int st = slots[s];
         const int c = slot_class(st, r, a.block_size);
-        if (c == 1) atomicAdd(&s_bins[base + (st - r.lo) / a.block_size], 1);
-        else if (c == 2) ++mult;
+        if (c == 1) {
+          atomicAdd(&s_bins[base + (st - r.lo) / a.block_size], 1);
+          full |= (uint64_t)1 << s;
+        } else if (c == 2) {
+          if (mult++ == 0) own_slot = s;
+        }
       }
     }
-    own_mult[pair] = mult;
+    pinfo[pair] = make_int4(mult, (int)(uint32_t)full, (int)(uint32_t)(full >> 32), own_slot);
   }
   __syncthreads();
   for (int l = threadIdx.x; l < n_lists; l += kHistThreads)
-    hist[(int64_t)blockIdx.x * n_lists + l] = s_bins[l];
+    hist[(int64_t)l * gridDim.x + blockIdx.x] = s_bins[l];
 }
 
 __global__ __launch_bounds__(kHistThreads) void k_bm_fill(AttnKernelArgs a, BlockTable bt,
@@ -151,7 +170,7 @@ __global__ __launch_bounds__(kHistThreads) void k_bm_fill(AttnKernelArgs a, Bloc
                                                           int32_t* __restrict__ entries) {
   extern __shared__ int s_bins[];
   for (int l = threadIdx.x; l < n_lists; l += kHistThreads)
-    s_bins[l] = list_off[l] + hist[(int64_t)blockIdx.x * n_lists + l];
+    s_bins[l] = list_off[l] + hist[(int64_t)l * gridDim.x + blockIdx.x];
   __syncthreads();
   const int hq = a.q.h;
   int64_t b, e;
@@ -192,27 +211,37 @@ __device__ int scan_incl(int x, int* s_wave, int* s_total) {
   return x + before;
 }
 
+// One wave per list: exclusive prefix of the list's per-range counts, and the
+// list total.
+__global__ __launch_bounds__(kHistThreads) void k_bm_colscan(int n_lists, int n_hist,
+                                                             int32_t* __restrict__ hist,
+                                                             int32_t* __restrict__ counts) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int l = blockIdx.x * (kHistThreads / kWave) + threadIdx.x / kWave;
+  if (l >= n_lists) return;
+  int32_t* h = hist + (int64_t)l * n_hist;
+  int carry = 0;
+  for (int w0 = 0; w0 < n_hist; w0 += kWave) {
+    const int w = w0 + lane;
+    const int x = w < n_hist ? h[w] : 0;
+    int incl = x;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += y;
+    }
+    if (w < n_hist) h[w] = carry + incl - x;
+    carry += __shfl(incl, kWave - 1, kWave);
+  }
+  if (lane == 0) counts[l] = carry;
+}
+
 __global__ __launch_bounds__(kScanThreads) void k_bm_scan(int n_lists,
-                                                          int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ hist,
+                                                          const int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ list_off,
                                                           int2* __restrict__ tiles,
                                                           int32_t* __restrict__ totals) {
   __shared__ int s_wave[kScanThreads / kWave];
-  // per list: exclusive prefix over the bucketing workgroups, and the total
-  for (int l = threadIdx.x; l < n_lists; l += kScanThreads) {
-    int c[kHistWgs];
-#pragma unroll
-    for (int w = 0; w < kHistWgs; ++w) c[w] = hist[(int64_t)w * n_lists + l];
-    int run = 0;
-#pragma unroll
-    for (int w = 0; w < kHistWgs; ++w) {
-      hist[(int64_t)w * n_lists + l] = run;
-      run += c[w];
-    }
-    counts[l] = run;
-  }
-  __syncthreads();
   int carry = 0, tcarry = 0, tot = 0;
   for (int base = 0; base < n_lists; base += kScanThreads) {
     const int l = base + threadIdx.x;
@@ -516,68 +545,6 @@ __device__ __forceinline__ void load_q(const View& Q, int row, int head, bf16x8*
     qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * half);
 }
 
-// Persistent walk over `total` work items with an XCD-aware order: workgroup b
-// runs on XCD b % 8 and takes items from that XCD's contiguous eighth, so the
-// tiles of one key block share one L2.
-struct XcdWalk {
-  int begin, end, step;
-  __device__ XcdWalk(int total) {
-    const int nx = 8;
-    const int x = blockIdx.x % nx;
-    const int per = (total + nx - 1) / nx;
-    const int wg_in_x = (gridDim.x + nx - 1 - x) / nx;  // workgroups on this XCD
-    begin = x * per + (int)(blockIdx.x / nx);
-    end = min(total, (x + 1) * per);
-    step = max(wg_in_x, 1);
-  }
-};
-
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void k_bm_tiles(AttnKernelArgs a, BmWs w,
-                                                          int n_blocks) {
-  __shared__ Lds<D> s;
-  const int total = w.totals[0];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int half = lane >> 5;
-  const int hq = a.q.h;
-  const int W = a.idx_width;
-  const XcdWalk walk(total);
-  for (int t = walk.begin; t < walk.end; t += walk.step) {
-    const int2 tl = w.tiles[t];
-    const int list = tl.x;
-    const int g = list / n_blocks;
-    const int blk = list % n_blocks;
-    const int cnt = min(kTM, w.counts[list] - tl.y);
-    const int32_t* ent = w.entries + w.list_off[list] + tl.y;
-    const int n = wave * kQW + (lane & 31);
-    const bool valid = n < cnt;
-    const int p = ent[valid ? n : 0];
-    const int row = p / (hq * W);
-    const int head = (p / W) % hq;
-    bf16x8 qf[D / 16];
-    load_q<D>(a.q, row, head, qf);
-    WaveState<D> st;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) st.o[dt] = f32x16{};
-    st.m = -INFINITY;
-    st.l = 0.f;
-    const int2 b = w.bt.blocks[blk];
-    run_keys<D, false>(s, a.k, a.v, g, b.x, b.y, wave * kQW < cnt, qf, a.scale_log2, st, 0, 0);
-    if (valid) {
-      if (half == 0) w.part_ml[p] = make_float2(st.m, st.l);
-      float* z = w.part_z + (int64_t)p * D;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          *reinterpret_cast<float4*>(z + dt * 32 + 8 * jj + 4 * half) =
-              make_float4(st.o[dt][4 * jj], st.o[dt][4 * jj + 1], st.o[dt][4 * jj + 2],
-                          st.o[dt][4 * jj + 3]);
-    }
-  }
-}
-
 __device__ inline void store4(float* p, float a, float b, float c, float d) {
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
@@ -586,122 +553,205 @@ __device__ inline void store4(__bf16* p, float a, float b, float c, float d) {
   *reinterpret_cast<bf16x4*>(p) = x;
 }
 
-// Diagonal tiles are fixed runs of TR = 128 / G consecutive rows (all G query
-// heads of one key head).  Rows of a tile whose own blocks differ (sequence or
-// zigzag-chunk boundaries) are handled run by run: each lane only takes keys in
-// the pass of its own row's block.
-template <int D, typename TO>
-__global__ __launch_bounds__(kThreads, 2) void k_bm_diag(AttnKernelArgs a, BmWs w) {
-  __shared__ Lds<D> s;
-  __shared__ int s_own[kTM];
-  __shared__ int s_pos[kTM];
-  const int hkv = a.k.h;
-  const int hq = a.q.h;
-  const int G = hq / hkv;
-  const int TR = kTM / G;  // rows per diagonal tile
-  const int n_tiles = (a.L.n_q + TR - 1) / TR;
+// Writes this lane's half of a chunk summary: (m, l) and the normalized output
+// z / l in bf16.  Every summary written has l >= 1: the key that set the
+// reference maximum contributes 2^0.
+template <int D>
+__device__ __forceinline__ void write_summary(const BmWs& w, int64_t p, const WaveState<D>& st,
+                                              int half) {
+  if (half == 0) w.part_ml[p] = make_float2(st.m, st.l);
+  const float inv = 1.f / st.l;
+  __bf16* o = w.part_o + p * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      store4(o + dt * 32 + 8 * jj + 4 * half, st.o[dt][4 * jj] * inv, st.o[dt][4 * jj + 1] * inv,
+             st.o[dt][4 * jj + 2] * inv, st.o[dt][4 * jj + 3] * inv);
+}
+
+template <int D>
+__device__ __forceinline__ void reset(WaveState<D>& st) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) st.o[dt] = f32x16{};
+  st.m = -INFINITY;
+  st.l = 0.f;
+}
+
+// List tile: up to kTM gathered (row, head) slots of one list against the
+// list's full key block; one summary per slot.
+template <int D>
+__device__ __forceinline__ void list_item(Lds<D>& s, const AttnKernelArgs& a, const BmWs& w,
+                                          int n_blocks, int t) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int half = lane >> 5;
+  const int hq = a.q.h;
   const int W = a.idx_width;
-  const int B = a.block_size;
-  const XcdWalk walk(n_tiles * hkv);
-  for (int item = walk.begin; item < walk.end; item += walk.step) {
-    const int tile = item / hkv;
-    const int g = item % hkv;
-    const int r0 = tile * TR;
-    const int nrows = min(TR, a.L.n_q - r0);
-    if (threadIdx.x < nrows) {
-      const RowKeys r = row_keys(a.L, r0 + threadIdx.x);
-      s_own[threadIdx.x] = r.valid ? w.bt.blk_off[r.seq] + (r.hi - r.lo) / B : -1;
-      s_pos[threadIdx.x] = r.hi;
-    }
-    __syncthreads();
-    const int n = wave * kQW + (lane & 31);
-    const int rl = n % TR;
-    const int head = g * G + n / TR;
-    const bool valid = rl < nrows;
-    const int rowc = r0 + (valid ? rl : 0);
-    const int my_pos = valid ? s_pos[rl] : -1;
+  const int2 tl = w.tiles[t];
+  const int list = tl.x;
+  const int g = list / n_blocks;
+  const int blk = list % n_blocks;
+  const int cnt = min(kTM, w.counts[list] - tl.y);
+  const int32_t* ent = w.entries + w.list_off[list] + tl.y;
+  const int n = wave * kQW + (lane & 31);
+  const bool valid = n < cnt;
+  const int p = ent[valid ? n : 0];
+  const int row = p / (hq * W);
+  const int head = (p / W) % hq;
+  bf16x8 qf[D / 16];
+  load_q<D>(a.q, row, head, qf);
+  WaveState<D> st;
+  reset(st);
+  const int2 b = w.bt.blocks[blk];
+  run_keys<D, false>(s, a.k, a.v, g, b.x, b.y, wave * kQW < cnt, qf, a.scale_log2, st, 0, 0);
+  if (valid) write_summary<D>(w, p, st, half);
+}
 
-    WaveState<D> st;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) st.o[dt] = f32x16{};
-    st.m = -INFINITY;
-    st.l = 0.f;
-    bf16x8 qf[D / 16];
-    load_q<D>(a.q, rowc, head, qf);
-    for (int start = 0; start < nrows;) {
-      const int ob = s_own[start];
-      int end = start + 1, maxpos = s_pos[start];
-      while (end < nrows && s_own[end] == ob) maxpos = max(maxpos, s_pos[end++]);
-      if (ob >= 0) {
-        // a lane joins only the run that holds its row: two runs may share a
-        // block when rows without keys sit between them
-        const int qpos = (valid && rl >= start && rl < end) ? my_pos : -1;
-        int wmax = qpos;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) wmax = max(wmax, __shfl_xor(wmax, off, kWave));
-        const int own_start = w.bt.blocks[ob].x;
-        run_keys<D, true>(s, a.k, a.v, g, own_start, maxpos - own_start + 1,
-                          wmax >= own_start, qf, a.scale_log2, st, qpos, wmax);
-      }
-      start = end;
-    }
-    __syncthreads();  // s_own / s_pos are rewritten by the next item
-    if (!valid) continue;
-    // own-block multiplicity, then the full-block summaries in slot order
-    const int pair = rowc * hq + head;
-    const int mult = w.own_mult[pair];
-    if (mult == 0) {
-      st.m = -INFINITY;
-      st.l = 0.f;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) st.o[dt] = f32x16{};
-    } else if (mult > 1) {
-      st.l *= (float)mult;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) st.o[dt][j] *= (float)mult;
-    }
-    const RowKeys r = row_keys(a.L, rowc);
-    if (r.valid) {
-      const int32_t* slots = slot_row(a, rowc, head);
-      for (int sl = 0; sl < W; ++sl) {
-        if (slot_class(slots[sl], r, B) != 1) continue;
-        const int64_t p = (int64_t)pair * W + sl;
-        const float2 ml = w.part_ml[p];
-        const float mn = fmaxf(st.m, ml.x);
-        const float al = (st.m == -INFINITY) ? 0.f : exp2f(st.m - mn);
-        const float be = exp2f(ml.x - mn);
-        st.l = st.l * al + ml.y * be;
-        st.m = mn;
-        const float* z = w.part_z + p * D;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float4 zz = *reinterpret_cast<const float4*>(z + dt * 32 + 8 * jj + 4 * half);
-            st.o[dt][4 * jj] = st.o[dt][4 * jj] * al + zz.x * be;
-            st.o[dt][4 * jj + 1] = st.o[dt][4 * jj + 1] * al + zz.y * be;
-            st.o[dt][4 * jj + 2] = st.o[dt][4 * jj + 2] * al + zz.z * be;
-            st.o[dt][4 * jj + 3] = st.o[dt][4 * jj + 3] * al + zz.w * be;
-          }
-      }
-    }
-    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
-    TO* out = reinterpret_cast<TO*>(a.out) + (int64_t)pair * D;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        store4(out + dt * 32 + 8 * jj + 4 * half, st.o[dt][4 * jj] * inv,
-               st.o[dt][4 * jj + 1] * inv, st.o[dt][4 * jj + 2] * inv,
-               st.o[dt][4 * jj + 3] * inv);
-    if (a.lse && half == 0)
-      a.lse[pair] = st.l > 0.f ? (st.m + log2f(st.l)) * kLn2 : -INFINITY;
+// Diagonal tile: TR = kTM / G consecutive rows x the G query heads of one key
+// head against their own blocks, with the causal mask at each row's global
+// position.  Rows of a tile whose own blocks differ (sequence or zigzag-chunk
+// boundaries) are handled run by run: each lane only takes keys in the pass of
+// its own row's block.  The summary goes to the (row, head)'s first own-block
+// slot; rows that did not select their own block write nothing.
+template <int D>
+__device__ __forceinline__ void diag_item(Lds<D>& s, int* s_own, int* s_pos,
+                                          const AttnKernelArgs& a, const BmWs& w, int item) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int half = lane >> 5;
+  const int hkv = a.k.h;
+  const int hq = a.q.h;
+  const int G = hq / hkv;
+  const int TR = kTM / G;
+  const int B = a.block_size;
+  const int tile = item / hkv;
+  const int g = item % hkv;
+  const int r0 = tile * TR;
+  const int nrows = min(TR, a.L.n_q - r0);
+  if (threadIdx.x < nrows) {
+    const RowKeys r = row_keys(a.L, r0 + threadIdx.x);
+    s_own[threadIdx.x] = r.valid ? w.bt.blk_off[r.seq] + (r.hi - r.lo) / B : -1;
+    s_pos[threadIdx.x] = r.hi;
   }
+  __syncthreads();
+  const int n = wave * kQW + (lane & 31);
+  const int rl = n % TR;
+  const int head = g * G + n / TR;
+  const bool valid = rl < nrows;
+  const int rowc = r0 + (valid ? rl : 0);
+  const int my_pos = valid ? s_pos[rl] : -1;
+  const int pair = rowc * hq + head;
+  const int own_slot = w.pinfo[pair].w;  // the load overlaps the key loop
+
+  WaveState<D> st;
+  reset(st);
+  bf16x8 qf[D / 16];
+  load_q<D>(a.q, rowc, head, qf);
+  bool has_keys = false;
+  for (int start = 0; start < nrows;) {
+    const int ob = s_own[start];
+    int end = start + 1, maxpos = s_pos[start];
+    while (end < nrows && s_own[end] == ob) maxpos = max(maxpos, s_pos[end++]);
+    if (ob >= 0) {
+      // a lane joins only the run that holds its row: two runs may share a
+      // block when rows without keys sit between them
+      const bool mine = valid && rl >= start && rl < end;
+      has_keys |= mine;
+      const int qpos = mine ? my_pos : -1;
+      int wmax = qpos;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) wmax = max(wmax, __shfl_xor(wmax, off, kWave));
+      const int own_start = w.bt.blocks[ob].x;
+      run_keys<D, true>(s, a.k, a.v, g, own_start, maxpos - own_start + 1, wmax >= own_start,
+                        qf, a.scale_log2, st, qpos, wmax);
+    }
+    start = end;
+  }
+  if (has_keys && own_slot >= 0)
+    write_summary<D>(w, (int64_t)pair * a.idx_width + own_slot, st, half);
+}
+
+// One persistent kernel for both kinds of chunk: workgroup b runs on XCD
+// b % 8 and takes items from that XCD's queue, which holds a contiguous eighth
+// of the list tiles (so the tiles of one key block share one L2) followed by
+// an eighth of the diagonal tiles (smaller, uneven items that fill the tail).
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void k_bm_attn(AttnKernelArgs a, BmWs w,
+                                                         int n_blocks) {
+  __shared__ Lds<D> s;
+  __shared__ int s_own[kTM];
+  __shared__ int s_pos[kTM];
+  __shared__ int s_item;
+  const int n_lt = w.totals[0];
+  const int G = a.q.h / a.k.h;
+  const int n_dt = (a.L.n_q + kTM / G - 1) / (kTM / G) * a.k.h;
+  const int x = blockIdx.x % kXcds;
+  const int lper = (n_lt + kXcds - 1) / kXcds, dper = (n_dt + kXcds - 1) / kXcds;
+  const int lb = min(n_lt, x * lper), ln = min(n_lt, lb + lper) - lb;
+  const int db = min(n_dt, x * dper), dn = min(n_dt, db + dper) - db;
+  for (;;) {
+    if (threadIdx.x == 0) s_item = atomicAdd(&w.totals[kQueue0 + x], 1);
+    __syncthreads();
+    const int q = s_item;
+    if (q >= ln + dn) break;
+    if (q < ln)
+      list_item<D>(s, a, w, n_blocks, lb + q);
+    else
+      diag_item<D>(s, s_own, s_pos, a, w, db + q - ln);
+    __syncthreads();  // s_item, s_own and s_pos are rewritten by the next item
+  }
+}
+
+__device__ inline float4 load4(const __bf16* p) {
+  const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+  return make_float4((float)x[0], (float)x[1], (float)x[2], (float)x[3]);
+}
+
+// Merge of each (row, head)'s chunk summaries ("Context parallel attention:
+// exchange keys and merge softmax globally", merge step): the own block
+// counted with its multiplicity first, then the full-block slots in slot
+// order, each by rescaling to the larger maximum; then the output z / l and
+// the log-sum-exp.  A (row, head) with no summary gets the neutral summary:
+// zero output, lse = -inf.  kLanes lanes per (row, head), 8 values each.
+template <int D, typename TO>
+__global__ __launch_bounds__(kHistThreads) void k_bm_merge(AttnKernelArgs a, BmWs w) {
+  constexpr int kLanes = D / 8;
+  const int64_t pair = (int64_t)blockIdx.x * (kHistThreads / kLanes) + threadIdx.x / kLanes;
+  if (pair >= (int64_t)a.L.n_q * a.q.h) return;
+  const int c8 = (threadIdx.x % kLanes) * 8;
+  const int W = a.idx_width;
+  const int4 info = w.pinfo[pair];
+  float m = -INFINITY, l = 0.f, z[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = 0.f;
+  auto take = [&](int64_t p, float mult) {
+    const float2 ml = w.part_ml[p];
+    const uint4 raw = *reinterpret_cast<const uint4*>(w.part_o + p * D + c8);
+    const float mn = fmaxf(m, ml.x);
+    const float al = (m == -INFINITY) ? 0.f : exp2f(m - mn);
+    const float be = exp2f(ml.x - mn) * ml.y * mult;
+    l = l * al + be;
+    m = mn;
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float o = __uint_as_float(e & 1 ? wd[e / 2] & 0xffff0000u : wd[e / 2] << 16);
+      z[e] = z[e] * al + o * be;
+    }
+  };
+  const int64_t pb = pair * W;
+  if (info.x > 0 && info.w >= 0) take(pb + info.w, (float)info.x);
+  uint64_t full = (uint64_t)(uint32_t)info.y | ((uint64_t)(uint32_t)info.z << 32);
+  while (full) {
+    take(pb + __builtin_ctzll(full), 1.f);
+    full &= full - 1;
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  TO* out = reinterpret_cast<TO*>(a.out) + pair * D + c8;
+  store4(out, z[0] * inv, z[1] * inv, z[2] * inv, z[3] * inv);
+  store4(out + 4, z[4] * inv, z[5] * inv, z[6] * inv, z[7] * inv);
+  if (a.lse && c8 == 0) a.lse[pair] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
 }
 
 int device_cus() {
@@ -723,29 +773,38 @@ hipError_t launch_d(const AttnKernelArgs& a, int n_blocks, void* ws, hipStream_t
   const int hq = a.q.h, hkv = a.k.h;
   carve_bm<true>(ws, a.L.n_q, n_seq, n_blocks, hq, hkv, D, a.idx_width, &w);
   const int n_lists = hkv * n_blocks;
-  hipError_t e = launch_block_table(a.L.cu, n_seq, a.block_size, n_blocks, w.bt, nullptr, 0,
+  // also zeroes the list-tile total and the work-queue counters
+  hipError_t e = launch_block_table(a.L.cu, n_seq, a.block_size, n_blocks, w.bt, w.totals, 16,
                                     stream);
   if (e != hipSuccess) return e;
   const size_t bins = (size_t)n_lists * sizeof(int);
-  hipLaunchKernelGGL(k_bm_hist, dim3(kHistWgs), dim3(kHistThreads), bins, stream, a, w.bt,
-                     n_blocks, n_lists, w.hist, w.own_mult);
+  const int n_hist = hist_wgs((int64_t)a.L.n_q * hq, n_lists);
+  hipLaunchKernelGGL(k_bm_hist, dim3(n_hist), dim3(kHistThreads), bins, stream, a, w.bt,
+                     n_blocks, n_lists, w.hist, w.pinfo);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int lists_per_wg = kHistThreads / kWave;
+  hipLaunchKernelGGL(k_bm_colscan, dim3((n_lists + lists_per_wg - 1) / lists_per_wg),
+                     dim3(kHistThreads), 0, stream, n_lists, n_hist, w.hist, w.counts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_bm_scan, dim3(1), dim3(kScanThreads), 0, stream, n_lists, w.counts,
-                     w.hist, w.list_off, w.tiles, w.totals);
+                     w.list_off, w.tiles, w.totals);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_bm_fill, dim3(kHistWgs), dim3(kHistThreads), bins, stream, a, w.bt,
+  hipLaunchKernelGGL(k_bm_fill, dim3(n_hist), dim3(kHistThreads), bins, stream, a, w.bt,
                      n_blocks, n_lists, w.list_off, w.hist, w.entries);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int grid = 2 * device_cus();
   int slot;
-  trace_begin(stream, "k_bm_tiles", &slot);
-  hipLaunchKernelGGL((k_bm_tiles<D>), dim3(grid), dim3(kThreads), 0, stream, a, w, n_blocks);
+  trace_begin(stream, "k_bm_attn", &slot);
+  hipLaunchKernelGGL((k_bm_attn<D>), dim3(grid), dim3(kThreads), 0, stream, a, w, n_blocks);
   trace_end(stream, slot);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t pairs = (int64_t)a.L.n_q * hq;
+  const int per_wg = kHistThreads / (D / 8);
+  const dim3 mgrid((unsigned)((pairs + per_wg - 1) / per_wg));
   if (a.out_dtype == CSA_BF16)
-    hipLaunchKernelGGL((k_bm_diag<D, __bf16>), dim3(grid), dim3(kThreads), 0, stream, a, w);
+    hipLaunchKernelGGL((k_bm_merge<D, __bf16>), mgrid, dim3(kHistThreads), 0, stream, a, w);
   else
-    hipLaunchKernelGGL((k_bm_diag<D, float>), dim3(grid), dim3(kThreads), 0, stream, a, w);
+    hipLaunchKernelGGL((k_bm_merge<D, float>), mgrid, dim3(kHistThreads), 0, stream, a, w);
   return hipGetLastError();
 }
 
@@ -760,6 +819,7 @@ bool attn_block_mfma_supported(const AttnKernelArgs& a, int n_blocks) {
   const int G = a.q.h / a.k.h;
   const int D = a.q.d;
   return a.mode == CSA_SEL_BLOCK && a.dtype == CSA_BF16 && (D == 64 || D == 128) &&
+         a.idx_width <= 64 &&
          (int64_t)a.k.h * n_blocks <= kMaxLists &&
          a.v.d == D && a.block_size % kTN == 0 && G >= 1 && G <= kTM && (G & (G - 1)) == 0 &&
          a.scale_log2 > 0.f;
