@@ -22,6 +22,7 @@
 // rescaled.  Chunk summaries merge exactly as in "Context parallel attention:
 // exchange keys and merge softmax globally" (chunk summary paragraph).
 #include "attention.hpp"
+#include "mfma.hpp"
 
 namespace csa {
 
@@ -36,12 +37,19 @@ constexpr int kTK = 32;          // gathered keys per tile
 constexpr float kLazy = 8.0f;    // log2 headroom before the running max moves
 constexpr float kLn2 = 0.69314718055994531f;
 
-template <int DQK, int DV, bool ALIAS>
+// Query fragments kept in LDS instead of registers (the 576-wide shape would
+// otherwise not fit its query, accumulators and fragment pipeline in 512 registers).
+template <int DQK, bool ALIAS>
+constexpr int q_in_lds() { return DQK == 576 ? (ALIAS ? 8 : 4) : 0; }
+
+template <int DQK, int DV, bool ALIAS, int NW>
 struct TokLds {
   static constexpr int kPitch = DQK + 16;  // bf16 elements per K row
   static constexpr int kVPitch = DV + 16;
+  static constexpr int kQL = q_in_lds<DQK, ALIAS>();
   __bf16 k[2][kTK * kPitch];
   __bf16 v[ALIAS ? 1 : 2][ALIAS ? 8 : kTK * kVPitch];
+  bf16x8 q[NW][kQL > 0 ? kQL : 1][kWave];  // [wave][fragment][lane]
 };
 
 // byte offset of element e (a multiple of 4) of row r in a padded, swizzled tile
@@ -99,7 +107,8 @@ __device__ __forceinline__ void issue_tile(const View& T, int g, const int* keys
 
 template <int DQK, int DV, bool ALIAS, int NW, typename TO>
 __global__ __launch_bounds__(NW * kWave, 1) void k_tok_attn(AttnKernelArgs a) {
-  using Lds = TokLds<DQK, DV, ALIAS>;
+  using Lds = TokLds<DQK, DV, ALIAS, NW>;
+  constexpr int NQR = DQK / 16 - Lds::kQL;  // query fragments held in registers
   __shared__ Lds s;
   // slot keys of tiles kt, kt + 1 and kt + 2 live in distinct slots (kt % 3)
   __shared__ int s_keys[3][kTK];
@@ -117,16 +126,19 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_tok_attn(AttnKernelArgs a) {
   const int32_t* slots = a.idx + (int64_t)i * W;
   const float c = a.scale_log2;
 
-  bf16x8 qf[DQK / 16];
+  bf16x8 qf[NQR];
   {
     const __bf16* qp = elem_ptr<__bf16>(a.q, i, head);
 #pragma unroll
-    for (int ks = 0; ks < DQK / 16; ++ks)
+    for (int ks = 0; ks < NQR; ++ks)
       qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * half);
-  }
-  f32x16 o[DV / 32];
 #pragma unroll
-  for (int dt = 0; dt < DV / 32; ++dt) o[dt] = f32x16{};
+    for (int ks = NQR; ks < DQK / 16; ++ks)
+      s.q[wave][ks - NQR][lane] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * half);
+  }
+  f32x16 o[DV / 32];  // in AGPRs
+#pragma unroll
+  for (int dt = 0; dt < DV / 32; ++dt) to_agpr(o[dt], f32x16{});
   float m = -INFINITY, l = 0.f;
 
   const int n_kt = r.valid ? (W + kTK - 1) / kTK : 0;
@@ -155,18 +167,41 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_tok_attn(AttnKernelArgs a) {
     const int buf = kt & 1;
     const int ks3 = kt % 3;
     if (kt + 1 < n_kt) issue(kt + 1);  // lands in the other buffer while this one is used
-    // S^T = K Q^T: lane holds keys 8 (j / 4) + 4 half + (j % 4) of its query
+    // S^T = K Q^T: lane holds keys 8 (j / 4) + 4 half + (j % 4) of its query.
+    // Two accumulators (even and odd steps) keep consecutive MFMAs independent;
+    // fragment reads run two MFMAs ahead.
     const char* kb = reinterpret_cast<const char*>(s.k[buf]);
-    f32x16 sc = f32x16{};
+    f32x16 sc;
     {
+      constexpr int NK = DQK / 16;
       const int row = lane & 31;
+      auto kfrag = [&](int ks) {
+        return *reinterpret_cast<const bf16x8*>(kb + tile_off<Lds::kPitch>(row, 16 * ks + 8 * half));
+      };
+      // query fragments past NQR come from LDS, read along with the key fragment
+      auto qlds = [&](int ks) { return s.q[wave][ks - NQR][lane]; };
+      f32x16 sab[2];  // even and odd steps
+      bf16x8 ka[3], qa[3];
+      ka[0] = kfrag(0);
+      ka[1] = kfrag(1);
+      if (NQR <= 0) qa[0] = qlds(0);
+      if (NQR <= 1) qa[1] = qlds(1);
 #pragma unroll
-      for (int ks = 0; ks < DQK / 16; ++ks) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(
-            kb + tile_off<Lds::kPitch>(row, 16 * ks + 8 * half));
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sc, 0, 0, 0);
-        if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      for (int ks = 0; ks < NK; ++ks) {
+        if (ks + 2 < NK) {
+          ka[(ks + 2) % 3] = kfrag(ks + 2);
+          if (ks + 2 >= NQR) qa[(ks + 2) % 3] = qlds(ks + 2);
+        }
+        const bf16x8 q = ks < NQR ? qf[ks < NQR ? ks : 0] : qa[ks % 3];
+        if (ks < 2)
+          mfma_v0(sab[ks], ka[ks % 3], q);
+        else
+          mfma_v(sab[ks & 1], ka[ks % 3], q);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      fence_v(sab);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sc[j] = sab[0][j] + sab[1][j];
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -178,6 +213,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_tok_attn(AttnKernelArgs a) {
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * c;
     const bool need = mx > m + kLazy || (m == -INFINITY && mx > -INFINITY);
     if (__any(need)) {
+      fence_a(o);
       const float mn = need ? mx : m;
       const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mn);
       l *= alpha;
@@ -192,29 +228,37 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_tok_attn(AttnKernelArgs a) {
     bf16x8 pb[2];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float p = exp2f(fmaf(sc[j], c, -mu));
+      const float p = __builtin_amdgcn_exp2f(fmaf(sc[j], c, -mu));
       rs += p;
       pb[j >> 3][j & 7] = (__bf16)p;
     }
     rs += __shfl_xor(rs, 32, kWave);
     l += rs;
-    // O^T += V^T P^T with V^T read transposed from the row-major tile
+    // O^T += V^T P^T with V^T read transposed from the row-major tile; the
+    // transposing reads of the next two MFMAs are in flight during each one
     const __bf16* vbase = ALIAS ? s.k[buf] : s.v[ALIAS ? 0 : buf];
     constexpr int VP = ALIAS ? Lds::kPitch : Lds::kVPitch;
-    const int c16 = lane & 15;
-    const int grp = lane >> 4;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int ka = 16 * st + 4 * half + (c16 >> 2);
-      const int kb2 = ka + 8;
-#pragma unroll
-      for (int dt = 0; dt < DV / 32; ++dt) {
+    {
+      constexpr int NO = 2 * (DV / 32);  // MFMA i: key step i / (DV / 32), value block i % (DV / 32)
+      const int c16 = lane & 15;
+      const int grp = lane >> 4;
+      auto vfrag = [&](int i) {
+        const int st = i / (DV / 32), dt = i % (DV / 32);
+        const int ka_ = 16 * st + 4 * half + (c16 >> 2);
         const int dv = dt * 32 + 16 * (grp & 1) + 4 * (c16 & 3);
-        const bf16x4 lo = read_tr(vbase, tile_off<VP>(ka, dv));
-        const bf16x4 hi = read_tr(vbase, tile_off<VP>(kb2, dv));
-        const bf16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[st], o[dt], 0, 0, 0);
-        if ((dt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        const bf16x4 lo = read_tr(vbase, tile_off<VP>(ka_, dv));
+        const bf16x4 hi = read_tr(vbase, tile_off<VP>(ka_ + 8, dv));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      bf16x8 va[3];
+      va[0] = vfrag(0);
+      va[1] = vfrag(1);
+#pragma unroll
+      for (int i = 0; i < NO; ++i) {
+        if (i + 2 < NO) va[(i + 2) % 3] = vfrag(i + 2);
+        const int st = i / (DV / 32), dt = i % (DV / 32);
+        mfma_a(o[dt], va[i % 3], pb[st]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (kt + 2 < n_kt) fetch_keys(kt + 2);
@@ -222,6 +266,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_tok_attn(AttnKernelArgs a) {
     __syncthreads();
   }
 
+  fence_a(o);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   TO* out = reinterpret_cast<TO*>(a.out) + ((int64_t)i * a.q.h + head) * DV;
 #pragma unroll
