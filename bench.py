@@ -40,7 +40,65 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cold", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain device-to-device copy of known size (the reference "
+                        "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return p.parse_args()
+
+
+# Source files of each attention kernel; the HBM traffic of a kernel, taken
+# from counter runs, is reported only while these files are unchanged.
+KERNEL_SOURCES = {
+    "k_bm_attn": ["attn_block_mfma.hip"],
+    "k_tok_attn": ["attn_token_mfma.hip", "mfma.hpp"],
+    "k_attn_generic": ["attn_generic.hip"],
+}
+COMMON_SOURCES = ["common.hpp", "attention.hpp"]
+COPY_BYTES = 1 << 30
+
+
+def source_sha(kernel):
+    """sha256 (16 hex digits) of the kernel's source files and the shared headers."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "context_sparse_attention_amd", "csrc")
+    for f in KERNEL_SOURCES.get(kernel, []) + COMMON_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from profiles/traffic.json, or None.
+
+    The file holds FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of each kernel
+    and workload, and what the same counters read for a plain copy of
+    COPY_BYTES; a kernel's bytes are its counters divided by the copy's
+    counter-per-byte.  An entry counts only if its source hash matches.
+    """
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    cal = t["calibration"]
+    for e in t["kernels"]:
+        if e["kernel"] == kernel and e["workload"] == workload and \
+                e["source_sha"] == source_sha(kernel):
+            return e["fetch_kib"] * 1024 / cal["fetch_per_byte"] + \
+                e["write_kib"] * 1024 / cal["write_per_byte"]
+    return None
+
+
+def copy_calibration():
+    import torch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3}), flush=True)
 
 
 def permitted_bounds(w):
@@ -166,6 +224,9 @@ def main():
     from csa_inputs import make_workload
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     w = make_workload(args.workload)
     dev = "cuda"
 
@@ -285,7 +346,8 @@ def main():
                    "block_size": w.block_size, "topk": w.topk,
                    "effective_pairs": pairs, "effective_gflop": flops / 1e9},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": measured_traffic(dom, w.name),
                      "kernel_ms": dom_ms, "kernel_gflop": dom_flops / 1e9},
         "stages": {"select_ms_median": sel_med, "attention_ms_median": att_med,
                    "attention_TFLOPs": flops / (att_med * 1e-3) / 1e12,
