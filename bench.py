@@ -9,9 +9,12 @@ mode) for the DSA workload.  The default workload is the 8K-token MoBA shard
 (16 heads, D=128, last 2048 queries, blocks of 512, top-3 + own block).
 
 Printed: one JSON line.  ``value`` is effective TFLOP/s of the whole step
-(selected permitted query-key pairs x 2 x (Dqk + Dv) per second).  Extra
-fields: per-stage times (warm and with caches flushed), the roofline of the
-attention kernel, and the fp64 CPU oracle timed on a bounded sample of rows.
+(selected permitted query-key pairs x 2 x (Dqk + Dv) per second), timed over
+replays of the step captured as a HIP graph (the same library calls; every
+checked replay reproduces the eager output bit for bit); ``--no-graph`` times
+the eager calls instead, whose step time is also reported.  Extra fields:
+per-stage times (warm and with caches flushed), the roofline of the attention
+kernel, and the fp64 CPU oracle timed on a bounded sample of rows.
 """
 
 import argparse
@@ -40,6 +43,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cold", action="store_true")
+    p.add_argument("--no-graph", action="store_true",
+                   help="time the eager calls instead of a captured HIP graph of the step")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device-to-device copy of known size (the reference "
                         "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -211,6 +216,41 @@ class _SubRows:
         self.q_seq, self.q_pos, self.hq = w.q_seq[rows], w.q_pos[rows], w.hq
 
 
+def graph_step(torch, select, attend, args):
+    """Captures one step (selection + attention, the same calls) into a HIP graph and
+    times `steps` replays.  Every checked replay must reproduce the eager output and
+    log-sum-exp bit for bit, with eager work and synchronizations in between."""
+    ref_out, ref_lse = attend(select())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            attend(select())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        g_out, g_lse = attend(select())
+    torch.cuda.synchronize()
+    replays = 3
+    for _ in range(replays):
+        g.replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(g_out, ref_out) and torch.equal(g_lse, ref_lse)):
+            raise RuntimeError("graph replay differs from the eager step")
+        attend(select())  # eager work between replays
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / args.steps, replays
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -275,7 +315,13 @@ def main():
     t1 = time.perf_counter()
     traced = csa.trace_collect()
     csa.trace_begin(0)
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    eager_ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_per_step = eager_ms_per_step
+    graph = None
+    if not args.no_graph:
+        graph_ms, replays = graph_step(torch, select, attend, args)
+        ms_per_step = graph_ms
+        graph = {"ms_per_step": graph_ms, "replays_checked": replays}
     sel_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(args.steps)]
     att_ms = [ev[s][1].elapsed_time(ev[s][2]) for s in range(args.steps)]
     kern = {}
@@ -358,6 +404,7 @@ def main():
                    "select_kernel": {"kernel": sk, "ms": sk_ms, "rate": sk_rate,
                                      "unit": sk_unit, "frac": sk_rate / sk_peak},
                    "kernels_ms": {k: float(np.mean(v)) for k, v in kern.items()},
+                   "eager_ms_per_step": eager_ms_per_step, "graph": graph,
                    "cold": cold},
     }
     if not args.no_cpu_baseline:
