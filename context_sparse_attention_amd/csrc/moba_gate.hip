@@ -8,7 +8,9 @@
 // reading of "Q x K^T" at block granularity: q . mean(k) = mean(q . k)).
 //
 // Three kernels:
-//   k_moba_need  - per packed sequence, the highest own block of any local row
+//   k_gate_prep  - block table and, per packed sequence, the highest own block of
+//                  any local row (one workgroup, small shards; k_block_table +
+//                  k_moba_need otherwise)
 //                  (blocks at or after it are never candidates, so they are
 //                  not pooled);
 //   k_moba_pool  - fp32 block means (and their bf16 high/low split), one
@@ -21,6 +23,7 @@
 #include <float.h>
 
 #include "common.hpp"
+#include "block_table.hpp"
 
 namespace csa {
 
@@ -60,6 +63,26 @@ size_t carve_bytes(int n_seq, int n_blocks, int hkv, int d, int block_size) {
   c.take<__bf16>((size_t)n_blocks * hkv * d);
   c.take<__bf16>((size_t)n_blocks * hkv * d);
   return align_up(c.used, 256);
+}
+
+// Block table and per-sequence need in one workgroup, for shards of at most
+// kPrepRows rows in at most kPrepSeqs sequences (the need is reduced in LDS);
+// larger shards are faster with the separate, wide k_moba_need.
+constexpr int kPrepSeqs = 4096;
+constexpr int kPrepRows = 4096;
+
+__global__ __launch_bounds__(kTableThreads) void k_gate_prep(DevLayout L, int block_size,
+                                                             int n_blocks, BlockTable bt,
+                                                             int32_t* __restrict__ need) {
+  __shared__ int s_need[kPrepSeqs];
+  for (int s = threadIdx.x; s < L.n_seq; s += kTableThreads) s_need[s] = 0;
+  block_table_wg(L.cu, L.n_seq, block_size, n_blocks, bt);  // ends with a barrier
+  for (int i = threadIdx.x; i < L.n_q; i += kTableThreads) {
+    const RowKeys r = row_keys(L, i);
+    if (r.valid) atomicMax(&s_need[r.seq], bt.blk_off[r.seq] + (r.hi - r.lo) / block_size);
+  }
+  __syncthreads();
+  for (int s = threadIdx.x; s < L.n_seq; s += kTableThreads) need[s] = s_need[s];
 }
 
 __global__ void k_moba_need(DevLayout L, int block_size, const int32_t* __restrict__ blk_off,
@@ -412,13 +435,21 @@ template <typename T>
 hipError_t launch_typed(const MobaGateArgs& a, hipStream_t stream) {
   const int n_seq = a.L.n_seq;
   MobaWs w = carve_moba(a.ws, n_seq, a.n_blocks, a.k.h, a.k.d, a.block_size);
-  hipError_t e = launch_block_table(a.L.cu, n_seq, a.block_size, a.n_blocks, w.bt, w.need,
-                                    n_seq, stream);
-  if (e != hipSuccess) return e;
-  if (a.L.n_q == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_moba_need, dim3((a.L.n_q + 255) / 256), dim3(256), 0, stream, a.L,
-                     a.block_size, w.bt.blk_off, w.need);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipError_t e;
+  if (n_seq <= kPrepSeqs && a.L.n_q <= kPrepRows) {
+    hipLaunchKernelGGL(k_gate_prep, dim3(1), dim3(kTableThreads), 0, stream, a.L, a.block_size,
+                       a.n_blocks, w.bt, w.need);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.L.n_q == 0) return hipSuccess;
+  } else {
+    e = launch_block_table(a.L.cu, n_seq, a.block_size, a.n_blocks, w.bt, w.need, n_seq,
+                           stream);
+    if (e != hipSuccess) return e;
+    if (a.L.n_q == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_moba_need, dim3((a.L.n_q + 255) / 256), dim3(256), 0, stream, a.L,
+                       a.block_size, w.bt.blk_off, w.need);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const bool use_mfma = a.dtype == CSA_BF16 && (a.q.d == 64 || a.q.d == 128 || a.q.d == 256);
   if (a.n_blocks > 0) {
     hipLaunchKernelGGL((k_moba_pool<T>), dim3(a.n_blocks * a.k.h), dim3(kPoolThreads), 0,
