@@ -85,6 +85,18 @@ __device__ __forceinline__ float acc_scale(float x, float s) {
   return y;
 }
 
+// One global_load_lds_dwordx4 (1 KiB of LDS from m0 on, 16 bytes per lane).
+// Issued as assembly so that the compiler does not see an LDS store: it would
+// otherwise wait for the gather before every later LDS read of the current
+// tile.  The gathered tile is read only after the explicit wait and barrier at
+// the end of the tile that issued it.  This kernel has no other use of m0.
+__device__ __forceinline__ void gather16(const void* src, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_dst)
+               : "memory", "m0");
+}
+
 template <int D>
 __device__ __forceinline__ void issue_tile(const View& T, int g, const int* keys, __bf16* tile,
                                            int wave, int nwaves) {
@@ -99,9 +111,9 @@ __device__ __forceinline__ void issue_tile(const View& T, int g, const int* keys
     const int pu = (byte - row * kPitchB) >> 4;
     const int u = pu < D / 8 ? (pu ^ ((row >> 2) & 1)) : 0;
     const __bf16* src = elem_ptr<__bf16>(T, keys[row], g) + u * 8;
-    __builtin_amdgcn_global_load_lds(
-        (const void*)src, (__attribute__((address_space(3))) void*)((lds_bytes)(void*)tile + ch * 1024),
-        16, 0, 0);
+    const uint32_t dst = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((lds_bytes)(void*)tile + ch * 1024));
+    gather16(src, __builtin_amdgcn_readfirstlane(dst));
   }
 }
 
