@@ -268,111 +268,102 @@ __global__ __launch_bounds__(kScanThreads) void k_bm_scan(int n_lists,
 // MFMA tile machinery
 // ---------------------------------------------------------------------------
 
-// LDS tiles use padded row pitches rather than swizzles, so that every
-// fragment read is one per-lane base address plus a compile-time offset.  Both
-// pitches are 4 mod 32 banks: eight consecutive rows read at one column cover
-// all 32 banks once.
-//   K   [kTN][D + 8]: row-major key tile.
-//   V^T [D][kTN + 8]: value column x key.  The 4-key groups of a row sit at
-//       permuted positions (vt_pos) so that the two groups one MFMA operand
-//       needs (keys 16s + 4h + 0..3 and 16s + 8 + 4h + 0..3) are adjacent.
+// LDS tiles are row-major with padded row pitches, filled straight from global
+// memory by the gather instructions (no staging registers, no VALU work):
+//   K [kTN][D + 8]: pitch 4 mod 32 banks, so eight consecutive rows read at one
+//       column (the S^T operand reads) cover all 32 banks once;
+//   V [kTN][D + 16]: pitch 8 mod 32 banks, so the four rows one transposing
+//       read touches (ds_read_b64_tr_b16) cover all 32 banks once.
+// Every fragment read is one per-lane base address plus a compile-time offset.
 template <int D>
 struct Lds {
   static constexpr int kKP = D + 8;
-  static constexpr int kVP = kTN + 8;
+  static constexpr int kVR = D + 16;
   __bf16 k[2][kTN * kKP];
-  __bf16 vt[2][D * kVP];
+  __bf16 v[2][kTN * kVR];
 };
 
-// position of 4-key group q in a V^T row: groups 4s, 4s + 2, 4s + 1, 4s + 3
-__device__ inline int vt_pos(int q) { return (q & ~3) | ((q & 1) << 1) | ((q >> 1) & 1); }
+// One global_load_lds_dwordx4: 1 KiB of LDS from m0 on, lane l writing bytes
+// [16 l, 16 l + 16), read from base + off.  Issued as assembly so that the
+// compiler does not see an LDS store: it would otherwise wait for the gather
+// before every later LDS read of the tile being computed.  The gathered tile
+// is read only after the explicit wait and barrier that close the tile during
+// which it was issued.  The kernels of this file have no other use of m0.
+__device__ __forceinline__ void gather16(uint32_t off, const char* base, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(lds_dst)
+               : "memory", "m0");
+}
 
-// Global -> register staging of one key/value tile (all threads).  The staging
-// registers are ext-vector values so that they stay in VGPRs.  Addresses are a
-// uniform tile base plus per-thread byte offsets that do not change from tile
-// to tile, so a load costs no address arithmetic.
-//   K: thread t loads 16-byte unit t % kUnits of rows t / kUnits + kRowsPerPass * p.
-//   V: thread t < kVThreads loads 4-key group t % 16, value columns 8 (t / 16) .. +7,
-//      so that the 16 threads of a store phase write one V^T row.
+// s_waitcnt vmcnt(0) (gfx9 encoding, the other counters left alone)
+__device__ __forceinline__ void wait_gathers() {
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  typedef __attribute__((address_space(3))) const char* lds_bytes;
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_bytes)p));
+}
+
+// The gather of one key/value tile, split over the workgroup's waves in 1 KiB
+// chunks: chunk c of a tile is issued by wave c % kWaves.  Lane l of chunk c
+// fills 16-byte slot 64 c + l of the padded tile, i.e. unit (slot % units) of
+// row (slot / units); pad slots re-read unit 0 of their row.  The per-lane
+// byte offsets from the tile's first key do not change from tile to tile.
 template <int D>
-struct Stage {
-  static constexpr int kUnits = D / 8;                  // 16-byte units per row
-  static constexpr int kRowsPerPass = kThreads / kUnits;
-  static constexpr int kPasses = kTN / kRowsPerPass;
-  static constexpr int kVThreads = kTN * D / 32;        // 4 keys x 8 values each
-  typedef uint32_t KVec __attribute__((ext_vector_type(4 * kPasses)));
-  typedef uint32_t VVec __attribute__((ext_vector_type(16)));
-  KVec kr;
-  VVec vr;  // 4 keys x 8 bf16: key kk in words 4kk .. 4kk+3
+struct Gather {
+  static constexpr int kKU = Lds<D>::kKP / 8;   // 16-byte slots per K row
+  static constexpr int kVU = Lds<D>::kVR / 8;   // 16-byte slots per V row
+  static constexpr int kKC = kTN * kKU / 64;    // 1 KiB chunks per K tile
+  static constexpr int kVC = kTN * kVU / 64;
+  static constexpr int kKPer = (kKC + kWaves - 1) / kWaves;
+  static constexpr int kVPer = (kVC + kWaves - 1) / kWaves;
+  static_assert(kTN * kKU % 64 == 0 && kTN * kVU % 64 == 0, "tiles must be whole KiBs");
+  uint32_t ko[kKPer], vo[kVPer];
 
-  struct Offs {
-    uint32_t k[kPasses];
-    uint32_t v[4];
-  };
-
-  // Byte offsets of this thread's rows from the tile base; rows at or beyond
-  // `rows` repeat row `rows - 1` (their scores are masked later).
-  static __device__ __forceinline__ void offsets(const View& K, const View& V, int rows,
-                                                 Offs& o) {
-    const int t = threadIdx.x;
-    const int ku8 = (t % kUnits) * 8;
+  // rows at or beyond `rows` repeat row rows - 1 (their scores are masked)
+  __device__ __forceinline__ void init(const View& K, const View& V, int rows) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
 #pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      const int row = min(p * kRowsPerPass + t / kUnits, rows - 1);
-      o.k[p] = (uint32_t)((row * K.stride_n + ku8) * (int64_t)sizeof(__bf16));
+    for (int j = 0; j < kKPer; ++j) {
+      const int slot = (wave + kWaves * j) * 64 + lane;
+      const int row = min(slot / kKU, rows - 1);
+      const int u = slot % kKU;
+      ko[j] = (uint32_t)((row * K.stride_n + (u < D / 8 ? u : 0) * 8) * (int64_t)sizeof(__bf16));
     }
-    const int vu8 = (t / 16) * 8;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int key = min((t % 16) * 4 + kk, rows - 1);
-      o.v[kk] = (uint32_t)((key * V.stride_n + vu8) * (int64_t)sizeof(__bf16));
+    for (int j = 0; j < kVPer; ++j) {
+      const int slot = (wave + kWaves * j) * 64 + lane;
+      const int row = min(slot / kVU, rows - 1);
+      const int u = slot % kVU;
+      vo[j] = (uint32_t)((row * V.stride_n + (u < D / 8 ? u : 0) * 8) * (int64_t)sizeof(__bf16));
     }
   }
 
-  __device__ __forceinline__ void load(const char* kb, const char* vb, const Offs& o) {
-    const int t = threadIdx.x;
+  __device__ __forceinline__ void issue(const char* kb, const char* vb, Lds<D>& s, int buf) const {
+    const int wave = threadIdx.x / kWave;
+    const uint32_t kl = lds_addr(&s.k[buf][0]), vl = lds_addr(&s.v[buf][0]);
 #pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      const uint4 x = *reinterpret_cast<const uint4*>(kb + o.k[p]);
-      kr[4 * p] = x.x;
-      kr[4 * p + 1] = x.y;
-      kr[4 * p + 2] = x.z;
-      kr[4 * p + 3] = x.w;
+    for (int j = 0; j < kKPer; ++j) {
+      const int c = wave + kWaves * j;
+      if (c < kKC) gather16(ko[j], kb, __builtin_amdgcn_readfirstlane(kl + c * 1024));
     }
-    if (t < kVThreads) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint4 x = *reinterpret_cast<const uint4*>(vb + o.v[kk]);
-        vr[4 * kk] = x.x;
-        vr[4 * kk + 1] = x.y;
-        vr[4 * kk + 2] = x.z;
-        vr[4 * kk + 3] = x.w;
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(Lds<D>& s, int buf) const {
-    const int t = threadIdx.x;
-    __bf16* kd = &s.k[buf][(t / kUnits) * Lds<D>::kKP + (t % kUnits) * 8];
-#pragma unroll
-    for (int p = 0; p < kPasses; ++p)
-      *reinterpret_cast<uint4*>(kd + p * kRowsPerPass * Lds<D>::kKP) =
-          make_uint4(kr[4 * p], kr[4 * p + 1], kr[4 * p + 2], kr[4 * p + 3]);
-    if (t < kVThreads) {
-      __bf16* vd = &s.vt[buf][(t / 16) * 8 * Lds<D>::kVP + vt_pos(t % 16) * 4];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // value columns 2w (low halves) and 2w + 1 (high halves) of this thread's eight
-        const uint32_t a0 = vr[w], a1 = vr[4 + w], a2 = vr[8 + w], a3 = vr[12 + w];
-        const uint2 even = make_uint2((a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16));
-        const uint2 odd = make_uint2((a0 >> 16) | (a1 & 0xffff0000u),
-                                     (a2 >> 16) | (a3 & 0xffff0000u));
-        *reinterpret_cast<uint2*>(vd + (2 * w) * Lds<D>::kVP) = even;
-        *reinterpret_cast<uint2*>(vd + (2 * w + 1) * Lds<D>::kVP) = odd;
-      }
+    for (int j = 0; j < kVPer; ++j) {
+      const int c = wave + kWaves * j;
+      if (c < kVC) gather16(vo[j], vb, __builtin_amdgcn_readfirstlane(vl + c * 1024));
     }
   }
 };
+
+__device__ __forceinline__ bf16x4 read_tr(const __bf16* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4* lds_ptr;
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(const_cast<__bf16*>(p)));
+  return __builtin_bit_cast(bf16x4, x);
+}
 
 // Per-wave online-softmax state for 32 queries (one per lane pair).  m is the
 // reference maximum the exponentials are taken against (log2 units); it is
@@ -406,19 +397,26 @@ template <int D, bool MASK>
 __device__ __forceinline__ void wave_tile(const Lds<D>& s, int buf, const bf16x8* qf, float c,
                                           WaveState<D>& st, int tile_key0, int kvalid,
                                           int qpos) {
-  constexpr int KP = Lds<D>::kKP, VP = Lds<D>::kVP;
+  constexpr int KP = Lds<D>::kKP, VR = Lds<D>::kVR;
   constexpr int NS = 2 * (D / 16);  // S^T MFMAs: MFMA i takes key block i & 1, step i >> 1
   constexpr int NDT = D / 32;       // value blocks
   constexpr int NO = 4 * NDT;       // O^T MFMAs: MFMA i takes value block i % NDT, step i / NDT
   const int lane = threadIdx.x & (kWave - 1);
   const int half = lane >> 5;
   const __bf16* kp = &s.k[buf][(lane & 31) * KP + 8 * half];
-  const __bf16* vp = &s.vt[buf][(lane & 31) * VP + 8 * half];
+  // V^T fragment: in a 16-lane group, lane c addresses 4 values of key
+  // kb + c / 4 at value column dvb + 4 (c % 4) and receives column dvb + c of
+  // keys kb .. kb + 3; lanes 16..31 take the next 16 columns, lanes 32..63 the
+  // keys 4 further on
+  const int c16 = lane & 15;
+  const __bf16* vp = &s.v[buf][(4 * half + (c16 >> 2)) * VR + 16 * ((lane >> 4) & 1) + 4 * (c16 & 3)];
   auto kfrag = [&](int i) {
     return *reinterpret_cast<const bf16x8*>(kp + (i & 1) * 32 * KP + (i >> 1) * 16);
   };
-  auto vfrag = [&](int i) {
-    return *reinterpret_cast<const bf16x8*>(vp + (i % NDT) * 32 * VP + (i / NDT) * 16);
+  auto vfrag = [&](int i) {  // value block i % NDT, keys 16 (i / NDT) + 4 half + (0..3, 8..11)
+    const __bf16* p = vp + (i / NDT) * 16 * VR + (i % NDT) * 32;
+    const bf16x4 lo = read_tr(p), hi = read_tr(p + 8 * VR);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
 
   f32x16 sc[2] = {f32x16{}, f32x16{}};
@@ -490,11 +488,10 @@ __device__ __forceinline__ void wave_tile(const Lds<D>& s, int buf, const bf16x8
 }
 
 // Runs every key tile of [key0, key0 + nkeys) through the workgroup.  Tile kt
-// is stored into LDS buffer kt & 1 and consumed after one barrier; the barrier
-// of tile kt + 1 also orders every read of buffer kt & 1 before its reuse by
-// tile kt + 2.  The global loads of tile kt + 1 are issued before the math of
-// tile kt, so their latency hides behind it.  Without MASK every tile is full
-// (nkeys is a multiple of kTN).
+// is gathered into LDS buffer kt & 1 while tile kt - 1 is computed; each tile
+// ends with a wait for this wave's gathers and a barrier, which makes the next
+// tile visible and orders every read of a buffer before its next gather.
+// Without MASK every tile is full (nkeys is a multiple of kTN).
 // active: this wave has work; wave_max_pos: skip tiles entirely past it (MASK).
 template <int D, bool MASK>
 __device__ __forceinline__ void run_keys(Lds<D>& s, const View& K, const View& V, int g,
@@ -504,36 +501,29 @@ __device__ __forceinline__ void run_keys(Lds<D>& s, const View& K, const View& V
   key0 = __builtin_amdgcn_readfirstlane(key0);
   nkeys = __builtin_amdgcn_readfirstlane(nkeys);
   const int n_kt = (nkeys + kTN - 1) / kTN;
-  typename Stage<D>::Offs full;
-  Stage<D>::offsets(K, V, kTN, full);
+  Gather<D> gt;
+  gt.init(K, V, MASK ? min(kTN, nkeys) : kTN);
   const char* kb = reinterpret_cast<const char*>(elem_ptr<__bf16>(K, key0, g));
   const char* vb = reinterpret_cast<const char*>(elem_ptr<__bf16>(V, key0, g));
   const int64_t kstep = kTN * K.stride_n * (int64_t)sizeof(__bf16);
   const int64_t vstep = kTN * V.stride_n * (int64_t)sizeof(__bf16);
-  Stage<D> stage;
-  auto load_tile = [&](int kt) {
-    const int rows = nkeys - kt * kTN;
-    if (MASK && rows < kTN) {
-      typename Stage<D>::Offs part;
-      Stage<D>::offsets(K, V, rows, part);
-      stage.load(kb, vb, part);
-    } else {
-      stage.load(kb, vb, full);
-    }
-    kb += kstep;
-    vb += vstep;
-  };
-  if (n_kt > 0) load_tile(0);
+  gt.issue(kb, vb, s, 0);
+  wait_gathers();
+  __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
     const int tk0 = key0 + kt * kTN;
-    stage.store(s, buf);
-    __syncthreads();
-    if (kt + 1 < n_kt) load_tile(kt + 1);
+    if (kt + 1 < n_kt) {
+      kb += kstep;
+      vb += vstep;
+      if (MASK && nkeys - (kt + 1) * kTN < kTN) gt.init(K, V, nkeys - (kt + 1) * kTN);
+      gt.issue(kb, vb, s, buf ^ 1);
+    }
     if (active && (!MASK || tk0 <= wave_max_pos))
       wave_tile<D, MASK>(s, buf, qf, c, st, tk0, min(kTN, nkeys - kt * kTN), qpos);
+    wait_gathers();
+    __syncthreads();
   }
-  __syncthreads();  // the caller may restage buffer 0 right away
 }
 
 template <int D>
