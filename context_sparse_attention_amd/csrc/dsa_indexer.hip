@@ -19,6 +19,7 @@
 //                  keys, then an index-order compaction that takes every larger
 //                  logit and the lowest-index equal ones (ties to the lower index).
 #include "common.hpp"
+#include "gather.hpp"
 
 namespace csa {
 
@@ -92,7 +93,10 @@ __global__ __launch_bounds__(kLgThreads, 2) void k_dsa_logits_mfma(View iq, View
                                                                    const float* __restrict__ w,
                                                                    int64_t w_stride, DevLayout L,
                                                                    float* __restrict__ logits) {
-  __shared__ __bf16 s_k[2][kLgKeys * DI];
+  // key tiles [kLgKeys][DI + 8]: pitch 4 mod 32 banks, so eight consecutive rows
+  // read at one column (the B operand reads) cover all 32 banks once
+  constexpr int KP = DI + 8;
+  __shared__ __bf16 s_k[2][kLgKeys * KP];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int half = lane >> 5;
@@ -137,36 +141,62 @@ __global__ __launch_bounds__(kLgThreads, 2) void k_dsa_logits_mfma(View iq, View
       wr[mt][j] = w[(int64_t)rowc * w_stride + mt * 32 + 8 * (j >> 2) + 4 * half + (j & 3)];
   }
 
-  constexpr int kUnits = DI / 8;
-  constexpr int kRowsPerPass = kLgThreads / kUnits;
-  constexpr int kPasses = kLgKeys / kRowsPerPass;
+  // Tile gather: chunk c (1 KiB) of a tile is issued by wave c % kLgWaves; lane
+  // l of chunk c fills 16-byte slot 64 c + l, i.e. unit (slot % kU) of row
+  // (slot / kU); pad slots re-read unit 0.  Rows past k_end repeat the last key.
+  constexpr int kU = KP / 8;
+  constexpr int kChunks = kLgKeys * kU / 64;
+  constexpr int kPer = (kChunks + kLgWaves - 1) / kLgWaves;
+  static_assert(kLgKeys * kU % 64 == 0, "tiles must be whole KiBs");
+  uint32_t goff[kPer];
+  auto offsets = [&](int rows) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int slot = (wave + kLgWaves * j) * 64 + lane;
+      const int r = min(slot / kU, rows - 1);
+      const int u = slot % kU;
+      goff[j] = (uint32_t)((r * ik.stride_n + (u < DI / 8 ? u : 0) * 8) * (int64_t)sizeof(__bf16));
+    }
+  };
+  auto issue = [&](int key0, int buf) {
+    const char* base = reinterpret_cast<const char*>(elem_ptr<__bf16>(ik, key0, 0));
+    const uint32_t l0 = lds_addr(&s_k[buf][0]);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int c = wave + kLgWaves * j;
+      if (c < kChunks) gather16(goff[j], base, __builtin_amdgcn_readfirstlane(l0 + c * 1024));
+    }
+  };
   const int n_kt = (k_end - k_begin + kLgKeys - 1) / kLgKeys;
+  offsets(min(kLgKeys, k_end - k_begin));
+  issue(k_begin, 0);
+  wait_gathers();
+  __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
     const int key0 = k_begin + kt * kLgKeys;
-#pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      const int r = p * kRowsPerPass + threadIdx.x / kUnits;
-      const int u = threadIdx.x % kUnits;
-      const int key = min(key0 + r, k_end - 1);
-      const uint4 x = *reinterpret_cast<const uint4*>(elem_ptr<__bf16>(ik, key, 0) + u * 8);
-      *reinterpret_cast<uint4*>(&s_k[buf][r * DI + ((u ^ (r & 7)) << 3)]) = x;
+    if (kt + 1 < n_kt) {
+      const int next = key0 + kLgKeys;
+      if (k_end - next < kLgKeys) offsets(k_end - next);
+      issue(next, buf ^ 1);  // lands while this tile is computed
     }
-    __syncthreads();
     if (hi >= lo && key0 <= hi) {
 #pragma unroll
       for (int nt = 0; nt < kLgKeys / 32; ++nt) {
         const int r = nt * 32 + (lane & 31);
+        const __bf16* kp = &s_k[buf][r * KP + 8 * half];
         f32x16 acc[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
+        bf16x8 bq[3];
+        bq[0] = *reinterpret_cast<const bf16x8*>(kp);
+        if (KS > 1) bq[1] = *reinterpret_cast<const bf16x8*>(kp + 16);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 b =
-              *reinterpret_cast<const bf16x8*>(&s_k[buf][r * DI + (((2 * ks + half) ^ (r & 7)) << 3)]);
+          if (ks + 2 < KS) bq[(ks + 2) % 3] = *reinterpret_cast<const bf16x8*>(kp + 16 * (ks + 2));
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
-            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][ks], b, acc[mt], 0, 0, 0);
+            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][ks], bq[ks % 3], acc[mt], 0, 0, 0);
         }
         float v = 0.f;
 #pragma unroll
@@ -179,7 +209,8 @@ __global__ __launch_bounds__(kLgThreads, 2) void k_dsa_logits_mfma(View iq, View
           logits[(int64_t)row * L.n_kv + key] = v;
       }
     }
-    // the barrier of the next tile orders these reads before buffer reuse
+    wait_gathers();
+    __syncthreads();  // the next tile has landed; this buffer is free for reuse
   }
 }
 
@@ -239,8 +270,23 @@ __global__ __launch_bounds__(kSelThreads) void k_dsa_select(DevLayout L, int top
     return;
   }
   const bool cached = n <= kSelCache;
-  if (cached)
-    for (int t = threadIdx.x; t < n; t += kSelThreads) s_key[t] = float_key(row[t]);
+  if (cached) {
+    // eight independent, coalesced loads in flight per thread
+    constexpr int kU = 8;
+    for (int base = 0; base < n; base += kSelThreads * kU) {
+      float x[kU];
+#pragma unroll
+      for (int j = 0; j < kU; ++j) {
+        const int t = base + j * kSelThreads + threadIdx.x;
+        x[j] = t < n ? row[t] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < kU; ++j) {
+        const int t = base + j * kSelThreads + threadIdx.x;
+        if (t < n) s_key[t] = float_key(x[j]);
+      }
+    }
+  }
 
   uint32_t prefix = 0, mask = 0;
   int remaining = topk;
