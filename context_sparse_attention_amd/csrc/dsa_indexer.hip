@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kLogitThreads) void k_dsa_logits(View iq, View ik,
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
-constexpr int kLgWaves = 8;                 // query tokens per workgroup (one per wave)
+constexpr int kLgWaves = 4;                 // query tokens per workgroup (one per wave)
 constexpr int kLgThreads = kLgWaves * kWave;
 constexpr int kLgKeys = 64;                 // keys per LDS tile
 constexpr int kLgChunk = 2048;              // keys per workgroup
