@@ -67,6 +67,8 @@ struct BmWs {
   int32_t* totals;    // [16]  [0] list tiles, [kQueue0 + x] work-queue counter of XCD x
   int4* pinfo;        // [n_q * hq]  own-block multiplicity, full-block slot mask (lo, hi),
                       //             first own-block slot (-1 if none)
+  int4* rowinfo;      // [n_q]  own block (-1 if the row has no key), position, own block's
+                      //        first key, 0
   int32_t* entries;   // [n_q * hq * W]  flat slot ids
   float2* part_ml;    // [n_q * hq * W]  (m in log2 units, l)
   __bf16* part_o;     // [n_q * hq * W * D]  normalized partial output z / l
@@ -98,6 +100,7 @@ size_t carve_bm(void* base, int n_q, int n_seq, int n_blocks, int hq, int hkv, i
   t.tiles = c.take<int2>(max_query_tiles(slots, n_lists));
   t.totals = c.take<int32_t>(16);
   t.pinfo = c.take<int4>((size_t)n_q * hq);
+  t.rowinfo = c.take<int4>((size_t)n_q);
   t.entries = c.take<int32_t>(slots);
   t.part_ml = c.take<float2>(slots);
   t.part_o = c.take<__bf16>(slots * dv);
@@ -129,7 +132,8 @@ __device__ inline void pair_range(int64_t pairs, int64_t* b, int64_t* e) {
 __global__ __launch_bounds__(kHistThreads) void k_bm_hist(AttnKernelArgs a, BlockTable bt,
                                                           int n_blocks, int n_lists,
                                                           int32_t* __restrict__ hist,
-                                                          int4* __restrict__ pinfo) {
+                                                          int4* __restrict__ pinfo,
+                                                          int4* __restrict__ rowinfo) {
   extern __shared__ int s_bins[];
   for (int l = threadIdx.x; l < n_lists; l += kHistThreads) s_bins[l] = 0;
   __syncthreads();
@@ -157,6 +161,10 @@ __global__ __launch_bounds__(kHistThreads) void k_bm_hist(AttnKernelArgs a, Bloc
       }
     }
     pinfo[pair] = make_int4(mult, (int)(uint32_t)full, (int)(uint32_t)(full >> 32), own_slot);
+    if (h == 0) {
+      const int ob = r.valid ? bt.blk_off[r.seq] + (r.hi - r.lo) / a.block_size : -1;
+      rowinfo[i] = make_int4(ob, r.hi, ob >= 0 ? bt.blocks[ob].x : 0, 0);
+    }
   }
   __syncthreads();
   for (int l = threadIdx.x; l < n_lists; l += kHistThreads)
@@ -604,9 +612,32 @@ __device__ __forceinline__ void list_item(Lds<D>& s, const AttnKernelArgs& a, co
 // boundaries) are handled run by run: each lane only takes keys in the pass of
 // its own row's block.  The summary goes to the (row, head)'s first own-block
 // slot; rows that did not select their own block write nothing.
+// Lowest set bit at or above `from` of the 128-bit mask (m1:m0), or n if none is below n.
+__device__ inline int next_set(uint64_t m0, uint64_t m1, int from, int n) {
+  if (from < 64) {
+    const uint64_t x = m0 & (~0ull << from);
+    if (x) return min(n, __builtin_ctzll(x));
+    from = 64;
+  }
+  if (from < 128) {
+    const uint64_t x = m1 & (~0ull << (from - 64));
+    if (x) return min(n, 64 + __builtin_ctzll(x));
+  }
+  return n;
+}
+
+// Diagonal tile: TR = kTM / G consecutive rows x the G query heads of one key
+// head against their own blocks, with the causal mask at each row's global
+// position.  Rows of a tile whose own blocks differ (sequence or zigzag-chunk
+// boundaries) are handled run by run: each lane only takes keys in the pass of
+// its own row's block.  The summary goes to the (row, head)'s first own-block
+// slot; rows that did not select their own block write nothing.  The runs are
+// found in parallel (one bit per row starting a run); positions normally rise
+// along a run, so its last row holds its largest position.
 template <int D>
-__device__ __forceinline__ void diag_item(Lds<D>& s, int* s_own, int* s_pos,
-                                          const AttnKernelArgs& a, const BmWs& w, int item) {
+__device__ __forceinline__ void diag_item(Lds<D>& s, int* s_own, int* s_pos, int* s_ostart,
+                                          uint64_t* s_mask, const AttnKernelArgs& a,
+                                          const BmWs& w, int item) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int half = lane >> 5;
@@ -614,36 +645,53 @@ __device__ __forceinline__ void diag_item(Lds<D>& s, int* s_own, int* s_pos,
   const int hq = a.q.h;
   const int G = hq / hkv;
   const int TR = kTM / G;
-  const int B = a.block_size;
   const int tile = item / hkv;
   const int g = item % hkv;
   const int r0 = tile * TR;
   const int nrows = min(TR, a.L.n_q - r0);
-  if (threadIdx.x < nrows) {
-    const RowKeys r = row_keys(a.L, r0 + threadIdx.x);
-    s_own[threadIdx.x] = r.valid ? w.bt.blk_off[r.seq] + (r.hi - r.lo) / B : -1;
-    s_pos[threadIdx.x] = r.hi;
-  }
-  __syncthreads();
   const int n = wave * kQW + (lane & 31);
   const int rl = n % TR;
   const int head = g * G + n / TR;
   const bool valid = rl < nrows;
   const int rowc = r0 + (valid ? rl : 0);
-  const int my_pos = valid ? s_pos[rl] : -1;
   const int pair = rowc * hq + head;
   const int own_slot = w.pinfo[pair].w;  // the load overlaps the key loop
+  bf16x8 qf[D / 16];
+  load_q<D>(a.q, rowc, head, qf);
+  if (threadIdx.x < kTM) {  // waves 0 and 1: one row each
+    const int t = threadIdx.x;
+    bool start = false, bad = false;
+    if (t < nrows) {
+      const int4 ri = w.rowinfo[r0 + t];
+      const int4 rp = w.rowinfo[r0 + max(t - 1, 0)];
+      start = t == 0 || rp.x != ri.x;
+      bad = !start && rp.y >= ri.y;
+      s_own[t] = ri.x;
+      s_pos[t] = ri.y;
+      s_ostart[t] = ri.z;
+    }
+    const uint64_t sm = __builtin_amdgcn_ballot_w64(start);
+    const uint64_t bm = __builtin_amdgcn_ballot_w64(bad);
+    if (lane == 0) {
+      s_mask[wave] = sm;
+      s_mask[2 + wave] = bm;
+    }
+  }
+  __syncthreads();
+  const int my_pos = valid ? s_pos[rl] : -1;
+  const uint64_t m0 = s_mask[0], m1 = s_mask[1];
+  const bool rising = (s_mask[2] | s_mask[3]) == 0;
 
   WaveState<D> st;
   reset(st);
-  bf16x8 qf[D / 16];
-  load_q<D>(a.q, rowc, head, qf);
   bool has_keys = false;
   for (int start = 0; start < nrows;) {
+    const int end = next_set(m0, m1, start + 1, nrows);
     const int ob = s_own[start];
-    int end = start + 1, maxpos = s_pos[start];
-    while (end < nrows && s_own[end] == ob) maxpos = max(maxpos, s_pos[end++]);
     if (ob >= 0) {
+      int maxpos = s_pos[end - 1];
+      if (!rising)
+        for (int t = start; t < end; ++t) maxpos = max(maxpos, s_pos[t]);
       // a lane joins only the run that holds its row: two runs may share a
       // block when rows without keys sit between them
       const bool mine = valid && rl >= start && rl < end;
@@ -652,7 +700,7 @@ __device__ __forceinline__ void diag_item(Lds<D>& s, int* s_own, int* s_pos,
       int wmax = qpos;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) wmax = max(wmax, __shfl_xor(wmax, off, kWave));
-      const int own_start = w.bt.blocks[ob].x;
+      const int own_start = s_ostart[start];
       run_keys<D, true>(s, a.k, a.v, g, own_start, maxpos - own_start + 1, wmax >= own_start,
                         qf, a.scale_log2, st, qpos, wmax);
     }
@@ -672,6 +720,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_bm_attn(AttnKernelArgs a, BmWs 
   __shared__ Lds<D> s;
   __shared__ int s_own[kTM];
   __shared__ int s_pos[kTM];
+  __shared__ int s_ostart[kTM];
+  __shared__ uint64_t s_mask[4];
   __shared__ int s_item;
   const int n_lt = w.totals[0];
   const int G = a.q.h / a.k.h;
@@ -688,8 +738,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_bm_attn(AttnKernelArgs a, BmWs 
     if (q < ln)
       list_item<D>(s, a, w, n_blocks, lb + q);
     else
-      diag_item<D>(s, s_own, s_pos, a, w, db + q - ln);
-    __syncthreads();  // s_item, s_own and s_pos are rewritten by the next item
+      diag_item<D>(s, s_own, s_pos, s_ostart, s_mask, a, w, db + q - ln);
+    __syncthreads();  // s_item and the diagonal tile's row tables are rewritten by the next item
   }
 }
 
@@ -770,7 +820,7 @@ hipError_t launch_d(const AttnKernelArgs& a, int n_blocks, void* ws, hipStream_t
   const size_t bins = (size_t)n_lists * sizeof(int);
   const int n_hist = hist_wgs((int64_t)a.L.n_q * hq, n_lists);
   hipLaunchKernelGGL(k_bm_hist, dim3(n_hist), dim3(kHistThreads), bins, stream, a, w.bt,
-                     n_blocks, n_lists, w.hist, w.pinfo);
+                     n_blocks, n_lists, w.hist, w.pinfo, w.rowinfo);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int lists_per_wg = kHistThreads / kWave;
   hipLaunchKernelGGL(k_bm_colscan, dim3((n_lists + lists_per_wg - 1) / lists_per_wg),
