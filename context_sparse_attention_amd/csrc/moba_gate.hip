@@ -351,27 +351,64 @@ __global__ __launch_bounds__(kGateThreads) void k_moba_gate_mfma(
     }
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
-    if (lane < 16) {
-      const int n = min(kGateCols, col_hi - cb);
-      for (int c = 0; c < n; ++c) {
-        const int b = cb + c;
-        if (b < first || b >= own) continue;
-        float cs = s_sc[wave][lane][c];
-        int cbk = b;
+    // four lanes per row, lane quad q taking the columns c = q (mod 4) in
+    // increasing order: a per-lane top list, descending, ties to the earlier column
+    const int n = min(kGateCols, col_hi - cb);
+    for (int c = quad; c < n; c += 4) {
+      const int b = cb + c;
+      if (b < first || b >= own) continue;
+      float cs = s_sc[wave][rl][c];
+      int cbk = b;
 #pragma unroll
-        for (int t = 0; t < KMAX; ++t) {
-          if (t < topk && cs > best_s[t]) {
-            const float ts = best_s[t];
-            const int tb = best_b[t];
-            best_s[t] = cs;
-            best_b[t] = cbk;
-            cs = ts;
-            cbk = tb;
-          }
+      for (int t = 0; t < KMAX; ++t) {
+        if (t < topk && cs > best_s[t]) {
+          const float ts = best_s[t];
+          const int tb = best_b[t];
+          best_s[t] = cs;
+          best_b[t] = cbk;
+          cs = ts;
+          cbk = tb;
         }
       }
     }
     __builtin_amdgcn_wave_barrier();
+  }
+  // merge the four lists of each row: topk rounds, each taking the best head
+  // (larger score, then smaller block) and popping it from the lane that held it
+  {
+    float out_s[KMAX];
+    int out_b[KMAX];
+#pragma unroll
+    for (int t = 0; t < KMAX; ++t) {
+      float ws = best_s[0];
+      int wb = best_b[0];
+#pragma unroll
+      for (int off = 16; off <= 32; off <<= 1) {
+        const float os = __shfl_xor(ws, off, kWave);
+        const int ob = __shfl_xor(wb, off, kWave);
+        if (os > ws || (os == ws && ob < wb)) {
+          ws = os;
+          wb = ob;
+        }
+      }
+      out_s[t] = ws;
+      out_b[t] = wb;
+      if (best_b[0] == wb && wb != INT32_MAX) {
+#pragma unroll
+        for (int u = 0; u + 1 < KMAX; ++u) {
+          best_s[u] = best_s[u + 1];
+          best_b[u] = best_b[u + 1];
+        }
+        best_s[KMAX - 1] = -INFINITY;
+        best_b[KMAX - 1] = INT32_MAX;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < KMAX; ++t) {
+      const bool keep = t < topk;
+      best_s[t] = keep ? out_s[t] : -INFINITY;
+      best_b[t] = keep ? out_b[t] : INT32_MAX;
+    }
   }
   if (lane >= 16 || row >= L.n_q) return;
   const int width = topk + 1;
