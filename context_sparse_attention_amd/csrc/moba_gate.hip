@@ -270,26 +270,31 @@ __global__ __launch_bounds__(kGateThreads) void k_moba_gate(View q, DevLayout L,
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
-constexpr int kGateCols = 64;  // block columns scored per pass
+constexpr int kGateCols = 64;  // score cells per row and pass: 64 / RG block columns
 
-// bf16 gate on the matrix cores.  One wave scores 16 consecutive rows of one
+// bf16 gate on the matrix cores.  One wave scores 16 RG consecutive rows of one
 // query head against 16-block column tiles with 16x16x32 bf16 MFMA: the A
 // operand is the rows' queries, the B operand the block means split into a
 // bf16 high and low part (two products per step, so the score keeps the fp32
-// mean to ~2^-17 relative).  The 16 x 64 score chunk goes through LDS and lanes
-// 0..15 each keep the register top-k of their row over its own candidates
-// (blocks of its sequence before its own block), in ascending block order so
-// that ties keep the lower block.
-template <int D, int KMAX>
+// mean to ~2^-17 relative); each B fragment serves the RG row groups.  The
+// score chunk goes through LDS; 4 / RG lanes per row each keep a register top
+// list over the row's own candidates (blocks of its sequence before its own
+// block) in a residue class of the columns, in ascending block order so that
+// ties keep the lower block, and the lists are merged by shuffles.
+template <int D, int KMAX, int RG>
 __global__ __launch_bounds__(kGateThreads) void k_moba_gate_mfma(
     View q, DevLayout L, int hkv, int block_size, int topk, int n_blocks, BlockTable bt,
     const __bf16* __restrict__ mu_hi, const __bf16* __restrict__ mu_lo,
     int32_t* __restrict__ idx, float* __restrict__ score) {
-  __shared__ float s_sc[kGateThreads / kWave][16][kGateCols + 1];
+  static_assert(RG == 1 || RG == 2 || RG == 4, "row groups per wave");
+  constexpr int RW = 16 * RG;          // rows per wave
+  constexpr int PW = kGateCols / RG;   // block columns per pass
+  constexpr int LPR = 4 / RG;          // selection lanes per row
+  __shared__ float s_sc[kGateThreads / kWave][RW][PW + 1];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int hq = q.h;
-  const int n_rg = (L.n_q + 15) / 16;
+  const int n_rg = (L.n_q + RW - 1) / RW;
   const int wg = blockIdx.x * (kGateThreads / kWave) + wave;
   if (wg >= n_rg * hq) return;  // whole wave
   const int h = wg % hq;
@@ -297,7 +302,10 @@ __global__ __launch_bounds__(kGateThreads) void k_moba_gate_mfma(
   const int g = h / (hq / hkv);
   const int rl = lane & 15;
   const int quad = lane >> 4;
-  const int row = rg * 16 + rl;
+  // selection: lane -> row sr of the wave, residue part of the columns
+  const int sr = lane & (RW - 1);
+  const int part = lane / RW;
+  const int row = rg * RW + sr;
 
   int first = 0, own = -1;
   if (row < L.n_q) {
@@ -315,11 +323,15 @@ __global__ __launch_bounds__(kGateThreads) void k_moba_gate_mfma(
     col_hi = max(col_hi, __shfl_xor(col_hi, off, kWave));
   }
 
-  bf16x8 a[D / 32];
-  const __bf16* qp = elem_ptr<__bf16>(q, row < L.n_q ? row : 0, h);
+  bf16x8 a[RG][D / 32];
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
-    a[ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks + 8 * quad);
+  for (int gi = 0; gi < RG; ++gi) {
+    const int qr = rg * RW + gi * 16 + rl;
+    const __bf16* qp = elem_ptr<__bf16>(q, qr < L.n_q ? qr : 0, h);
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      a[gi][ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks + 8 * quad);
+  }
 
   float best_s[KMAX];
   int best_b[KMAX];
@@ -329,35 +341,42 @@ __global__ __launch_bounds__(kGateThreads) void k_moba_gate_mfma(
     best_b[t] = INT32_MAX;
   }
   const int hd = hkv * D;
-  for (int cb = col_lo; cb < col_hi; cb += kGateCols) {
+  for (int cb = col_lo; cb < col_hi; cb += PW) {
 #pragma unroll
-    for (int t = 0; t < kGateCols / 16; ++t) {
+    for (int t = 0; t < PW / 16; ++t) {
       const int c0 = cb + 16 * t;
       if (c0 >= col_hi) break;  // uniform across the wave
       const int blk = min(c0 + rl, n_blocks - 1);
       const __bf16* ph = mu_hi + (size_t)blk * hd + (size_t)g * D + 8 * quad;
       const __bf16* pl = mu_lo + (size_t)blk * hd + (size_t)g * D + 8 * quad;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc[RG];
+#pragma unroll
+      for (int gi = 0; gi < RG; ++gi) acc[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
         const bf16x8 bh = *reinterpret_cast<const bf16x8*>(ph + 32 * ks);
         const bf16x8 bl = *reinterpret_cast<const bf16x8*>(pl + 32 * ks);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bl, acc, 0, 0, 0);
-      }
-      // lane holds block c0 + rl for rows 4*quad .. 4*quad + 3
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s_sc[wave][4 * quad + j][16 * t + rl] = acc[j];
+        for (int gi = 0; gi < RG; ++gi) {
+          acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[gi][ks], bh, acc[gi], 0, 0, 0);
+          acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[gi][ks], bl, acc[gi], 0, 0, 0);
+        }
+      }
+      // lane holds block c0 + rl for rows 16 gi + 4 quad .. 16 gi + 4 quad + 3
+#pragma unroll
+      for (int gi = 0; gi < RG; ++gi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s_sc[wave][16 * gi + 4 * quad + j][16 * t + rl] = acc[gi][j];
     }
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
-    // four lanes per row, lane quad q taking the columns c = q (mod 4) in
-    // increasing order: a per-lane top list, descending, ties to the earlier column
-    const int n = min(kGateCols, col_hi - cb);
-    for (int c = quad; c < n; c += 4) {
+    // lane part p takes the columns c = p (mod LPR) in increasing order: a
+    // per-lane top list, descending, ties to the earlier column
+    const int n = min(PW, col_hi - cb);
+    for (int c = part; c < n; c += LPR) {
       const int b = cb + c;
       if (b < first || b >= own) continue;
-      float cs = s_sc[wave][rl][c];
+      float cs = s_sc[wave][sr][c];
       int cbk = b;
 #pragma unroll
       for (int t = 0; t < KMAX; ++t) {
@@ -373,9 +392,9 @@ __global__ __launch_bounds__(kGateThreads) void k_moba_gate_mfma(
     }
     __builtin_amdgcn_wave_barrier();
   }
-  // merge the four lists of each row: topk rounds, each taking the best head
-  // (larger score, then smaller block) and popping it from the lane that held it
-  {
+  if (LPR > 1) {
+    // merge the lists of each row: topk rounds, each taking the best head
+    // (larger score, then smaller block) and popping it from the lane that held it
     float out_s[KMAX];
     int out_b[KMAX];
 #pragma unroll
@@ -383,7 +402,7 @@ __global__ __launch_bounds__(kGateThreads) void k_moba_gate_mfma(
       float ws = best_s[0];
       int wb = best_b[0];
 #pragma unroll
-      for (int off = 16; off <= 32; off <<= 1) {
+      for (int off = RW; off < kWave; off <<= 1) {
         const float os = __shfl_xor(ws, off, kWave);
         const int ob = __shfl_xor(wb, off, kWave);
         if (os > ws || (os == ws && ob < wb)) {
@@ -410,7 +429,7 @@ __global__ __launch_bounds__(kGateThreads) void k_moba_gate_mfma(
       best_b[t] = keep ? out_b[t] : INT32_MAX;
     }
   }
-  if (lane >= 16 || row >= L.n_q) return;
+  if (part != 0 || row >= L.n_q) return;
   const int width = topk + 1;
   int32_t* out = idx + ((int64_t)row * hq + h) * width;
   float* out_s = score ? score + ((int64_t)row * hq + h) * width : nullptr;
@@ -439,16 +458,25 @@ __global__ __launch_bounds__(kGateThreads) void k_moba_gate_mfma(
     if (out_s) out_s[t] = -INFINITY;
   }
 }
+// Waves of 64 rows once there are enough of them to fill the chip: each block
+// mean fragment then serves four MFMAs.
+constexpr int64_t kGateWideWaves = 16384;
 
-template <int D, int KMAX>
-hipError_t launch_gate_mfma(const MobaGateArgs& a, const MobaWs& w, hipStream_t stream) {
-  const int64_t waves = (int64_t)((a.L.n_q + 15) / 16) * a.q.h;
+template <int D, int KMAX, int RG>
+hipError_t launch_gate_rg(const MobaGateArgs& a, const MobaWs& w, hipStream_t stream) {
+  const int64_t waves = (int64_t)((a.L.n_q + 16 * RG - 1) / (16 * RG)) * a.q.h;
   const int per_wg = kGateThreads / kWave;
   const int grid = (int)((waves + per_wg - 1) / per_wg);
-  hipLaunchKernelGGL((k_moba_gate_mfma<D, KMAX>), dim3(grid), dim3(kGateThreads), 0, stream,
+  hipLaunchKernelGGL((k_moba_gate_mfma<D, KMAX, RG>), dim3(grid), dim3(kGateThreads), 0, stream,
                      a.q, a.L, a.k.h, a.block_size, a.topk, a.n_blocks, w.bt, w.mu_hi,
                      w.mu_lo, a.idx, a.score);
   return hipGetLastError();
+}
+template <int D, int KMAX>
+hipError_t launch_gate_mfma(const MobaGateArgs& a, const MobaWs& w, hipStream_t stream) {
+  if ((int64_t)((a.L.n_q + 15) / 16) * a.q.h >= kGateWideWaves)
+    return launch_gate_rg<D, KMAX, 4>(a, w, stream);
+  return launch_gate_rg<D, KMAX, 1>(a, w, stream);
 }
 
 template <int D>
