@@ -14,10 +14,14 @@
 //   k_dsa_logits - other cases: one workgroup per (row, 256-key tile): the row's indexer
 //                  queries sit in LDS, each thread holds one key in registers
 //                  and reduces the 64 heads in fp32;
-//   k_dsa_select - one workgroup per row, row cached in LDS: 4-pass 8-bit radix
-//                  select of the k-th largest logit on order-preserving uint32
-//                  keys, then an index-order compaction that takes every larger
-//                  logit and the lowest-index equal ones (ties to the lower index).
+//   k_dsa_select_reg - one workgroup per row of up to kRgCap permitted keys, the
+//                  row in registers: a value-range histogram finds the bin of the
+//                  k-th largest logit, an exact (value, lower index first) order
+//                  resolves that bin, and an index-order compaction writes the
+//                  selection (ties to the lower index);
+//   k_dsa_select - longer rows: one workgroup per row, row cached in LDS when it
+//                  fits: 4-pass 8-bit radix select of the k-th largest logit on
+//                  order-preserving uint32 keys, then the same compaction.
 #include "common.hpp"
 #include "gather.hpp"
 
@@ -219,6 +223,30 @@ constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kSelCache = 12288;  // row keys cached in LDS (48 KiB)
 constexpr int kSelPer = 8;        // elements per thread in the compaction
 
+// Exclusive prefix sum of one int per thread across a workgroup of NW waves,
+// plus the total.
+template <int NW>
+__device__ inline int sel_excl_scan_n(int x, int* s_wave, int* total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) s_wave[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    if (w < wave) before += s_wave[w];
+    all += s_wave[w];
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - x;
+}
+
 // Exclusive prefix sum of one int per thread across the workgroup, plus the total.
 __device__ inline int sel_excl_scan(int x, int* s_wave, int* total) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
@@ -248,7 +276,8 @@ __device__ inline int sel_excl_scan(int x, int* s_wave, int* total) {
 __global__ __launch_bounds__(kSelThreads) void k_dsa_select(DevLayout L, int topk,
                                                             const float* __restrict__ logits,
                                                             int32_t* __restrict__ idx,
-                                                            float* __restrict__ score) {
+                                                            float* __restrict__ score,
+                                                            int min_n) {
   __shared__ uint32_t s_key[kSelCache];
   __shared__ int s_hist[256];
   __shared__ int s_wave[kSelWaves];
@@ -258,6 +287,7 @@ __global__ __launch_bounds__(kSelThreads) void k_dsa_select(DevLayout L, int top
   const int lane = threadIdx.x & (kWave - 1);
   const RowKeys r = row_keys(L, i);
   const int n = r.valid ? r.hi - r.lo + 1 : 0;
+  if (n <= min_n) return;  // rows the register-resident select has taken
   const float* row = logits + (int64_t)i * L.n_kv + r.lo;
   int32_t* out = idx + (int64_t)i * topk;
   float* out_s = score ? score + (int64_t)i * topk : nullptr;
@@ -395,6 +425,394 @@ __global__ __launch_bounds__(kSelThreads) void k_dsa_select(DevLayout L, int top
   }
 }
 
+// ---- register-resident select ----------------------------------------------
+//
+// One workgroup per row, the row held in registers (float4 groups, coalesced).
+// 1. min / max of the row and a monotone map of value to one of kRgBins bins,
+//    bin(x) = min(trunc(max(fma(x, s, o), -1)), kRgBins - 1), s = kRgBins / (max - min):
+//    a higher bin holds strictly larger values, equal values share a bin.
+// 2. LDS histogram; the bin T holding the k-th largest value, the count of
+//    values in higher bins, and T's value interval [xa, xb] (found by binary
+//    search over the float order, evaluating the same bin function).
+// 3. One pass counts, per (group, wave), the values above xb and collects the
+//    values inside [xa, xb] as composite keys (value key, then lower index
+//    first).  The (k - above)-th largest composite (v*, i*) is found by pairwise
+//    ranking, or by an 8-bit radix select re-reading the row when T holds more
+//    than kRgCand values (mass ties, e.g. a constant row).
+// 4. The selection is {e : x_e > v* or (x_e == v* and e <= i*)} (just x_e >= v*
+//    when no value equal to v* is left out); it is written in index order, each
+//    lane's offset taken from wave ballots.
+// Non-finite logits are never selected (a row with fewer than k finite logits
+// is padded with -1).
+constexpr int kRgThreads = 512;
+constexpr int kRgWaves = kRgThreads / kWave;
+constexpr int kRgPer4 = 9;                                     // float4 groups per thread
+constexpr int kRgCap = kRgThreads * 4 * kRgPer4 - 3;           // longest row (any alignment)
+constexpr int kRgBins = 2048;
+constexpr int kRgCand = 1024;
+constexpr int kRgSlots = kRgWaves * kRgPer4;                   // (group j, wave) counters
+
+__device__ __forceinline__ int rg_bin(float x, float s, float o) {
+  const float t = fmaxf(fmaf(x, s, o), -1.0f);  // NaN -> -1
+  return min((int)t, kRgBins - 1);
+}
+
+// order key of a float, -0 below +0 (an order on the non-NaN floats)
+__device__ __forceinline__ uint32_t rg_raw_key(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float rg_key_float(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Smallest order key k in [lo, hi] with rg_bin(float(k)) >= target, for two
+// targets at once (independent chains); hi is returned when none below it is.
+__device__ inline void rg_edges(int t0, int t1, float s, float o, uint32_t lo0, uint32_t hi0,
+                                uint32_t lo1, uint32_t hi1, uint32_t* k0, uint32_t* k1) {
+  while (lo0 < hi0 || lo1 < hi1) {
+    const uint32_t m0 = lo0 + ((hi0 - lo0) >> 1), m1 = lo1 + ((hi1 - lo1) >> 1);
+    if (lo0 < hi0) {
+      if (rg_bin(rg_key_float(m0), s, o) >= t0) hi0 = m0; else lo0 = m0 + 1;
+    }
+    if (lo1 < hi1) {
+      if (rg_bin(rg_key_float(m1), s, o) >= t1) hi1 = m1; else lo1 = m1 + 1;
+    }
+  }
+  *k0 = lo0;
+  *k1 = lo1;
+}
+
+__device__ inline uint64_t rg_composite(float x, int e) {
+  return ((uint64_t)float_key(x) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+}
+
+__global__ __launch_bounds__(kRgThreads) void k_dsa_select_reg(DevLayout L, int topk,
+                                                               const float* __restrict__ logits,
+                                                               int32_t* __restrict__ idx,
+                                                               float* __restrict__ score) {
+  __shared__ int s_hist[kRgBins + 1];  // entry 0 counts nothing (bin -1 lands there)
+  __shared__ uint64_t s_cand[kRgCand];
+  __shared__ float s_red[2][kRgWaves];
+  __shared__ int s_wave[kRgWaves];
+  __shared__ int s_cnt[kRgSlots];    // selected per (j, wave), index j * kRgWaves + wave
+  __shared__ int s_base[kRgSlots];   // exclusive prefix of s_cnt in index order
+  __shared__ int s_bin, s_above, s_ncand, s_rem, s_straddle;
+  __shared__ float s_xa, s_xb;
+  __shared__ uint64_t s_cstar, s_prefix;
+
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const RowKeys r = row_keys(L, i);
+  const int n = r.valid ? r.hi - r.lo + 1 : 0;
+  if (n > kRgCap) return;  // longer rows go to k_dsa_select
+  const int64_t g0 = (int64_t)i * L.n_kv + r.lo;
+  int32_t* out = idx + (int64_t)i * topk;
+  float* out_s = score ? score + (int64_t)i * topk : nullptr;
+  if (n <= topk) {
+    for (int t = tid; t < topk; t += kRgThreads) {
+      out[t] = t < n ? r.lo + t : -1;
+      if (out_s) out_s[t] = t < n ? logits[g0 + t] : -INFINITY;
+    }
+    return;
+  }
+
+  // element e of the row is aligned position e + sh of the float4 groups from
+  // g0 - sh; group q = tid + kRgThreads * j of this thread holds positions 4q .. 4q+3
+  const int sh = (int)(g0 & 3);
+  const float4* base4 = reinterpret_cast<const float4*>(logits + (g0 - sh));
+  const int n4 = (n + sh + 3) >> 2;
+  const int e0 = 4 * tid - sh;  // element of (j, c) = e0 + 4 * kRgThreads * j + c
+  float x[kRgPer4][4];
+#pragma unroll
+  for (int j = 0; j < kRgPer4; ++j) {
+    const int q = tid + kRgThreads * j;
+    float4 v = make_float4(NAN, NAN, NAN, NAN);
+    if (q < n4) v = base4[q];
+    x[j][0] = v.x; x[j][1] = v.y; x[j][2] = v.z; x[j][3] = v.w;
+  }
+  // positions outside the row (only in the first and the last group) become NaN
+  {
+    const int jl = (n + sh - 1) / 4 / kRgThreads;  // j of the group holding the last element
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (e0 + c < 0) x[0][c] = NAN;
+#pragma unroll
+      for (int j = 0; j < kRgPer4; ++j)
+        if (j == jl && e0 + 4 * kRgThreads * j + c >= n) x[j][c] = NAN;
+    }
+  }
+
+  float mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+  for (int j = 0; j < kRgPer4; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      mx = fmaxf(mx, x[j][c]);
+      mn = fminf(mn, x[j][c]);
+    }
+  mx = wave_max(mx);
+  mn = -wave_max(-mn);
+  if (__builtin_expect(mx == INFINITY || mn == -INFINITY, 0)) {
+    // infinite logits are never selected either: make them NaN (rare, per wave)
+    mx = -INFINITY;
+    mn = INFINITY;
+#pragma unroll
+    for (int j = 0; j < kRgPer4; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (fabsf(x[j][c]) == INFINITY) x[j][c] = NAN;
+        mx = fmaxf(mx, x[j][c]);
+        mn = fminf(mn, x[j][c]);
+      }
+    mx = wave_max(mx);
+    mn = -wave_max(-mn);
+  }
+  for (int b = tid; b <= kRgBins; b += kRgThreads) s_hist[b] = 0;
+  if (tid < kRgSlots) s_cnt[tid] = 0;
+  if (lane == 0) {
+    s_red[0][wave] = mx;
+    s_red[1][wave] = mn;
+  }
+  if (tid == 0) {  // defaults that only non-finite logits leave in place
+    s_ncand = 0;
+    s_cstar = 0;
+    s_prefix = 0;
+    s_rem = 1;
+    s_bin = -1;
+    s_above = 0;
+    s_straddle = 1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kRgWaves; ++w) {
+    mx = fmaxf(mx, s_red[0][w]);
+    mn = fminf(mn, s_red[1][w]);
+  }
+  const float range = mx - mn;
+  const bool spread = range > 0.f && range <= 3.0e38f;
+  const float bs = spread ? (float)kRgBins / range : 0.f;
+  const float bo = spread ? -mn * bs : 0.f;
+
+  // groups j with kRgThreads * j >= n4 hold no element of the row in any thread
+  const int jn = (n4 + kRgThreads - 1) / kRgThreads;
+#pragma unroll
+  for (int j = 0; j < kRgPer4; ++j)
+    if (j < jn) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) atomicAdd(&s_hist[rg_bin(x[j][c], bs, bo) + 1], 1);
+    }
+  __syncthreads();
+
+  // threshold bin: thread t owns bins kRgBins-1-4t .. kRgBins-4-4t (from the top);
+  // the thread whose bins hold the k-th largest also finds T's value interval
+  {
+    int cnt[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      cnt[j] = s_hist[kRgBins - 4 * tid - j];
+      sum += cnt[j];
+    }
+    int total;
+    int above = sel_excl_scan_n<kRgWaves>(sum, s_wave, &total);
+    if (above < topk && above + sum >= topk) {
+      int T = 0, ab = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (above < topk && above + cnt[j] >= topk) {
+          T = kRgBins - 1 - 4 * tid - j;
+          ab = above;
+        }
+        above += cnt[j];
+      }
+      // search brackets: a few bins around mn + T / s, checked, else the whole order
+      constexpr uint32_t kMinKey = 0x007fffffu, kMaxKey = 0xff800000u;  // -inf, +inf
+      uint32_t lo0 = kMinKey, hi0 = kMaxKey, lo1 = kMinKey, hi1 = kMaxKey;
+      if (spread) {
+        const uint32_t kl = rg_raw_key(mn + (float)(T - 2) / bs);
+        const uint32_t kh = rg_raw_key(mn + (float)(T + 3) / bs);
+        if (kl > kMinKey && kl < kh && kh < kMaxKey &&
+            rg_bin(rg_key_float(kl), bs, bo) < T && rg_bin(rg_key_float(kh), bs, bo) > T + 1) {
+          lo0 = lo1 = kl;
+          hi0 = hi1 = kh;
+        }
+      }
+      uint32_t ka, k1;
+      rg_edges(T, T + 1, bs, bo, lo0, hi0, lo1, hi1, &ka, &k1);
+      // bin T is [first float of bin T, the float just below the first of bin T+1]
+      s_bin = T;
+      s_above = ab;
+      s_xa = rg_key_float(ka);
+      s_xb = T + 1 < kRgBins ? rg_key_float(k1 - 1) : INFINITY;
+    }
+  }
+  __syncthreads();
+  const int T = s_bin;  // -1: fewer than k finite logits, all of them are taken
+  const int rem = topk - s_above;
+  const int nT = T >= 0 ? s_hist[T + 1] : 0;
+  const float xa = T >= 0 ? s_xa : -INFINITY;
+  const float xb = T >= 0 ? s_xb : -INFINITY;
+
+  // counts above xb per (j, wave); values of [xa, xb] become candidates
+#pragma unroll
+  for (int j = 0; j < kRgPer4; ++j) {
+    if (j < jn) {
+      int above = 0;
+      bool any = false;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bool gt = x[j][c] > xb;
+        above += __popcll(__ballot(gt));
+        any |= !gt && x[j][c] >= xa;
+      }
+      if (lane == 0) s_cnt[j * kRgWaves + wave] += above;
+      if (nT <= kRgCand && __ballot(any)) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (!(x[j][c] > xb) && x[j][c] >= xa) {
+            const int slot = atomicAdd(&s_ncand, 1);
+            if (slot < kRgCand) s_cand[slot] = rg_composite(x[j][c], e0 + 4 * kRgThreads * j + c);
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // (j, wave) slot of element e: q = (e + sh) / 4 = tid' + kRgThreads * j
+  auto slot_of = [&](int e) {
+    const int q = (e + sh) >> 2;
+    return (q / kRgThreads) * kRgWaves + (q % kRgThreads) / kWave;
+  };
+  if (T >= 0 && nT <= kRgCand) {
+    for (int a = tid; a < nT; a += kRgThreads) {
+      const uint64_t ca = s_cand[a];
+      int rank = 0, tie_below = 0;
+      for (int b = 0; b < nT; ++b) {
+        const uint64_t cb = s_cand[b];
+        rank += cb > ca;
+        tie_below += (cb >> 32) == (ca >> 32) && cb < ca;
+      }
+      if (rank < rem) atomicAdd(&s_cnt[slot_of((int)(0xffffffffu - (uint32_t)ca))], 1);
+      if (rank == rem - 1) {
+        s_cstar = ca;
+        s_straddle = tie_below > 0;  // an equal value with a higher index is left out
+      }
+    }
+    __syncthreads();
+  } else if (T >= 0) {
+    // mass ties in bin T: radix select of the rem-th largest composite, 8 bits a
+    // pass, re-reading the row from memory each pass
+    const float* row = logits + g0;
+    uint64_t prefix = 0, mask = 0;
+    int remaining = rem;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      for (int b = tid; b < 256; b += kRgThreads) s_hist[b] = 0;
+      __syncthreads();
+      for (int e = tid; e < n; e += kRgThreads) {
+        const float v = row[e];
+        if (v >= xa && !(v > xb)) {
+          const uint64_t u = rg_composite(v, e);
+          if ((u & mask) == prefix) atomicAdd(&s_hist[(int)((u >> shift) & 255u)], 1);
+        }
+      }
+      __syncthreads();
+      if (tid < kWave) {
+        int cnt[4], sum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          cnt[j] = s_hist[255 - 4 * lane - j];
+          sum += cnt[j];
+        }
+        int incl = sum;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+          const int y = __shfl_up(incl, off, kWave);
+          if (lane >= off) incl += y;
+        }
+        int above = incl - sum;
+        if (above < remaining && above + sum >= remaining) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (above < remaining && above + cnt[j] >= remaining) {
+              s_prefix = prefix | ((uint64_t)(255 - 4 * lane - j) << shift);
+              s_rem = remaining - above;
+            }
+            above += cnt[j];
+          }
+        }
+      }
+      __syncthreads();
+      prefix = s_prefix;
+      remaining = s_rem;
+      mask |= (uint64_t)255u << shift;
+      __syncthreads();
+    }
+    if (tid == 0) s_cstar = prefix;  // s_straddle stays 1: the exact predicate
+    for (int e = tid; e < n; e += kRgThreads) {
+      const float v = row[e];
+      if (v >= xa && !(v > xb) && rg_composite(v, e) >= prefix) atomicAdd(&s_cnt[slot_of(e)], 1);
+    }
+    __syncthreads();
+  }
+  // exclusive prefix of the counts in index order (j, then wave)
+  if (tid < kWave) {
+    const int a0 = 2 * lane < kRgSlots ? s_cnt[2 * lane] : 0;
+    const int a1 = 2 * lane + 1 < kRgSlots ? s_cnt[2 * lane + 1] : 0;
+    int incl = a0 + a1;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += y;
+    }
+    if (2 * lane < kRgSlots) s_base[2 * lane] = incl - a0 - a1;
+    if (2 * lane + 1 < kRgSlots) s_base[2 * lane + 1] = incl - a1;
+    if (lane == kWave - 1) s_wave[0] = incl;
+  }
+  __syncthreads();
+  const uint64_t cstar = s_cstar;
+  const float vstar = T >= 0 ? rg_key_float((uint32_t)(cstar >> 32)) : -INFINITY;
+  const int istar = T >= 0 ? (int)(0xffffffffu - (uint32_t)cstar) : -1;
+  const int total = s_wave[0];
+
+  auto place = [&](auto sel_of) {
+#pragma unroll
+    for (int j = 0; j < kRgPer4; ++j) {
+      if (j < jn) {
+        const int ej = e0 + 4 * kRgThreads * j;
+        bool sel[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sel[c] = sel_of(x[j][c], ej + c);
+        int slot = s_base[j * kRgWaves + wave];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint64_t m = __ballot(sel[c]);
+          slot = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)slot));
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (sel[c] && slot < topk) {
+            out[slot] = r.lo + ej + c;
+            if (out_s) out_s[slot] = x[j][c];
+          }
+          slot += sel[c];
+        }
+      }
+    }
+  };
+  if (T >= 0 && !s_straddle) {
+    place([&](float v, int) { return v >= vstar; });
+  } else {
+    place([&](float v, int e) { return v > vstar || (v == vstar && e <= istar); });
+  }
+  for (int t = total + tid; t < topk; t += kRgThreads) {
+    out[t] = -1;
+    if (out_s) out_s[t] = -INFINITY;
+  }
+}
+
 template <typename T>
 hipError_t launch_typed(const DsaArgs& a, hipStream_t stream) {
   float* logits = static_cast<float*>(a.ws);
@@ -429,8 +847,13 @@ hipError_t launch_typed(const DsaArgs& a, hipStream_t stream) {
     }
   }
   trace_end(stream, slot);
-  hipLaunchKernelGGL(k_dsa_select, dim3(a.L.n_q), dim3(kSelThreads), 0, stream, a.L,
+  hipLaunchKernelGGL(k_dsa_select_reg, dim3(a.L.n_q), dim3(kRgThreads), 0, stream, a.L,
                      a.topk, logits, a.idx, a.score);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.L.n_kv <= kRgCap) return e;
+  // rows longer than the register capacity
+  hipLaunchKernelGGL(k_dsa_select, dim3(a.L.n_q), dim3(kSelThreads), 0, stream, a.L,
+                     a.topk, logits, a.idx, a.score, kRgCap);
   return hipGetLastError();
 }
 

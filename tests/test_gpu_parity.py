@@ -217,6 +217,59 @@ def test_ties_all_zero_keys_pick_lowest():
         assert [x for x in idx[i] if x >= 0] == list(range(min(n, wt.topk)))
 
 
+# Crafted indexer inputs whose logits are exact: head 0 has weight 1 and query
+# e_0, every other head weight 0 and query 0, and key j is (v_j, 0, ..., 0) with
+# v_j >= 0 a bf16 value, so logit(i, j) = v_j in any precision.  The selection
+# is then unique (ties to the lower index) and must match the oracle bit for bit.
+SELECT_CASES = {
+    # many equal bf16 values around the k-th: resolved by the per-bin ranking
+    "bf16_ties": dict(lengths=(6000,), topk=1000, values="bf16"),
+    # four distinct values, thousands of ties in the threshold bin: radix resolution
+    "four_values": dict(lengths=(5000,), topk=700, values="four"),
+    # a constant row: everything ties, the lowest indices win
+    "constant": dict(lengths=(3000,), topk=300, values="constant"),
+    # rows longer than the register-resident capacity take the long-row kernel
+    "long_rows": dict(lengths=(18000,), topk=2048, values="bf16"),
+}
+
+
+@pytest.mark.parametrize("case", list(SELECT_CASES))
+def test_token_select_crafted_logits(case):
+    c = SELECT_CASES[case]
+    n_kv = sum(c["lengths"])
+    rng = np.random.default_rng(31)
+    pos = np.unique(np.concatenate([rng.integers(0, n_kv, 40), [0, 1, c["topk"] - 1,
+                                    c["topk"], c["topk"] + 1, n_kv - 1]])).astype(np.int32)
+    w = tiny_token_workload(seed=31, lengths=c["lengths"], positions=pos, hq=4, dqk=64, dv=64,
+                            hi=32, di=64, topk=c["topk"], dtype="bf16")
+    if c["values"] == "bf16":
+        v = torch.from_numpy(rng.uniform(0, 100, n_kv).astype(np.float32)).bfloat16().float()
+        v = v.numpy()
+    elif c["values"] == "four":
+        v = rng.integers(0, 4, n_kv).astype(np.float32)
+    else:
+        v = np.full(n_kv, 5.0, np.float32)
+    w.iq = np.zeros_like(w.iq)
+    w.iq[:, 0, 0] = 1.0
+    w.ik = np.zeros_like(w.ik)
+    w.ik[:, 0] = v
+    w.w = np.zeros_like(w.w)
+    w.w[:, 0] = 1.0
+    _say("crafted select", case, "n_kv", n_kv, "rows", len(pos), "topk", w.topk)
+    d = upload(w)
+    idx, score = csa.dsa_indexer_topk(d["iq"], d["ik"], d["w"], d["layout"], w.topk,
+                                      return_score=True)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    score = score.cpu().numpy()
+    ref, _, _ = oracle.indexer_topk(w.iq, w.ik, w.w, w.q_pos, w.q_seq, w.cu_seqlens, w.topk)
+    bad = [i for i in range(len(pos)) if not np.array_equal(idx[i], ref[i])]
+    assert not bad, f"rows {bad[:5]} differ, e.g. row {bad[0]} at pos {pos[bad[0]]}"
+    sel = idx >= 0
+    assert np.array_equal(score[sel], v[idx[sel]])
+    assert np.isneginf(score[~sel]).all()
+
+
 def test_determinism_bitwise():
     w = tiny_block_workload(seed=13, layout="all", lengths=(1000, 537), hq=8, hkv=2, d=128,
                             block=64, topk=3, dtype="bf16")
