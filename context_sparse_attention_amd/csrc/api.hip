@@ -3,6 +3,7 @@
 // Every entry point validates all arguments before enqueueing anything; a
 // failure returns a status and leaves its text in csa_last_error().  No C++
 // exception leaves this file.
+#include <algorithm>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -201,6 +202,18 @@ csa_status dsa_indexer_topk(const csa_tensor3* iq, const csa_tensor3* ik, const 
     a.L = make_dev_layout(L);
     a.topk = topk;
     a.dtype = iq->dtype;
+    // a row's keys lie in one sequence; their float4 misalignment in the logits is
+    // zero when n_kv and every sequence start are multiples of 4
+    {
+      const int32_t* cu = L->cu_seqlens_host;
+      int longest = 0;
+      bool aligned = L->n_kv % 4 == 0;
+      for (int s = 0; s < L->n_seq; ++s) {
+        longest = std::max(longest, cu[s + 1] - cu[s]);
+        aligned = aligned && cu[s] % 4 == 0;
+      }
+      a.max_span = longest + (aligned ? 0 : 3);
+    }
     a.idx = idx;
     a.score = score;
     a.ws = ws;

@@ -794,18 +794,6 @@ __global__ __launch_bounds__(kHistThreads) void k_bm_merge(AttnKernelArgs a, BmW
   if (a.lse && c8 == 0) a.lse[pair] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
 }
 
-int device_cus() {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-  }
-  return cus;
-}
-
 template <int D>
 hipError_t launch_d(const AttnKernelArgs& a, int n_blocks, void* ws, hipStream_t stream) {
   BmWs w;

@@ -127,6 +127,8 @@ struct Carver {
   }
 };
 
+int device_cus();  // compute units of the current device (attn_block_mfma.hip)
+
 // ---- tracing (trace.hip) ----------------------------------------------------
 void trace_begin(hipStream_t stream, const char* kernel, int* slot);
 void trace_end(hipStream_t stream, int slot);
@@ -162,6 +164,7 @@ struct DsaArgs {
   int64_t w_stride;
   DevLayout L;
   int topk, dtype;
+  int max_span;  // bound on a row's permitted keys plus its float4 misalignment
   int32_t* idx;
   float* score;
   void* ws;

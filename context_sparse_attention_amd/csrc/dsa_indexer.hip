@@ -14,14 +14,16 @@
 //   k_dsa_logits - other cases: one workgroup per (row, 256-key tile): the row's indexer
 //                  queries sit in LDS, each thread holds one key in registers
 //                  and reduces the 64 heads in fp32;
-//   k_dsa_select_reg - one workgroup per row of up to kRgCap permitted keys, the
-//                  row in registers: a value-range histogram finds the bin of the
+//   k_dsa_select_reg - persistent, one row at a time per workgroup, rows of up to
+//                  kRgSpan aligned positions, the row in registers: a value-range histogram finds the bin of the
 //                  k-th largest logit, an exact (value, lower index first) order
 //                  resolves that bin, and an index-order compaction writes the
 //                  selection (ties to the lower index);
 //   k_dsa_select - longer rows: one workgroup per row, row cached in LDS when it
 //                  fits: 4-pass 8-bit radix select of the k-th largest logit on
 //                  order-preserving uint32 keys, then the same compaction.
+#include <algorithm>
+
 #include "common.hpp"
 #include "gather.hpp"
 
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(kSelThreads) void k_dsa_select(DevLayout L, int top
                                                             const float* __restrict__ logits,
                                                             int32_t* __restrict__ idx,
                                                             float* __restrict__ score,
-                                                            int min_n) {
+                                                            int span) {
   __shared__ uint32_t s_key[kSelCache];
   __shared__ int s_hist[256];
   __shared__ int s_wave[kSelWaves];
@@ -287,7 +289,8 @@ __global__ __launch_bounds__(kSelThreads) void k_dsa_select(DevLayout L, int top
   const int lane = threadIdx.x & (kWave - 1);
   const RowKeys r = row_keys(L, i);
   const int n = r.valid ? r.hi - r.lo + 1 : 0;
-  if (n <= min_n) return;  // rows the register-resident select has taken
+  // rows the register-resident select takes: short ones and those that fit its span
+  if (n <= topk || n + (int)(((int64_t)i * L.n_kv + r.lo) & 3) <= span) return;
   const float* row = logits + (int64_t)i * L.n_kv + r.lo;
   int32_t* out = idx + (int64_t)i * topk;
   float* out_s = score ? score + (int64_t)i * topk : nullptr;
@@ -431,12 +434,12 @@ __global__ __launch_bounds__(kSelThreads) void k_dsa_select(DevLayout L, int top
 // 1. min / max of the row and a monotone map of value to one of kRgBins bins,
 //    bin(x) = min(trunc(max(fma(x, s, o), -1)), kRgBins - 1), s = kRgBins / (max - min):
 //    a higher bin holds strictly larger values, equal values share a bin.
-// 2. LDS histogram; the bin T holding the k-th largest value, the count of
-//    values in higher bins, and T's value interval [xa, xb] (found by binary
-//    search over the float order, evaluating the same bin function).
-// 3. One pass counts, per (group, wave), the values above xb and collects the
-//    values inside [xa, xb] as composite keys (value key, then lower index
-//    first).  The (k - above)-th largest composite (v*, i*) is found by pairwise
+// 2. LDS histogram; the bin T holding the k-th largest value and the count of
+//    values in higher bins.
+// 3. One pass counts, per (group, wave), the values in bins above T and
+//    collects the values of bin T as composite keys (value key, then lower
+//    index first); the bin of a value is recomputed with the same instructions,
+//    so it is the one the histogram counted.  The (k - above)-th largest composite (v*, i*) is found by pairwise
 //    ranking, or by an 8-bit radix select re-reading the row when T holds more
 //    than kRgCand values (mass ties, e.g. a constant row).
 // 4. The selection is {e : x_e > v* or (x_e == v* and e <= i*)} (just x_e >= v*
@@ -446,8 +449,8 @@ __global__ __launch_bounds__(kSelThreads) void k_dsa_select(DevLayout L, int top
 // is padded with -1).
 constexpr int kRgThreads = 512;
 constexpr int kRgWaves = kRgThreads / kWave;
-constexpr int kRgPer4 = 9;                                     // float4 groups per thread
-constexpr int kRgCap = kRgThreads * 4 * kRgPer4 - 3;           // longest row (any alignment)
+constexpr int kRgPer4 = 8;                                     // float4 groups per thread
+constexpr int kRgSpan = kRgThreads * 4 * kRgPer4;              // aligned positions of a row
 constexpr int kRgBins = 2048;
 constexpr int kRgCand = 1024;
 constexpr int kRgSlots = kRgWaves * kRgPer4;                   // (group j, wave) counters
@@ -457,91 +460,80 @@ __device__ __forceinline__ int rg_bin(float x, float s, float o) {
   return min((int)t, kRgBins - 1);
 }
 
-// order key of a float, -0 below +0 (an order on the non-NaN floats)
-__device__ __forceinline__ uint32_t rg_raw_key(float x) {
-  const uint32_t b = __float_as_uint(x);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
 __device__ __forceinline__ float rg_key_float(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
-}
-
-// Smallest order key k in [lo, hi] with rg_bin(float(k)) >= target, for two
-// targets at once (independent chains); hi is returned when none below it is.
-__device__ inline void rg_edges(int t0, int t1, float s, float o, uint32_t lo0, uint32_t hi0,
-                                uint32_t lo1, uint32_t hi1, uint32_t* k0, uint32_t* k1) {
-  while (lo0 < hi0 || lo1 < hi1) {
-    const uint32_t m0 = lo0 + ((hi0 - lo0) >> 1), m1 = lo1 + ((hi1 - lo1) >> 1);
-    if (lo0 < hi0) {
-      if (rg_bin(rg_key_float(m0), s, o) >= t0) hi0 = m0; else lo0 = m0 + 1;
-    }
-    if (lo1 < hi1) {
-      if (rg_bin(rg_key_float(m1), s, o) >= t1) hi1 = m1; else lo1 = m1 + 1;
-    }
-  }
-  *k0 = lo0;
-  *k1 = lo1;
 }
 
 __device__ inline uint64_t rg_composite(float x, int e) {
   return ((uint64_t)float_key(x) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
 }
 
-__global__ __launch_bounds__(kRgThreads) void k_dsa_select_reg(DevLayout L, int topk,
-                                                               const float* __restrict__ logits,
-                                                               int32_t* __restrict__ idx,
-                                                               float* __restrict__ score) {
-  __shared__ int s_hist[kRgBins + 1];  // entry 0 counts nothing (bin -1 lands there)
-  __shared__ uint64_t s_cand[kRgCand];
+// One workgroup per row; the row is loaded from memory straight into registers.
+__global__ __launch_bounds__(kRgThreads, 6) void k_dsa_select_reg(DevLayout L, int topk,
+                                                                  const float* __restrict__ logits,
+                                                                  int32_t* __restrict__ idx,
+                                                                  float* __restrict__ score) {
+  __shared__ uint64_t s_hc[(kRgBins + 2) / 2];  // histogram, then candidates, then the output
   __shared__ float s_red[2][kRgWaves];
   __shared__ int s_wave[kRgWaves];
   __shared__ int s_cnt[kRgSlots];    // selected per (j, wave), index j * kRgWaves + wave
   __shared__ int s_base[kRgSlots];   // exclusive prefix of s_cnt in index order
   __shared__ int s_bin, s_above, s_ncand, s_rem, s_straddle;
-  __shared__ float s_xa, s_xb;
   __shared__ uint64_t s_cstar, s_prefix;
+  int* const s_hist = reinterpret_cast<int*>(s_hc);  // [kRgBins + 1], entry 0 counts nothing
+  uint64_t* const s_cand = s_hc;                      // [kRgCand], after the histogram is read
+  static_assert(kRgCand <= (kRgBins + 2) / 2, "candidates alias the histogram");
 
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const RowKeys r = row_keys(L, i);
   const int n = r.valid ? r.hi - r.lo + 1 : 0;
-  if (n > kRgCap) return;  // longer rows go to k_dsa_select
-  const int64_t g0 = (int64_t)i * L.n_kv + r.lo;
+  const int lo = r.lo;
+  const int64_t g0 = (int64_t)i * L.n_kv + lo;
+  // element e of the row is aligned position e + sh; group q = tid + kRgThreads * j
+  // of this thread holds positions 4q .. 4q+3
+  const int sh = (int)(g0 & 3);
+  if (n > topk && n + sh > kRgSpan) return;  // rows longer than the registers: k_dsa_select
   int32_t* out = idx + (int64_t)i * topk;
   float* out_s = score ? score + (int64_t)i * topk : nullptr;
   if (n <= topk) {
     for (int t = tid; t < topk; t += kRgThreads) {
-      out[t] = t < n ? r.lo + t : -1;
+      out[t] = t < n ? lo + t : -1;
       if (out_s) out_s[t] = t < n ? logits[g0 + t] : -INFINITY;
     }
     return;
   }
-
-  // element e of the row is aligned position e + sh of the float4 groups from
-  // g0 - sh; group q = tid + kRgThreads * j of this thread holds positions 4q .. 4q+3
-  const int sh = (int)(g0 & 3);
-  const float4* base4 = reinterpret_cast<const float4*>(logits + (g0 - sh));
   const int n4 = (n + sh + 3) >> 2;
   const int e0 = 4 * tid - sh;  // element of (j, c) = e0 + 4 * kRgThreads * j + c
   float x[kRgPer4][4];
-#pragma unroll
-  for (int j = 0; j < kRgPer4; ++j) {
-    const int q = tid + kRgThreads * j;
-    float4 v = make_float4(NAN, NAN, NAN, NAN);
-    if (q < n4) v = base4[q];
-    x[j][0] = v.x; x[j][1] = v.y; x[j][2] = v.z; x[j][3] = v.w;
-  }
-  // positions outside the row (only in the first and the last group) become NaN
   {
-    const int jl = (n + sh - 1) / 4 / kRgThreads;  // j of the group holding the last element
+    const float4* base4 = reinterpret_cast<const float4*>(logits + (g0 - sh));
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (e0 + c < 0) x[0][c] = NAN;
-#pragma unroll
-      for (int j = 0; j < kRgPer4; ++j)
-        if (j == jl && e0 + 4 * kRgThreads * j + c >= n) x[j][c] = NAN;
+    for (int j = 0; j < kRgPer4; ++j) {
+      const int q = tid + kRgThreads * j;
+      float4 v = make_float4(NAN, NAN, NAN, NAN);
+      if (q < n4) v = base4[q];
+      x[j][0] = v.x; x[j][1] = v.y; x[j][2] = v.z; x[j][3] = v.w;
     }
+  }
+  // positions outside the row (the first sh of group 0, the tail of the last
+  // group) become NaN; written per thread so that no per-element index stays live
+  if (tid == 0) {
+#pragma unroll
+    for (int c = 0; c < 3; ++c)
+      if (c < sh) x[0][c] = NAN;
+  }
+  if (tid == (n4 - 1) % kRgThreads) {
+    const int jl = (n4 - 1) / kRgThreads;
+    const int cl = n + sh - 4 * (n4 - 1);  // elements of the last group inside the row
+#pragma unroll
+    for (int j = 0; j < kRgPer4; ++j)
+      if (j == jl) {
+#pragma unroll
+        for (int c = 1; c < 4; ++c)
+          if (c >= cl) x[j][c] = NAN;
+      }
   }
 
   float mx = -INFINITY, mn = INFINITY;
@@ -605,8 +597,7 @@ __global__ __launch_bounds__(kRgThreads) void k_dsa_select_reg(DevLayout L, int 
     }
   __syncthreads();
 
-  // threshold bin: thread t owns bins kRgBins-1-4t .. kRgBins-4-4t (from the top);
-  // the thread whose bins hold the k-th largest also finds T's value interval
+  // threshold bin: thread t owns bins kRgBins-1-4t .. kRgBins-4-4t (from the top)
   {
     int cnt[4], sum = 0;
 #pragma unroll
@@ -626,51 +617,38 @@ __global__ __launch_bounds__(kRgThreads) void k_dsa_select_reg(DevLayout L, int 
         }
         above += cnt[j];
       }
-      // search brackets: a few bins around mn + T / s, checked, else the whole order
-      constexpr uint32_t kMinKey = 0x007fffffu, kMaxKey = 0xff800000u;  // -inf, +inf
-      uint32_t lo0 = kMinKey, hi0 = kMaxKey, lo1 = kMinKey, hi1 = kMaxKey;
-      if (spread) {
-        const uint32_t kl = rg_raw_key(mn + (float)(T - 2) / bs);
-        const uint32_t kh = rg_raw_key(mn + (float)(T + 3) / bs);
-        if (kl > kMinKey && kl < kh && kh < kMaxKey &&
-            rg_bin(rg_key_float(kl), bs, bo) < T && rg_bin(rg_key_float(kh), bs, bo) > T + 1) {
-          lo0 = lo1 = kl;
-          hi0 = hi1 = kh;
-        }
-      }
-      uint32_t ka, k1;
-      rg_edges(T, T + 1, bs, bo, lo0, hi0, lo1, hi1, &ka, &k1);
-      // bin T is [first float of bin T, the float just below the first of bin T+1]
       s_bin = T;
       s_above = ab;
-      s_xa = rg_key_float(ka);
-      s_xb = T + 1 < kRgBins ? rg_key_float(k1 - 1) : INFINITY;
     }
   }
   __syncthreads();
   const int T = s_bin;  // -1: fewer than k finite logits, all of them are taken
   const int rem = topk - s_above;
   const int nT = T >= 0 ? s_hist[T + 1] : 0;
-  const float xa = T >= 0 ? s_xa : -INFINITY;
-  const float xb = T >= 0 ? s_xb : -INFINITY;
 
-  // counts above xb per (j, wave); values of [xa, xb] become candidates
+  // counts of bins above T per (j, wave); the values of bin T become candidates
+  // (T = -1: every finite value counts).  The map's parameters pass through an
+  // empty asm so that the histogram's bins are recomputed here rather than kept
+  // live in registers; the values, and so the bins, are the same.
+  float bs2 = bs, bo2 = bo;
+  asm volatile("" : "+v"(bs2), "+v"(bo2));
 #pragma unroll
   for (int j = 0; j < kRgPer4; ++j) {
     if (j < jn) {
       int above = 0;
       bool any = false;
+      int b[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bool gt = x[j][c] > xb;
-        above += __popcll(__ballot(gt));
-        any |= !gt && x[j][c] >= xa;
+        b[c] = rg_bin(x[j][c], bs2, bo2);
+        above += __popcll(__ballot(b[c] > T));
+        any |= b[c] == T;
       }
       if (lane == 0) s_cnt[j * kRgWaves + wave] += above;
       if (nT <= kRgCand && __ballot(any)) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          if (!(x[j][c] > xb) && x[j][c] >= xa) {
+          if (b[c] == T) {
             const int slot = atomicAdd(&s_ncand, 1);
             if (slot < kRgCand) s_cand[slot] = rg_composite(x[j][c], e0 + 4 * kRgThreads * j + c);
           }
@@ -712,7 +690,7 @@ __global__ __launch_bounds__(kRgThreads) void k_dsa_select_reg(DevLayout L, int 
       __syncthreads();
       for (int e = tid; e < n; e += kRgThreads) {
         const float v = row[e];
-        if (v >= xa && !(v > xb)) {
+        if (rg_bin(v, bs, bo) == T) {
           const uint64_t u = rg_composite(v, e);
           if ((u & mask) == prefix) atomicAdd(&s_hist[(int)((u >> shift) & 255u)], 1);
         }
@@ -752,7 +730,7 @@ __global__ __launch_bounds__(kRgThreads) void k_dsa_select_reg(DevLayout L, int 
     if (tid == 0) s_cstar = prefix;  // s_straddle stays 1: the exact predicate
     for (int e = tid; e < n; e += kRgThreads) {
       const float v = row[e];
-      if (v >= xa && !(v > xb) && rg_composite(v, e) >= prefix) atomicAdd(&s_cnt[slot_of(e)], 1);
+      if (rg_bin(v, bs, bo) == T && rg_composite(v, e) >= prefix) atomicAdd(&s_cnt[slot_of(e)], 1);
     }
     __syncthreads();
   }
@@ -776,6 +754,10 @@ __global__ __launch_bounds__(kRgThreads) void k_dsa_select_reg(DevLayout L, int 
   const int istar = T >= 0 ? (int)(0xffffffffu - (uint32_t)cstar) : -1;
   const int total = s_wave[0];
 
+  // the indices are gathered in LDS (the histogram's space) and written out
+  // coalesced when the selection fits there
+  int* const s_stage = s_hist;
+  const bool stage = topk <= 2 * ((kRgBins + 2) / 2);
   auto place = [&](auto sel_of) {
 #pragma unroll
     for (int j = 0; j < kRgPer4; ++j) {
@@ -794,7 +776,8 @@ __global__ __launch_bounds__(kRgThreads) void k_dsa_select_reg(DevLayout L, int 
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           if (sel[c] && slot < topk) {
-            out[slot] = r.lo + ej + c;
+            if (stage) s_stage[slot] = lo + ej + c;
+            else out[slot] = lo + ej + c;
             if (out_s) out_s[slot] = x[j][c];
           }
           slot += sel[c];
@@ -807,9 +790,16 @@ __global__ __launch_bounds__(kRgThreads) void k_dsa_select_reg(DevLayout L, int 
   } else {
     place([&](float v, int e) { return v > vstar || (v == vstar && e <= istar); });
   }
-  for (int t = total + tid; t < topk; t += kRgThreads) {
-    out[t] = -1;
-    if (out_s) out_s[t] = -INFINITY;
+  if (stage) {
+    __syncthreads();
+    for (int t = tid; t < topk; t += kRgThreads) out[t] = t < total ? s_stage[t] : -1;
+    if (out_s)
+      for (int t = total + tid; t < topk; t += kRgThreads) out_s[t] = -INFINITY;
+  } else {
+    for (int t = total + tid; t < topk; t += kRgThreads) {
+      out[t] = -1;
+      if (out_s) out_s[t] = -INFINITY;
+    }
   }
 }
 
@@ -847,13 +837,14 @@ hipError_t launch_typed(const DsaArgs& a, hipStream_t stream) {
     }
   }
   trace_end(stream, slot);
-  hipLaunchKernelGGL(k_dsa_select_reg, dim3(a.L.n_q), dim3(kRgThreads), 0, stream, a.L,
-                     a.topk, logits, a.idx, a.score);
+  const int grid = a.L.n_q;  // one row per workgroup
+  hipLaunchKernelGGL(k_dsa_select_reg, dim3(grid), dim3(kRgThreads), 0, stream, a.L, a.topk,
+                     logits, a.idx, a.score);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.L.n_kv <= kRgCap) return e;
-  // rows longer than the register capacity
+  if (e != hipSuccess || a.max_span <= kRgSpan) return e;
+  // rows longer than the register-resident span
   hipLaunchKernelGGL(k_dsa_select, dim3(a.L.n_q), dim3(kSelThreads), 0, stream, a.L,
-                     a.topk, logits, a.idx, a.score, kRgCap);
+                     a.topk, logits, a.idx, a.score, kRgSpan);
   return hipGetLastError();
 }
 

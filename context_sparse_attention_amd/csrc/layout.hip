@@ -31,4 +31,19 @@ hipError_t launch_block_table(const int32_t* cu, int n_seq, int block_size, int 
   return hipGetLastError();
 }
 
+int device_cus() {
+  // queried once per process; the library drives one device model
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
 }  // namespace csa
