@@ -16,11 +16,13 @@
 // convention for rows with no permitted key: same article, masking paragraph).
 //
 // Kernels (in stream order):
-//   k_block_table  (layout.hip) block table + zeroed list counters
+//   k_block_table  (layout.hip) block table + zeroed list counters, only for
+//                  more than kLocalSeqs sequences (otherwise k_bm_hist does it)
 //   k_bm_hist      LDS histogram of full block slots per list for each range of
 //                  (row, head) pairs, own-block multiplicity per (row, head)
 //   k_bm_colscan   one wave per list: prefix of the histogram over the ranges
 //   k_bm_scan      one workgroup: list offsets and the query-tile table
+//                  (for small matrices the fill workgroups derive both themselves)
 //   k_bm_fill      place slot ids into the lists (counting sort)
 //   k_bm_attn      persistent, per-XCD work queues: list tiles, then diagonal
 //                  tiles; S^T = K Q^T and O^T = V^T P^T on LDS-staged key/value
@@ -129,12 +131,73 @@ __device__ inline void pair_range(int64_t pairs, int64_t* b, int64_t* e) {
   *e = min(pairs, *b + per);
 }
 
+// Sequences whose block offsets the bucketing workgroups build in LDS themselves
+// (then no separate block-table kernel runs); more go through k_block_table.
+constexpr int kLocalSeqs = 4096;
+
+// First global block of every sequence, blk_off[0 .. n_seq], into s_off by the
+// workgroup's kHistThreads threads (an exclusive scan of the block counts).
+__device__ inline void local_blk_off(const int32_t* __restrict__ cu, int n_seq, int B,
+                                     int* s_off) {
+  __shared__ int s_wave[kHistThreads / kWave];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  int carry = 0;
+  for (int base = 0; base < n_seq; base += kHistThreads) {
+    const int s = base + threadIdx.x;
+    const int nb = s < n_seq ? (cu[s + 1] - cu[s] + B - 1) / B : 0;
+    int incl = nb;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += y;
+    }
+    if (lane == kWave - 1) s_wave[wave] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kHistThreads / kWave; ++w) {
+      before += w < wave ? s_wave[w] : 0;
+      all += s_wave[w];
+    }
+    if (s < n_seq) s_off[s] = carry + before + incl - nb;
+    carry += all;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) s_off[n_seq] = carry;
+  __syncthreads();
+}
+
+// LOCAL: the workgroup builds the sequences' block offsets in LDS, and
+// workgroup 0 also writes the block table for the later kernels and clears the
+// list-tile total and the work-queue counters (in place of k_block_table).
+template <bool LOCAL>
 __global__ __launch_bounds__(kHistThreads) void k_bm_hist(AttnKernelArgs a, BlockTable bt,
                                                           int n_blocks, int n_lists,
                                                           int32_t* __restrict__ hist,
                                                           int4* __restrict__ pinfo,
-                                                          int4* __restrict__ rowinfo) {
+                                                          int4* __restrict__ rowinfo,
+                                                          int32_t* __restrict__ totals) {
   extern __shared__ int s_bins[];
+  const int* blk_off = bt.blk_off;
+  if (LOCAL) {
+    int* s_off = s_bins + n_lists;
+    local_blk_off(a.L.cu, a.L.n_seq, a.block_size, s_off);
+    blk_off = s_off;
+    if (blockIdx.x == 0) {
+      if (threadIdx.x < 16) totals[threadIdx.x] = 0;
+      for (int s = threadIdx.x; s <= a.L.n_seq; s += kHistThreads) bt.blk_off[s] = s_off[s];
+      for (int b = threadIdx.x; b < n_blocks; b += kHistThreads) {
+        int lo = 0, hi = a.L.n_seq - 1;  // last sequence whose first block is <= b
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_off[mid] <= b) lo = mid; else hi = mid - 1;
+        }
+        const int start = a.L.cu[lo] + (b - s_off[lo]) * a.block_size;
+        bt.blocks[b] = make_int2(start, min(a.block_size, a.L.cu[lo + 1] - start));
+        bt.blk_seq[b] = lo;
+      }
+    }
+  }
   for (int l = threadIdx.x; l < n_lists; l += kHistThreads) s_bins[l] = 0;
   __syncthreads();
   const int hq = a.q.h;
@@ -148,7 +211,7 @@ __global__ __launch_bounds__(kHistThreads) void k_bm_hist(AttnKernelArgs a, Bloc
     uint64_t full = 0;
     if (r.valid) {
       const int32_t* slots = slot_row(a, i, h);
-      const int base = g * n_blocks + bt.blk_off[r.seq];
+      const int base = g * n_blocks + blk_off[r.seq];
       for (int s = 0; s < a.idx_width; ++s) {
         const int st = slots[s];
         const int c = slot_class(st, r, a.block_size);
@@ -162,8 +225,9 @@ __global__ __launch_bounds__(kHistThreads) void k_bm_hist(AttnKernelArgs a, Bloc
     }
     pinfo[pair] = make_int4(mult, (int)(uint32_t)full, (int)(uint32_t)(full >> 32), own_slot);
     if (h == 0) {
-      const int ob = r.valid ? bt.blk_off[r.seq] + (r.hi - r.lo) / a.block_size : -1;
-      rowinfo[i] = make_int4(ob, r.hi, ob >= 0 ? bt.blocks[ob].x : 0, 0);
+      const int ob = r.valid ? blk_off[r.seq] + (r.hi - r.lo) / a.block_size : -1;
+      const int ostart = r.valid ? r.lo + (r.hi - r.lo) / a.block_size * a.block_size : 0;
+      rowinfo[i] = make_int4(ob, r.hi, ostart, 0);
     }
   }
   __syncthreads();
@@ -171,14 +235,101 @@ __global__ __launch_bounds__(kHistThreads) void k_bm_hist(AttnKernelArgs a, Bloc
     hist[(int64_t)l * gridDim.x + blockIdx.x] = s_bins[l];
 }
 
+// SCAN (small histogram matrices, in place of k_bm_colscan and k_bm_scan): the
+// workgroup reads the whole matrix, one list a thread, and derives its own
+// list offsets (exclusive scan of the list totals) and per-range prefixes;
+// workgroup 0 also writes the list totals, offsets, the list-tile table and
+// the tile count for the attention kernel.
+template <bool LOCAL, bool SCAN>
 __global__ __launch_bounds__(kHistThreads) void k_bm_fill(AttnKernelArgs a, BlockTable bt,
                                                           int n_blocks, int n_lists,
-                                                          const int32_t* __restrict__ list_off,
+                                                          int32_t* __restrict__ list_off,
                                                           const int32_t* __restrict__ hist,
-                                                          int32_t* __restrict__ entries) {
+                                                          int32_t* __restrict__ entries,
+                                                          int32_t* __restrict__ counts,
+                                                          int2* __restrict__ tiles,
+                                                          int32_t* __restrict__ totals) {
   extern __shared__ int s_bins[];
-  for (int l = threadIdx.x; l < n_lists; l += kHistThreads)
-    s_bins[l] = list_off[l] + hist[(int64_t)l * gridDim.x + blockIdx.x];
+  const int* blk_off = bt.blk_off;
+  if (LOCAL) {
+    local_blk_off(a.L.cu, a.L.n_seq, a.block_size, s_bins + n_lists + (SCAN ? n_lists : 0));
+    blk_off = s_bins + n_lists + (SCAN ? n_lists : 0);
+  }
+  if (SCAN) {
+    __shared__ int s_wave[kHistThreads / kWave];
+    __shared__ int s_carry[2];
+    int* s_cnt = s_bins + n_lists;  // list totals, then the list offsets
+    const int n_hist = gridDim.x;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    for (int l = threadIdx.x; l < n_lists; l += kHistThreads) {
+      const int32_t* h = hist + (int64_t)l * n_hist;
+      int tot = 0, pre = 0;
+#pragma unroll 16
+      for (int w = 0; w < n_hist; ++w) {
+        const int v = h[w];
+        tot += v;
+        pre += w < (int)blockIdx.x ? v : 0;
+      }
+      s_cnt[l] = tot;
+      s_bins[l] = pre;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) s_carry[0] = s_carry[1] = 0;
+    for (int base = 0; base < n_lists; base += kHistThreads) {
+      const int l = base + threadIdx.x;
+      const int c = l < n_lists ? s_cnt[l] : 0;
+      const int nt = (c + kTM - 1) / kTM;
+      int incl = c, tincl = nt;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(incl, off, kWave), ty = __shfl_up(tincl, off, kWave);
+        if (lane >= off) {
+          incl += y;
+          tincl += ty;
+        }
+      }
+      if (lane == kWave - 1) s_wave[wave] = incl;
+      __syncthreads();
+      int before = 0, all = 0;
+#pragma unroll
+      for (int w = 0; w < kHistThreads / kWave; ++w) {
+        before += w < wave ? s_wave[w] : 0;
+        all += s_wave[w];
+      }
+      __syncthreads();
+      if (lane == kWave - 1) s_wave[wave] = tincl;
+      __syncthreads();
+      int tbefore = 0, tall = 0;
+#pragma unroll
+      for (int w = 0; w < kHistThreads / kWave; ++w) {
+        tbefore += w < wave ? s_wave[w] : 0;
+        tall += s_wave[w];
+      }
+      const int off = s_carry[0] + before + incl - c;
+      const int first = s_carry[1] + tbefore + tincl - nt;
+      if (l < n_lists) {
+        s_bins[l] += off;
+        if (blockIdx.x == 0) {
+          counts[l] = c;
+          list_off[l] = off;
+          for (int j = 0; j < nt; ++j) tiles[first + j] = make_int2(l, j * kTM);
+        }
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        s_carry[0] += all;
+        s_carry[1] += tall;
+      }
+    }
+    __syncthreads();
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      list_off[n_lists] = s_carry[0];
+      totals[0] = s_carry[1];
+    }
+  } else {
+    for (int l = threadIdx.x; l < n_lists; l += kHistThreads)
+      s_bins[l] = list_off[l] + hist[(int64_t)l * gridDim.x + blockIdx.x];
+  }
   __syncthreads();
   const int hq = a.q.h;
   int64_t b, e;
@@ -189,7 +340,7 @@ __global__ __launch_bounds__(kHistThreads) void k_bm_fill(AttnKernelArgs a, Bloc
     const RowKeys r = row_keys(a.L, i);
     if (!r.valid) continue;
     const int32_t* slots = slot_row(a, i, h);
-    const int base = g * n_blocks + bt.blk_off[r.seq];
+    const int base = g * n_blocks + blk_off[r.seq];
     for (int s = 0; s < a.idx_width; ++s) {
       const int st = slots[s];
       if (slot_class(st, r, a.block_size) != 1) continue;
@@ -243,6 +394,11 @@ __global__ __launch_bounds__(kHistThreads) void k_bm_colscan(int n_lists, int n_
   }
   if (lane == 0) counts[l] = carry;
 }
+
+// Histogram matrices of at most this many cells (and lists) are scanned by the
+// fill workgroups themselves; larger ones by k_bm_colscan then k_bm_scan.
+constexpr int64_t kFillScanCells = 1 << 15;
+constexpr int kFillScanLists = 4096;
 
 __global__ __launch_bounds__(kScanThreads) void k_bm_scan(int n_lists,
                                                           const int32_t* __restrict__ counts,
@@ -801,24 +957,43 @@ hipError_t launch_d(const AttnKernelArgs& a, int n_blocks, void* ws, hipStream_t
   const int hq = a.q.h, hkv = a.k.h;
   carve_bm<true>(ws, a.L.n_q, n_seq, n_blocks, hq, hkv, D, a.idx_width, &w);
   const int n_lists = hkv * n_blocks;
-  // also zeroes the list-tile total and the work-queue counters
-  hipError_t e = launch_block_table(a.L.cu, n_seq, a.block_size, n_blocks, w.bt, w.totals, 16,
-                                    stream);
-  if (e != hipSuccess) return e;
-  const size_t bins = (size_t)n_lists * sizeof(int);
   const int n_hist = hist_wgs((int64_t)a.L.n_q * hq, n_lists);
-  hipLaunchKernelGGL(k_bm_hist, dim3(n_hist), dim3(kHistThreads), bins, stream, a, w.bt,
-                     n_blocks, n_lists, w.hist, w.pinfo, w.rowinfo);
+  // the LDS of a bucketing workgroup holds the list bins and, if local, the offsets
+  const bool local = n_seq <= kLocalSeqs && (int64_t)(2 * n_lists + n_seq + 1) * 4 <= 65536;
+  hipError_t e;
+  if (!local) {
+    // also zeroes the list-tile total and the work-queue counters
+    e = launch_block_table(a.L.cu, n_seq, a.block_size, n_blocks, w.bt, w.totals, 16, stream);
+    if (e != hipSuccess) return e;
+  }
+  const size_t bins = (size_t)(n_lists + (local ? n_seq + 1 : 0)) * sizeof(int);
+  if (local)
+    hipLaunchKernelGGL(k_bm_hist<true>, dim3(n_hist), dim3(kHistThreads), bins, stream, a, w.bt,
+                       n_blocks, n_lists, w.hist, w.pinfo, w.rowinfo, w.totals);
+  else
+    hipLaunchKernelGGL(k_bm_hist<false>, dim3(n_hist), dim3(kHistThreads), bins, stream, a,
+                       w.bt, n_blocks, n_lists, w.hist, w.pinfo, w.rowinfo, w.totals);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int lists_per_wg = kHistThreads / kWave;
-  hipLaunchKernelGGL(k_bm_colscan, dim3((n_lists + lists_per_wg - 1) / lists_per_wg),
-                     dim3(kHistThreads), 0, stream, n_lists, n_hist, w.hist, w.counts);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_bm_scan, dim3(1), dim3(kScanThreads), 0, stream, n_lists, w.counts,
-                     w.list_off, w.tiles, w.totals);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_bm_fill, dim3(n_hist), dim3(kHistThreads), bins, stream, a, w.bt,
-                     n_blocks, n_lists, w.list_off, w.hist, w.entries);
+  const bool fused = (int64_t)n_lists * n_hist <= kFillScanCells && n_lists <= kFillScanLists;
+  if (!fused) {
+    const int lists_per_wg = kHistThreads / kWave;
+    hipLaunchKernelGGL(k_bm_colscan, dim3((n_lists + lists_per_wg - 1) / lists_per_wg),
+                       dim3(kHistThreads), 0, stream, n_lists, n_hist, w.hist, w.counts);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_bm_scan, dim3(1), dim3(kScanThreads), 0, stream, n_lists, w.counts,
+                       w.list_off, w.tiles, w.totals);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const size_t fbins = bins + (fused ? (size_t)n_lists * sizeof(int) : 0);
+#define CSA_FILL(L_, S_)                                                                      \
+  hipLaunchKernelGGL((k_bm_fill<L_, S_>), dim3(n_hist), dim3(kHistThreads), fbins, stream, a, \
+                     w.bt, n_blocks, n_lists, w.list_off, w.hist, w.entries, w.counts, w.tiles, \
+                     w.totals)
+  if (local && fused) CSA_FILL(true, true);
+  else if (local) CSA_FILL(true, false);
+  else if (fused) CSA_FILL(false, true);
+  else CSA_FILL(false, false);
+#undef CSA_FILL
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int grid = 2 * device_cus();
   int slot;

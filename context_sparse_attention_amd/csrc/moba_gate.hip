@@ -7,12 +7,11 @@
 // of a block is the query's dot product with the block's mean key (the plain
 // reading of "Q x K^T" at block granularity: q . mean(k) = mean(q . k)).
 //
-// Three kernels:
-//   k_gate_prep  - block table and, per packed sequence, the highest own block of
-//                  any local row (one workgroup, small shards; k_block_table +
-//                  k_moba_need otherwise)
-//                  (blocks at or after it are never candidates, so they are
-//                  not pooled);
+// Kernels:
+//   k_block_table + k_moba_need - block table and, per packed sequence, the
+//                  highest own block of any local row (blocks at or after it
+//                  are never candidates, so they are not pooled); for small
+//                  shards the pool kernel works both out itself;
 //   k_moba_pool  - fp32 block means (and their bf16 high/low split), one
 //                  workgroup per (block, key head), coalesced 16-byte loads,
 //                  fixed-order LDS reduction (deterministic);
@@ -112,16 +111,120 @@ __global__ void k_moba_need(DevLayout L, int block_size, const int32_t* __restri
 // loads, the other lanes stride over the block's keys, and the partial sums
 // are reduced through LDS in a fixed order (deterministic, no atomics, no
 // cross-workgroup fences).
-template <typename T>
-__global__ __launch_bounds__(kPoolThreads) void k_moba_pool(View k, BlockTable bt,
+// LOCAL (small shards): no table or need kernel runs before; each workgroup
+// builds the sequences' block offsets in LDS, finds its block's sequence and
+// extent, and checks over the shard's rows whether any row's own block lies
+// after it; workgroup 0 writes the block table for the gate kernel.
+template <typename T, bool LOCAL>
+__global__ __launch_bounds__(kPoolThreads) void k_moba_pool(View k, DevLayout L, int block_size,
+                                                            BlockTable bt,
                                                             const int32_t* __restrict__ need,
                                                             float* __restrict__ mu,
                                                             __bf16* __restrict__ mu_hi,
                                                             __bf16* __restrict__ mu_lo) {
   const int b = blockIdx.x / k.h;
   const int g = blockIdx.x % k.h;
-  if (b >= need[bt.blk_seq[b]]) return;  // never a candidate of any local row
-  const int2 blk = bt.blocks[b];
+  int2 blk;
+  if (LOCAL) {
+    __shared__ int s_off[kPrepSeqs + 1];
+    __shared__ int s_wave[kPoolThreads / kWave];
+    __shared__ int s_max[kPoolThreads / kWave];
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    int carry = 0;
+    for (int base = 0; base < L.n_seq; base += kPoolThreads) {
+      const int s = base + threadIdx.x;
+      const int nb = s < L.n_seq ? (L.cu[s + 1] - L.cu[s] + block_size - 1) / block_size : 0;
+      int incl = nb;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += y;
+      }
+      if (lane == kWave - 1) s_wave[wave] = incl;
+      __syncthreads();
+      int before = 0, all = 0;
+#pragma unroll
+      for (int w = 0; w < kPoolThreads / kWave; ++w) {
+        before += w < wave ? s_wave[w] : 0;
+        all += s_wave[w];
+      }
+      if (s < L.n_seq) s_off[s] = carry + before + incl - nb;
+      carry += all;
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) s_off[L.n_seq] = carry;
+    __syncthreads();
+    auto seq_of = [&](int bb) {  // last sequence whose first block is <= bb
+      int lo = 0, hi = L.n_seq - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_off[mid] <= bb) lo = mid; else hi = mid - 1;
+      }
+      return lo;
+    };
+    if (blockIdx.x == 0) {
+      for (int s = threadIdx.x; s <= L.n_seq; s += kPoolThreads) bt.blk_off[s] = s_off[s];
+      for (int bb = threadIdx.x; bb < gridDim.x / k.h; bb += kPoolThreads) {
+        const int s = seq_of(bb);
+        const int start = L.cu[s] + (bb - s_off[s]) * block_size;
+        bt.blocks[bb] = make_int2(start, min(block_size, L.cu[s + 1] - start));
+        bt.blk_seq[bb] = s;
+      }
+    }
+    const int seq = seq_of(b);
+    const int bl = b - s_off[seq];  // block within its sequence
+    blk.x = L.cu[seq] + bl * block_size;
+    blk.y = min(block_size, L.cu[seq + 1] - blk.x);
+    // needed when some row of the sequence has its own block after this one;
+    // the rows' sequence ids and positions are read four at a time, all loads
+    // of a thread in flight together
+    const int lo_s = L.cu[seq], end_s = L.cu[seq + 1];
+    int own = -1;
+    constexpr int kRowsPer = kPrepRows / kPoolThreads;  // rows of one thread, at most
+    static_assert(kRowsPer % 4 == 0, "rows are read in groups of four");
+    int4 sq[kRowsPer / 4], ps[kRowsPer / 4];
+    const bool vec = (L.n_q & 3) == 0 && ((uintptr_t)L.q_seq & 15) == 0 &&
+                     ((uintptr_t)L.q_pos & 15) == 0;
+#pragma unroll
+    for (int j = 0; j < kRowsPer / 4; ++j) {
+      const int i0 = 4 * (threadIdx.x + kPoolThreads * j);
+      sq[j] = make_int4(-1, -1, -1, -1);
+      ps[j] = make_int4(0, 0, 0, 0);
+      if (vec && i0 < L.n_q) {
+        sq[j] = *reinterpret_cast<const int4*>(L.q_seq + i0);
+        ps[j] = *reinterpret_cast<const int4*>(L.q_pos + i0);
+      } else if (!vec) {
+        int s4[4] = {-1, -1, -1, -1}, p4[4] = {0, 0, 0, 0};
+        for (int t = 0; t < 4; ++t)
+          if (i0 + t < L.n_q) {
+            s4[t] = L.q_seq[i0 + t];
+            p4[t] = L.q_pos[i0 + t];
+          }
+        sq[j] = make_int4(s4[0], s4[1], s4[2], s4[3]);
+        ps[j] = make_int4(p4[0], p4[1], p4[2], p4[3]);
+      }
+    }
+    auto take = [&](int s, int p) {
+      if (s == seq && p >= lo_s && p < end_s) own = max(own, (p - lo_s) / block_size);
+    };
+#pragma unroll
+    for (int j = 0; j < kRowsPer / 4; ++j) {
+      take(sq[j].x, ps[j].x);
+      take(sq[j].y, ps[j].y);
+      take(sq[j].z, ps[j].z);
+      take(sq[j].w, ps[j].w);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) own = max(own, __shfl_xor(own, off, kWave));
+    if (lane == 0) s_max[wave] = own;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kPoolThreads / kWave; ++w) own = max(own, s_max[w]);
+    if (bl >= own) return;  // never a candidate of any local row
+  } else {
+    if (b >= need[bt.blk_seq[b]]) return;  // never a candidate of any local row
+    blk = bt.blocks[b];
+  }
   const int d = k.d;
   const int units = d / 8;                // <= 32
   const int lanes_k = kPoolThreads / units;
@@ -501,7 +604,10 @@ hipError_t launch_typed(const MobaGateArgs& a, hipStream_t stream) {
   const int n_seq = a.L.n_seq;
   MobaWs w = carve_moba(a.ws, n_seq, a.n_blocks, a.k.h, a.k.d, a.block_size);
   hipError_t e;
-  if (n_seq <= kPrepSeqs && a.L.n_q <= kPrepRows) {
+  const bool local = n_seq <= kPrepSeqs && a.L.n_q <= kPrepRows && a.n_blocks > 0;
+  if (local) {
+    if (a.L.n_q == 0) return hipSuccess;
+  } else if (n_seq <= kPrepSeqs && a.L.n_q <= kPrepRows) {
     hipLaunchKernelGGL(k_gate_prep, dim3(1), dim3(kTableThreads), 0, stream, a.L, a.block_size,
                        a.n_blocks, w.bt, w.need);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -517,9 +623,14 @@ hipError_t launch_typed(const MobaGateArgs& a, hipStream_t stream) {
   }
   const bool use_mfma = a.dtype == CSA_BF16 && (a.q.d == 64 || a.q.d == 128 || a.q.d == 256);
   if (a.n_blocks > 0) {
-    hipLaunchKernelGGL((k_moba_pool<T>), dim3(a.n_blocks * a.k.h), dim3(kPoolThreads), 0,
-                       stream, a.k, w.bt, w.need, w.mu, use_mfma ? w.mu_hi : nullptr,
-                       use_mfma ? w.mu_lo : nullptr);
+    if (local)
+      hipLaunchKernelGGL((k_moba_pool<T, true>), dim3(a.n_blocks * a.k.h), dim3(kPoolThreads), 0,
+                         stream, a.k, a.L, a.block_size, w.bt, w.need, w.mu,
+                         use_mfma ? w.mu_hi : nullptr, use_mfma ? w.mu_lo : nullptr);
+    else
+      hipLaunchKernelGGL((k_moba_pool<T, false>), dim3(a.n_blocks * a.k.h), dim3(kPoolThreads),
+                         0, stream, a.k, a.L, a.block_size, w.bt, w.need, w.mu,
+                         use_mfma ? w.mu_hi : nullptr, use_mfma ? w.mu_lo : nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   int slot;
