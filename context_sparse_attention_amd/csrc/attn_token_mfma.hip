@@ -35,6 +35,8 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTK = 32;          // gathered keys per tile
+constexpr int kKD = 2;           // key (and LDS query) fragment reads in flight ahead of use
+constexpr int kVD = 2;           // transposed value fragment reads in flight ahead of use
 constexpr float kLazy = 8.0f;    // log2 headroom before the running max moves
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -160,15 +162,20 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_tok_attn(AttnKernelArgs a) {
   float m = -INFINITY, l = 0.f;
 
   const int n_kt = r.valid ? (W + kTK - 1) / kTK : 0;
-  auto fetch_keys = [&](int kt) {
+  // slot key of tile kt for thread t < kTK (loaded a tile ahead of its store,
+  // so that the load's latency hides under a tile of MFMAs)
+  auto load_key = [&](int kt) {
+    const int j = kt * kTK + threadIdx.x;
+    return (threadIdx.x < kTK && j < W) ? slots[j] : -1;
+  };
+  auto store_key = [&](int kt, int key) {
     if (threadIdx.x < kTK) {
-      const int j = kt * kTK + threadIdx.x;
-      const int key = j < W ? slots[j] : -1;
       const bool ok = key >= r.lo && key <= r.hi;
       s_keys[kt % 3][threadIdx.x] = ok ? key : r.lo;  // masked slots read a valid row
       s_valid[kt % 3][threadIdx.x] = ok;
     }
   };
+  auto fetch_keys = [&](int kt) { store_key(kt, load_key(kt)); };
   auto issue = [&](int kt) {
     issue_tile<DQK>(a.k, g, s_keys[kt % 3], s.k[kt & 1], wave, NW);
     if constexpr (!ALIAS) issue_tile<DV>(a.v, g, s_keys[kt % 3], s.v[ALIAS ? 0 : (kt & 1)], wave, NW);
@@ -184,7 +191,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_tok_attn(AttnKernelArgs a) {
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
     const int ks3 = kt % 3;
-    if (kt + 1 < n_kt) issue(kt + 1);  // lands in the other buffer while this one is used
+    const int key2 = kt + 2 < n_kt ? load_key(kt + 2) : -1;
     // S^T = K Q^T: lane holds keys 8 (j / 4) + 4 half + (j % 4) of its query.
     // Two accumulators (even and odd steps) keep consecutive MFMAs independent;
     // fragment reads run two MFMAs ahead.
@@ -199,28 +206,52 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_tok_attn(AttnKernelArgs a) {
       // query fragments past NQR come from LDS, read along with the key fragment
       auto qlds = [&](int ks) { return s.q[wave][ks - NQR][lane]; };
       f32x16 sab[2];  // even and odd steps
-      bf16x8 ka[3], qa[3];
-      ka[0] = kfrag(0);
-      ka[1] = kfrag(1);
-      if (NQR <= 0) qa[0] = qlds(0);
-      if (NQR <= 1) qa[1] = qlds(1);
+      bf16x8 ka[kKD + 1], qa[kKD + 1];
+#pragma unroll
+      for (int t = 0; t < kKD; ++t) {
+        ka[t] = kfrag(t);
+        if (t >= NQR) qa[t] = qlds(t);
+      }
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) {
-        if (ks + 2 < NK) {
-          ka[(ks + 2) % 3] = kfrag(ks + 2);
-          if (ks + 2 >= NQR) qa[(ks + 2) % 3] = qlds(ks + 2);
+        if (ks + kKD < NK) {
+          ka[(ks + kKD) % (kKD + 1)] = kfrag(ks + kKD);
+          if (ks + kKD >= NQR) qa[(ks + kKD) % (kKD + 1)] = qlds(ks + kKD);
         }
-        const bf16x8 q = ks < NQR ? qf[ks < NQR ? ks : 0] : qa[ks % 3];
+        const bf16x8 q = ks < NQR ? qf[ks < NQR ? ks : 0] : qa[ks % (kKD + 1)];
         if (ks < 2)
-          mfma_v0(sab[ks], ka[ks % 3], q);
+          mfma_v0(sab[ks], ka[ks % (kKD + 1)], q);
         else
-          mfma_v(sab[ks & 1], ka[ks % 3], q);
+          mfma_v(sab[ks & 1], ka[ks % (kKD + 1)], q);
+        // the next tile's gather (into the other buffer) is issued once the
+        // first MFMAs run, so that its address work overlaps them
+        if (ks == 3 && kt + 1 < n_kt) issue(kt + 1);
         __builtin_amdgcn_sched_barrier(0);
       }
       fence_v(sab);
 #pragma unroll
       for (int j = 0; j < 16; ++j) sc[j] = sab[0][j] + sab[1][j];
     }
+    // O^T += V^T P^T with V^T read transposed from the row-major tile: the first
+    // kVD fragment reads are issued before the softmax, and each MFMA has the
+    // reads of the next kVD in flight
+    const __bf16* vbase = ALIAS ? s.k[buf] : s.v[ALIAS ? 0 : buf];
+    constexpr int VP = ALIAS ? Lds::kPitch : Lds::kVPitch;
+    constexpr int NO = 2 * (DV / 32);  // MFMA i: key step i / (DV / 32), value block i % (DV / 32)
+    const int c16 = lane & 15;
+    const int grp = lane >> 4;
+    auto vfrag = [&](int i) {
+      const int st = i / (DV / 32), dt = i % (DV / 32);
+      const int ka_ = 16 * st + 4 * half + (c16 >> 2);
+      const int dv = dt * 32 + 16 * (grp & 1) + 4 * (c16 & 3);
+      const bf16x4 lo = read_tr(vbase, tile_off<VP>(ka_, dv));
+      const bf16x4 hi = read_tr(vbase, tile_off<VP>(ka_ + 8, dv));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8 va[kVD + 1];
+#pragma unroll
+    for (int t = 0; t < kVD; ++t) va[t] = vfrag(t);
+
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -252,34 +283,16 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_tok_attn(AttnKernelArgs a) {
     }
     rs += __shfl_xor(rs, 32, kWave);
     l += rs;
-    // O^T += V^T P^T with V^T read transposed from the row-major tile; the
-    // transposing reads of the next two MFMAs are in flight during each one
-    const __bf16* vbase = ALIAS ? s.k[buf] : s.v[ALIAS ? 0 : buf];
-    constexpr int VP = ALIAS ? Lds::kPitch : Lds::kVPitch;
     {
-      constexpr int NO = 2 * (DV / 32);  // MFMA i: key step i / (DV / 32), value block i % (DV / 32)
-      const int c16 = lane & 15;
-      const int grp = lane >> 4;
-      auto vfrag = [&](int i) {
-        const int st = i / (DV / 32), dt = i % (DV / 32);
-        const int ka_ = 16 * st + 4 * half + (c16 >> 2);
-        const int dv = dt * 32 + 16 * (grp & 1) + 4 * (c16 & 3);
-        const bf16x4 lo = read_tr(vbase, tile_off<VP>(ka_, dv));
-        const bf16x4 hi = read_tr(vbase, tile_off<VP>(ka_ + 8, dv));
-        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      };
-      bf16x8 va[3];
-      va[0] = vfrag(0);
-      va[1] = vfrag(1);
 #pragma unroll
       for (int i = 0; i < NO; ++i) {
-        if (i + 2 < NO) va[(i + 2) % 3] = vfrag(i + 2);
+        if (i + kVD < NO) va[(i + kVD) % (kVD + 1)] = vfrag(i + kVD);
         const int st = i / (DV / 32), dt = i % (DV / 32);
-        mfma_a(o[dt], va[i % 3], pb[st]);
+        mfma_a(o[dt], va[i % (kVD + 1)], pb[st]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (kt + 2 < n_kt) fetch_keys(kt + 2);
+    if (kt + 2 < n_kt) store_key(kt + 2, key2);
     __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct loads have landed
     __syncthreads();
   }
