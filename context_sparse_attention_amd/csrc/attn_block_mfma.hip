@@ -65,7 +65,7 @@ struct BmWs {
   int32_t* counts;    // [n_lists]  slots per list
   int32_t* hist;      // [n_lists, n_hist]  per-range counts, then prefixes
   int32_t* list_off;  // [n_lists + 1]
-  int2* tiles;        // [max_tiles]  (list, first entry)
+  int4* tiles;        // [max_tiles]  (list, first entry in entries[], slots, 0)
   int32_t* totals;    // [16]  [0] list tiles, [kQueue0 + x] work-queue counter of XCD x
   int4* pinfo;        // [n_q * hq]  own-block multiplicity, full-block slot mask (lo, hi),
                       //             first own-block slot (-1 if none)
@@ -99,7 +99,7 @@ size_t carve_bm(void* base, int n_q, int n_seq, int n_blocks, int hq, int hkv, i
   t.counts = c.take<int32_t>(n_lists);
   t.hist = c.take<int32_t>((size_t)hist_wgs((int64_t)n_q * hq, n_lists) * n_lists);
   t.list_off = c.take<int32_t>(n_lists + 1);
-  t.tiles = c.take<int2>(max_query_tiles(slots, n_lists));
+  t.tiles = c.take<int4>(max_query_tiles(slots, n_lists));
   t.totals = c.take<int32_t>(16);
   t.pinfo = c.take<int4>((size_t)n_q * hq);
   t.rowinfo = c.take<int4>((size_t)n_q);
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(kHistThreads) void k_bm_fill(AttnKernelArgs a, Bloc
                                                           const int32_t* __restrict__ hist,
                                                           int32_t* __restrict__ entries,
                                                           int32_t* __restrict__ counts,
-                                                          int2* __restrict__ tiles,
+                                                          int4* __restrict__ tiles,
                                                           int32_t* __restrict__ totals) {
   extern __shared__ int s_bins[];
   const int* blk_off = bt.blk_off;
@@ -312,7 +312,8 @@ __global__ __launch_bounds__(kHistThreads) void k_bm_fill(AttnKernelArgs a, Bloc
         if (blockIdx.x == 0) {
           counts[l] = c;
           list_off[l] = off;
-          for (int j = 0; j < nt; ++j) tiles[first + j] = make_int2(l, j * kTM);
+          for (int j = 0; j < nt; ++j)
+            tiles[first + j] = make_int4(l, off + j * kTM, min(kTM, c - j * kTM), 0);
         }
       }
       __syncthreads();
@@ -403,7 +404,7 @@ constexpr int kFillScanLists = 4096;
 __global__ __launch_bounds__(kScanThreads) void k_bm_scan(int n_lists,
                                                           const int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ list_off,
-                                                          int2* __restrict__ tiles,
+                                                          int4* __restrict__ tiles,
                                                           int32_t* __restrict__ totals) {
   __shared__ int s_wave[kScanThreads / kWave];
   int carry = 0, tcarry = 0, tot = 0;
@@ -417,7 +418,8 @@ __global__ __launch_bounds__(kScanThreads) void k_bm_scan(int n_lists,
     if (l < n_lists) {
       list_off[l] = carry + incl - c;
       const int first = tcarry + tincl - nt;
-      for (int j = 0; j < nt; ++j) tiles[first + j] = make_int2(l, j * kTM);
+      for (int j = 0; j < nt; ++j)
+        tiles[first + j] = make_int4(l, carry + incl - c + j * kTM, min(kTM, c - j * kTM), 0);
     }
     carry += ctot;
     tcarry += tot;
@@ -742,12 +744,12 @@ __device__ __forceinline__ void list_item(Lds<D>& s, const AttnKernelArgs& a, co
   const int half = lane >> 5;
   const int hq = a.q.h;
   const int W = a.idx_width;
-  const int2 tl = w.tiles[t];
+  const int4 tl = w.tiles[t];
   const int list = tl.x;
   const int g = list / n_blocks;
   const int blk = list % n_blocks;
-  const int cnt = min(kTM, w.counts[list] - tl.y);
-  const int32_t* ent = w.entries + w.list_off[list] + tl.y;
+  const int cnt = tl.z;
+  const int32_t* ent = w.entries + tl.y;
   const int n = wave * kQW + (lane & 31);
   const bool valid = n < cnt;
   const int p = ent[valid ? n : 0];
