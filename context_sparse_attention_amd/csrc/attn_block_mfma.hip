@@ -491,7 +491,7 @@ struct Gather {
   // rows at or beyond `rows` repeat row rows - 1 (their scores are masked)
   __device__ __forceinline__ void init(const View& K, const View& V, int rows) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar branches
 #pragma unroll
     for (int j = 0; j < kKPer; ++j) {
       const int slot = (wave + kWaves * j) * 64 + lane;
@@ -509,7 +509,7 @@ struct Gather {
   }
 
   __device__ __forceinline__ void issue(const char* kb, const char* vb, Lds<D>& s, int buf) const {
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar branches
     const uint32_t kl = lds_addr(&s.k[buf][0]), vl = lds_addr(&s.v[buf][0]);
 #pragma unroll
     for (int j = 0; j < kKPer; ++j) {

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_tok_attn(AttnKernelArgs a) {
   __shared__ int s_keys[3][kTK];
   __shared__ int s_valid[3][kTK];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar branches
   const int half = lane >> 5;
   const int hkv = a.k.h;
   const int i = blockIdx.x / hkv;

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kLgThreads, 2) void k_dsa_logits_mfma(View iq, View
   constexpr int KP = DI + 8;
   __shared__ __bf16 s_k[2][kLgKeys * KP];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar branches
   const int half = lane >> 5;
   const int t0 = blockIdx.x * kLgWaves;
   const int row = t0 + wave;
