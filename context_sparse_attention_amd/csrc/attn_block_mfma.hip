@@ -407,6 +407,8 @@ __global__ __launch_bounds__(kScanThreads) void k_bm_scan(int n_lists,
                                                           int4* __restrict__ tiles,
                                                           int32_t* __restrict__ totals) {
   __shared__ int s_wave[kScanThreads / kWave];
+  __shared__ int s_tfirst[kMaxLists + 1];  // first tile of each list
+  __shared__ int s_loff[kMaxLists];        // first entry of each list
   int carry = 0, tcarry = 0, tot = 0;
   for (int base = 0; base < n_lists; base += kScanThreads) {
     const int l = base + threadIdx.x;
@@ -416,10 +418,8 @@ __global__ __launch_bounds__(kScanThreads) void k_bm_scan(int n_lists,
     const int nt = (c + kTM - 1) / kTM;
     const int tincl = scan_incl(nt, s_wave, &tot);
     if (l < n_lists) {
-      list_off[l] = carry + incl - c;
-      const int first = tcarry + tincl - nt;
-      for (int j = 0; j < nt; ++j)
-        tiles[first + j] = make_int4(l, carry + incl - c + j * kTM, min(kTM, c - j * kTM), 0);
+      list_off[l] = s_loff[l] = carry + incl - c;
+      s_tfirst[l] = tcarry + tincl - nt;
     }
     carry += ctot;
     tcarry += tot;
@@ -427,6 +427,25 @@ __global__ __launch_bounds__(kScanThreads) void k_bm_scan(int n_lists,
   if (threadIdx.x == 0) {
     list_off[n_lists] = carry;
     totals[0] = tcarry;
+    s_tfirst[n_lists] = tcarry;
+  }
+  __syncthreads();
+  // the tile table: each thread writes a run of consecutive tiles, finding the
+  // list of its first tile by binary search over the lists' first tiles
+  const int per = (tcarry + kScanThreads - 1) / kScanThreads;
+  const int t0 = threadIdx.x * per, t1 = min(tcarry, t0 + per);
+  if (t0 < t1) {
+    int lo = 0, hi = n_lists - 1;  // last list whose first tile is <= t0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_tfirst[mid] <= t0) lo = mid; else hi = mid - 1;
+    }
+    for (int t = t0; t < t1; ++t) {
+      while (s_tfirst[lo + 1] <= t) ++lo;  // empty lists have no tiles
+      const int j = t - s_tfirst[lo];
+      const int cnt = (lo + 1 < n_lists ? s_loff[lo + 1] : carry) - s_loff[lo];
+      tiles[t] = make_int4(lo, s_loff[lo] + j * kTM, min(kTM, cnt - j * kTM), 0);
+    }
   }
 }
 
@@ -740,7 +759,7 @@ template <int D>
 __device__ __forceinline__ void list_item(Lds<D>& s, const AttnKernelArgs& a, const BmWs& w,
                                           int n_blocks, int t) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int half = lane >> 5;
   const int hq = a.q.h;
   const int W = a.idx_width;
@@ -797,7 +816,7 @@ __device__ __forceinline__ void diag_item(Lds<D>& s, int* s_own, int* s_pos, int
                                           uint64_t* s_mask, const AttnKernelArgs& a,
                                           const BmWs& w, int item) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int half = lane >> 5;
   const int hkv = a.k.h;
   const int hq = a.q.h;

@@ -395,7 +395,7 @@ __global__ __launch_bounds__(kGateThreads) void k_moba_gate_mfma(
   constexpr int LPR = 4 / RG;          // selection lanes per row
   __shared__ float s_sc[kGateThreads / kWave][RW][PW + 1];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int hq = q.h;
   const int n_rg = (L.n_q + RW - 1) / RW;
   const int wg = blockIdx.x * (kGateThreads / kWave) + wave;
