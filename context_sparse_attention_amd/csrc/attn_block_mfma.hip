@@ -891,6 +891,11 @@ __device__ __forceinline__ void diag_item(Lds<D>& s, int* s_own, int* s_pos, int
 // b % 8 and takes items from that XCD's queue, which holds a contiguous eighth
 // of the list tiles (so the tiles of one key block share one L2) followed by
 // an eighth of the diagonal tiles (smaller, uneven items that fill the tail).
+// A queue's first items go one to each of its workgroups without an atomic
+// (b / 8 is the workgroup's index among them); the counter hands out the rest.
+// Device-scope atomics take microseconds here, and all workgroups asking at
+// once made the first one the slowest.  The workgroup that takes a queue's
+// last item knows that nothing is left and ends without asking again.
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void k_bm_attn(AttnKernelArgs a, BmWs w,
                                                          int n_blocks) {
@@ -907,16 +912,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_bm_attn(AttnKernelArgs a, BmWs 
   const int lper = (n_lt + kXcds - 1) / kXcds, dper = (n_dt + kXcds - 1) / kXcds;
   const int lb = min(n_lt, x * lper), ln = min(n_lt, lb + lper) - lb;
   const int db = min(n_dt, x * dper), dn = min(n_dt, db + dper) - db;
-  for (;;) {
-    if (threadIdx.x == 0) s_item = atomicAdd(&w.totals[kQueue0 + x], 1);
-    __syncthreads();
-    const int q = s_item;
-    if (q >= ln + dn) break;
+  const int nper = (gridDim.x - x + kXcds - 1) / kXcds;  // workgroups serving this queue
+  int q = blockIdx.x / kXcds;
+  while (q < ln + dn) {
     if (q < ln)
       list_item<D>(s, a, w, n_blocks, lb + q);
     else
       diag_item<D>(s, s_own, s_pos, s_ostart, s_mask, a, w, db + q - ln);
-    __syncthreads();  // s_item and the diagonal tile's row tables are rewritten by the next item
+    if (q == ln + dn - 1) break;  // the counter hands out items in order: none is left
+    // s_item and the diagonal tile's row tables are rewritten by the next item
+    __syncthreads();
+    if (threadIdx.x == 0) s_item = nper + atomicAdd(&w.totals[kQueue0 + x], 1);
+    __syncthreads();
+    q = s_item;
   }
 }
 
