@@ -52,7 +52,7 @@ constexpr int kTM = kQW * kWaves;        // queries per workgroup tile
 constexpr int kThreads = kWaves * kWave;
 constexpr int kScanThreads = 1024;
 constexpr int kHistThreads = 256;
-constexpr int kHistPairs = 512;        // (row, head) pairs per bucketing workgroup
+constexpr int kHistPairs = 256;        // (row, head) pairs per bucketing workgroup (one a thread)
 constexpr int kMaxHistWgs = 512;
 constexpr int64_t kHistCells = 1 << 21;  // bound on workgroups x lists
 constexpr int kMaxLists = 16384;      // LDS histogram bins (64 KiB)
@@ -78,12 +78,13 @@ struct BmWs {
 
 int64_t max_query_tiles(int64_t slots, int64_t n_lists) { return slots / kTM + n_lists + 1; }
 
-// Number of bucketing workgroups (ranges of (row, head) pairs).
+// Number of bucketing workgroups (ranges of (row, head) pairs), a multiple of
+// 4 so that a list's row of the histogram matrix is read in 16-byte pieces.
 int hist_wgs(int64_t pairs, int64_t n_lists) {
   int64_t w = (pairs + kHistPairs - 1) / kHistPairs;
   w = std::min<int64_t>(w, kMaxHistWgs);
   w = std::min<int64_t>(w, std::max<int64_t>(16, kHistCells / std::max<int64_t>(n_lists, 1)));
-  return (int)std::max<int64_t>(w, 1);
+  return (int)((std::max<int64_t>(w, 1) + 3) / 4 * 4);
 }
 
 template <bool CARVE>
@@ -261,14 +262,18 @@ __global__ __launch_bounds__(kHistThreads) void k_bm_fill(AttnKernelArgs a, Bloc
     int* s_cnt = s_bins + n_lists;  // list totals, then the list offsets
     const int n_hist = gridDim.x;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int bx = blockIdx.x;
     for (int l = threadIdx.x; l < n_lists; l += kHistThreads) {
-      const int32_t* h = hist + (int64_t)l * n_hist;
+      // n_hist is a multiple of 4; sixteen 16-byte loads in flight
+      const int4* h = reinterpret_cast<const int4*>(hist + (int64_t)l * n_hist);
       int tot = 0, pre = 0;
 #pragma unroll 16
-      for (int w = 0; w < n_hist; ++w) {
-        const int v = h[w];
-        tot += v;
-        pre += w < (int)blockIdx.x ? v : 0;
+      for (int w4 = 0; w4 < n_hist / 4; ++w4) {
+        const int4 v = h[w4];
+        const int w = 4 * w4;
+        tot += v.x + v.y + v.z + v.w;
+        pre += (w < bx ? v.x : 0) + (w + 1 < bx ? v.y : 0) + (w + 2 < bx ? v.z : 0) +
+               (w + 3 < bx ? v.w : 0);
       }
       s_cnt[l] = tot;
       s_bins[l] = pre;
