@@ -384,8 +384,13 @@ constexpr int kGateCols = 64;  // score cells per row and pass: 64 / RG block co
 // list over the row's own candidates (blocks of its sequence before its own
 // block) in a residue class of the columns, in ascending block order so that
 // ties keep the lower block, and the lists are merged by shuffles.
+// Four workgroups per CU (128 registers) for the common shapes, so that a
+// 32K-row shard's waves are resident at once; wider lists and rows get more.
+template <int D, int KMAX>
+constexpr int gate_wgs_per_cu() { return (D <= 128 && KMAX <= 4) ? 4 : 2; }
+
 template <int D, int KMAX, int RG>
-__global__ __launch_bounds__(kGateThreads) void k_moba_gate_mfma(
+__global__ __launch_bounds__(kGateThreads, (gate_wgs_per_cu<D, KMAX>())) void k_moba_gate_mfma(
     View q, DevLayout L, int hkv, int block_size, int topk, int n_blocks, BlockTable bt,
     const __bf16* __restrict__ mu_hi, const __bf16* __restrict__ mu_lo,
     int32_t* __restrict__ idx, float* __restrict__ score) {
@@ -474,23 +479,34 @@ __global__ __launch_bounds__(kGateThreads) void k_moba_gate_mfma(
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
     // lane part p takes the columns c = p (mod LPR) in increasing order: a
-    // per-lane top list, descending, ties to the earlier column
+    // per-lane top list, descending, ties to the earlier column.  The lane's
+    // 16 columns are read together and columns outside the row's candidates
+    // become -inf (they never enter the list), so the insertion runs without
+    // branches or waits between columns.
+    static_assert(PW == 16 * LPR, "16 columns per lane and pass");
     const int n = min(PW, col_hi - cb);
-    for (int c = part; c < n; c += LPR) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int c = part + LPR * j;
       const int b = cb + c;
-      if (b < first || b >= own) continue;
-      float cs = s_sc[wave][sr][c];
-      int cbk = b;
+      const float x = s_sc[wave][sr][c];
+      v[j] = (c < n && b >= first && b < own) ? x : -INFINITY;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (LPR * j >= n) break;  // wave-uniform: no lane has a column left
+      float cs = v[j];
+      int cbk = cb + part + LPR * j;
 #pragma unroll
       for (int t = 0; t < KMAX; ++t) {
-        if (t < topk && cs > best_s[t]) {
-          const float ts = best_s[t];
-          const int tb = best_b[t];
-          best_s[t] = cs;
-          best_b[t] = cbk;
-          cs = ts;
-          cbk = tb;
-        }
+        const bool take = t < topk && cs > best_s[t];
+        const float ts = best_s[t];
+        const int tb = best_b[t];
+        best_s[t] = take ? cs : ts;
+        best_b[t] = take ? cbk : tb;
+        cs = take ? ts : cs;
+        cbk = take ? tb : cbk;
       }
     }
     __builtin_amdgcn_wave_barrier();
