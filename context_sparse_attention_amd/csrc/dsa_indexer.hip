@@ -204,11 +204,14 @@ __global__ __launch_bounds__(kLgThreads, 2) void k_dsa_logits_mfma(View iq, View
           for (int mt = 0; mt < MT; ++mt)
             acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][ks], bq[ks % 3], acc[mt], 0, 0, 0);
         }
+        // ReLU as a signed max on the bit pattern: negative values and -0 become
+        // +0, others pass unchanged (one instruction; fmaxf adds a NaN-quieting one)
         float v = 0.f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) v = fmaf(wr[mt][j], fmaxf(acc[mt][j], 0.f), v);
+          for (int j = 0; j < 16; ++j)
+            v = fmaf(wr[mt][j], __int_as_float(max(__float_as_int(acc[mt][j]), 0)), v);
         v += __shfl_xor(v, 32, kWave);
         const int key = key0 + r;
         if (half == 0 && key >= lo && key <= hi && key < k_end)
