@@ -23,6 +23,8 @@ docstring.  Sources (by page title):
 * Megatron-LM PR #3674, "[1/2] Enable DSA CP, THD with absorbed MLA" - an
   indexer picks the top-k key tokens of each query; packed THD masking;
   absorbed MLA (value = latent part of the key, up-projection after attention).
+  The earlier PR description quoted on that page: the value up-projection is
+  applied after sparse attention (``mla.v_up_proj``).
 
 Parity status: every function here is pinned by a CPU test (tests/test_oracle_*),
 except the input-generation conventions, which belong to ``csa_inputs``.
@@ -42,6 +44,7 @@ from .attention import (
     finalize,
     merge_parts,
 )
+from .mla import v_up_proj
 
 __all__ = [
     "permitted_interval",
@@ -63,4 +66,5 @@ __all__ = [
     "merge",
     "finalize",
     "merge_parts",
+    "v_up_proj",
 ]
