@@ -353,6 +353,29 @@ def main():
                 "select_GBs": sel_bytes["total"] / (np.median(c_sel) * 1e-3) / 1e9,
                 "attention_TFLOPs": flops / (np.median(c_att) * 1e-3) / 1e12}
 
+    up_proj = None
+    if w.mode == "token" and w.v_alias:
+        # absorbed MLA: the value up-projection after the attention, on this step's
+        # latent output and a synthetic per-head weight (128 output channels); not
+        # part of the step, timed on its own over 20 launches
+        from csa_inputs import up_projection_inputs
+        o_lat = attend(select())[0]
+        w_up = torch.from_numpy(up_projection_inputs(1, w.hq, w.dv, 128)[1]).to(dev)
+        w_up = w_up.to(torch.bfloat16)
+        for _ in range(3):
+            csa.mla_v_up_proj(o_lat, w_up)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(20):
+            csa.mla_v_up_proj(o_lat, w_up)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        up_ms = e0.elapsed_time(e1) / 20
+        up_bytes = (o_lat.numel() + w_up.numel() + w.n_q * w.hq * 128) * 2
+        up_proj = {"kernel": "k_mla_v_up", "ms": up_ms, "alg_bytes": up_bytes,
+                   "GBs": up_bytes / (up_ms * 1e-3) / 1e9,
+                   "frac_hbm": up_bytes / (up_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
     att_med = float(np.median(att_ms))
     sel_med = float(np.median(sel_ms))
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
@@ -409,7 +432,7 @@ def main():
                                      "unit": sk_unit, "frac": sk_rate / sk_peak},
                    "kernels_ms": {k: float(np.mean(v)) for k, v in kern.items()},
                    "eager_ms_per_step": eager_ms_per_step, "graph": graph,
-                   "cold": cold},
+                   "cold": cold, "v_up_proj": up_proj},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -15,6 +15,7 @@ from ._binding import (
     dsa_indexer_topk,
     sparse_attn_fwd_shard,
     summary_merge,
+    mla_v_up_proj,
     trace_begin,
     trace_collect,
     library_path,
@@ -30,6 +31,7 @@ __all__ = [
     "dsa_indexer_topk",
     "sparse_attn_fwd_shard",
     "summary_merge",
+    "mla_v_up_proj",
     "trace_begin",
     "trace_collect",
     "library_path",

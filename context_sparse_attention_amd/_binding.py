@@ -69,6 +69,8 @@ lib.csa_trace_collect.argtypes = [ctypes.POINTER(ctypes.c_float),
                                   ctypes.POINTER(ctypes.c_char_p), ctypes.c_int]
 lib.summary_merge.restype = ctypes.c_int
 lib.summary_merge.argtypes = [_i32, _i64, _i32, _P, _P, _P, _P, _P, _P, _P, _i32, _P, _P]
+lib.mla_v_up_proj.restype = ctypes.c_int
+lib.mla_v_up_proj.argtypes = [_T3, _T3, _P, _i32, _P]
 
 
 def _check(status):
@@ -208,6 +210,15 @@ def summary_merge(m, l, z, finalize=True, merged=False, o_dtype=torch.float32):
                              CSA_BF16 if o_dtype == torch.bfloat16 else CSA_F32, _ptr(lse),
                              _stream()))
     return res
+
+
+def mla_v_up_proj(o, w, out_dtype=None):
+    """out [n_q, Hq, Dv] = per head o [n_q, Hq, Dl] @ w[h]^T, w [Hq, Dv, Dl] (bf16)."""
+    out_dtype = out_dtype or o.dtype
+    out = torch.empty((o.shape[0], o.shape[1], w.shape[1]), dtype=out_dtype, device=o.device)
+    _check(lib.mla_v_up_proj(ctypes.byref(_tensor3(o)), ctypes.byref(_tensor3(w)),
+                             out.data_ptr(), _dtype_code(out), _stream()))
+    return out
 
 
 def trace_begin(max_records):

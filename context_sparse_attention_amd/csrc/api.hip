@@ -342,4 +342,37 @@ csa_status summary_merge(int32_t n_parts, int64_t n_rows, int32_t dv, const floa
   });
 }
 
+csa_status mla_v_up_proj(const csa_tensor3* o, const csa_tensor3* w, void* out,
+                         int32_t out_dtype, void* stream) {
+  return guarded([&]() -> csa_status {
+    csa_status st;
+    if ((st = check_tensor(o, "o")) || (st = check_tensor(w, "w"))) return st;
+    if (o->dtype != CSA_BF16 || w->dtype != CSA_BF16)
+      return fail(CSA_ERR_UNSUPPORTED, "o and w must be bf16");
+    if (w->n != o->h)
+      return fail(CSA_ERR_INVALID_ARG, "w has %lld heads, o has %d", (long long)w->n, o->h);
+    if (w->d != o->d)
+      return fail(CSA_ERR_INVALID_ARG, "w latent width %d != o width %d", w->d, o->d);
+    if (o->d % 64 || o->d > 8192)
+      return fail(CSA_ERR_UNSUPPORTED, "latent width %d (a multiple of 64, at most 8192)", o->d);
+    if (o->stride_n * 2 * 128 >= ((int64_t)1 << 32))
+      return fail(CSA_ERR_UNSUPPORTED, "o: row stride %lld too large", (long long)o->stride_n);
+    if (w->h % 32 || w->h > 128)
+      return fail(CSA_ERR_UNSUPPORTED, "output width %d (32, 64, 96 or 128)", w->h);
+    if (out_dtype != CSA_F32 && out_dtype != CSA_BF16)
+      return fail(CSA_ERR_INVALID_ARG, "out_dtype %d", out_dtype);
+    if (o->n > 0 && !out) return fail(CSA_ERR_INVALID_ARG, "out: null");
+    if (out && !aligned16(out)) return fail(CSA_ERR_INVALID_ARG, "out: not 16-byte aligned");
+    MlaUpArgs a;
+    a.o = make_view(o);
+    a.w = make_view(w);
+    a.n_q = (int)o->n;
+    a.out = out;
+    a.out_dtype = out_dtype;
+    hipError_t e = launch_mla_v_up_proj(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "mla_v_up_proj");
+    return CSA_OK;
+  });
+}
+
 }  // extern "C"

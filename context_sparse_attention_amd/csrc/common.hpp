@@ -198,4 +198,13 @@ struct MergeArgs {
 };
 hipError_t launch_summary_merge(const MergeArgs& a, hipStream_t stream);
 
+struct MlaUpArgs {
+  View o;  // [n_q, Hq, Dl] bf16
+  View w;  // [Hq, Dv, Dl] bf16 (n = head, h = output channel, d = latent channel)
+  int n_q;
+  void* out;  // [n_q, Hq, Dv] contiguous
+  int out_dtype;
+};
+hipError_t launch_mla_v_up_proj(const MlaUpArgs& a, hipStream_t stream);
+
 }  // namespace csa

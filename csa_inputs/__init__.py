@@ -29,6 +29,7 @@ from .workloads import (
     make_workload,
     tiny_block_workload,
     tiny_token_workload,
+    up_projection_inputs,
     WORKLOAD_NAMES,
 )
 
@@ -42,5 +43,6 @@ __all__ = [
     "make_workload",
     "tiny_block_workload",
     "tiny_token_workload",
+    "up_projection_inputs",
     "WORKLOAD_NAMES",
 ]

@@ -244,3 +244,17 @@ def tiny_token_workload(seed=0, lengths=(48, 16), positions=None, hq=4, dqk=12, 
         positions = np.arange(total, dtype=np.int32)
     return _token_workload(f"tiny_token_{seed}", seed, dtype, list(lengths),
                            np.asarray(positions, np.int32), hq, dqk, dv, hi, di, topk)
+
+
+def up_projection_inputs(n_q, hq, dl, dv, seed=11):
+    """Inputs of the absorbed-MLA value up-projection, as exact bf16 values in float32.
+
+    o [n_q, hq, dl]: stands in for the latent attention output, a convex
+    combination of latent value rows drawn N(0, 1), so N(0, 1) entries scaled by
+    1/2; w [hq, dv, dl]: each head's up-projection (linear-layer layout, rows =
+    output channels), N(0, 1/dl) as at initialisation.
+    """
+    rng = np.random.default_rng(seed)
+    o = bf16_round(0.5 * rng.standard_normal(size=(n_q, hq, dl), dtype=np.float32))
+    w = bf16_round(rng.standard_normal(size=(hq, dv, dl), dtype=np.float32) / np.float32(np.sqrt(dl)))
+    return o, w

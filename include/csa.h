@@ -207,6 +207,28 @@ csa_status summary_merge(int32_t n_parts, int64_t n_rows, int32_t dv, const floa
                          void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * mla_v_up_proj - absorbed-MLA value up-projection after the sparse attention
+ * [MLM#3674, the earlier PR description quoted on that page: with matrix
+ * absorption the value up-projection is applied after sparse attention; the
+ * review summary's sequence diagram: an einsum with up_v_weight after the
+ * sparse attention gives [sq, b, np, v_channels]].
+ *
+ *   out[i, h, d] = sum_c o[i, h, c] * w[h, d, c]
+ *
+ *  o    [n_q, Hq, Dl] bf16: the latent attention output (sparse_attn_fwd_shard's
+ *       out with the latent part of the key as the value).  Dl a multiple of 64,
+ *       at most 8192; 128 rows span less than 4 GiB.
+ *  w    bf16, head h's up-projection as a linear layer's weight: row d holds
+ *       the Dl latent weights of output channel d.  Passed as a csa_tensor3
+ *       with n = Hq, h = Dv, d = Dl.  Dv is 32, 64, 96 or 128.
+ *  out  [n_q, Hq, Dv] in out_dtype (CSA_BF16 or CSA_F32), contiguous, 16-byte
+ *       aligned, written.
+ *  fp32 accumulation of exact bf16 products; deterministic.  No workspace.
+ * ------------------------------------------------------------------------------- */
+csa_status mla_v_up_proj(const csa_tensor3* o, const csa_tensor3* w, void* out,
+                         int32_t out_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Tracing (host-side, for profiling; not needed for computing).
  *
  * csa_trace_begin(n) allocates n HIP event pairs and turns tracing on

@@ -28,7 +28,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert {"moba_gate_topk", "dsa_indexer_topk", "sparse_attn_fwd_shard", "summary_merge",
-            "csa_last_error"} <= set(names)
+            "mla_v_up_proj", "csa_last_error"} <= set(names)
     for name in names:
         assert hasattr(B.lib, name), f"{name} missing from libcsa.so"
 
@@ -137,3 +137,19 @@ def test_indexer_rejects_bad_arguments():
     assert call(ik_=t3(1024, 2, 128))[0] == 1
     assert call(iq_=t3(16, 64, 256), ik_=t3(1024, 1, 256))[0] == 2
     assert call(w_stride=10)[0] == 1
+
+
+def test_up_projection_rejects_bad_arguments():
+    def call(o=None, w=None, out=1 << 20, out_dtype=1):
+        o = o or t3(64, 8, 512)
+        w = w or t3(8, 128, 512)
+        st = B.lib.mla_v_up_proj(ctypes.byref(o), ctypes.byref(w), out, out_dtype, None)
+        return st, B.lib.csa_last_error().decode()
+
+    assert call(w=t3(4, 128, 512))[0] == 1           # head counts differ
+    assert call(w=t3(8, 128, 256))[0] == 1           # latent widths differ
+    assert call(w=t3(8, 48, 512))[0] == 2            # output width not a multiple of 32
+    assert call(o=t3(64, 8, 544), w=t3(8, 128, 544))[0] == 2  # latent width not a multiple of 64
+    assert call(out_dtype=7)[0] == 1
+    assert call(out=None)[0] == 1
+    assert call(out=(1 << 20) + 8)[0] == 1           # misaligned output
