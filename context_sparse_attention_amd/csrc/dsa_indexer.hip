@@ -89,7 +89,7 @@ constexpr int kLgChunk = 2048;              // keys per workgroup
 
 // bf16 indexer logits on the matrix cores.  Wave w owns query token
 // t0 + w: its H_I x D_I indexer queries sit in registers as the A operand
-// (rows = heads), each 64-key ik tile is staged once in LDS for the eight
+// (rows = heads), each 64-key ik tile is staged once in LDS for the four
 // tokens of the workgroup and read as the B operand (columns = keys), so the
 // 32x32 accumulator gives a lane one key column and 16 heads per M tile; the
 // ReLU and head weights are applied in-lane and the two lane halves are added.
