@@ -91,3 +91,33 @@ def test_up_projection_dsa_shape_sampled_rows():
     rows = np.sort(np.random.default_rng(5).choice(n_q, 96, replace=False))
     rows = np.concatenate([[0, 127, 128, n_q - 1], rows])
     _check(o_np, w_np, out, torch.bfloat16, rows)
+
+
+def test_absorbed_path_end_to_end():
+    # indexer -> latent attention (value = the first dv key columns) -> up-projection,
+    # against the oracle attending, on the GPU's own selection, over each head's
+    # up-projected values (the softmax weights do not depend on the values)
+    from csa_inputs import tiny_token_workload
+    _say("absorbed path end to end")
+    t = tiny_token_workload(seed=31, lengths=(320,), hq=16, dqk=128, dv=64, hi=4, di=32,
+                            topk=40, dtype="bf16")
+    lay = csa.Layout(t.q_pos, t.q_seq, t.cu_seqlens)
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda().to(torch.bfloat16)
+
+    q, k = dev(t.q), dev(t.k)
+    iq, ik = dev(t.iq), dev(t.ik)
+    idx = csa.dsa_indexer_topk(iq, ik, torch.from_numpy(t.w).cuda(), lay, t.topk)
+    o_lat, _ = csa.sparse_attn_fwd_shard(q, k, k[..., : t.dv], lay, csa.CSA_SEL_TOKEN, idx,
+                                         softmax_scale=t.scale, out_dtype=torch.float32)
+    _, w_np = up_projection_inputs(1, t.hq, t.dv, 32, seed=32)
+    up = csa.mla_v_up_proj(o_lat.to(torch.bfloat16), dev(w_np), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    k_rep = np.repeat(t.k, t.hq, axis=1)
+    v_proj = np.einsum("jc,hdc->jhd", t.value[:, 0, :].astype(np.float64), w_np)
+    ref, _ = oracle.shard_forward(t.q, k_rep, v_proj, t.q_pos, t.q_seq, t.cu_seqlens, "token",
+                                  idx_np[:, None, :], t.scale)
+    err = np.abs(up.cpu().numpy() - ref).max()
+    assert err <= 2e-2, f"max abs error {err:.3e}"
