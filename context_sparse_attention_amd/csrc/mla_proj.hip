@@ -121,9 +121,36 @@ __global__ __launch_bounds__(kUpWaves * kWave) void k_mla_v_up(View o, View w, i
     wait_gathers();
     __syncthreads();  // the next slice has landed; this buffer is free again
   }
+  const int dv = NM * 32;
+  if constexpr (sizeof(TO) == 2) {
+    // bf16: the wave's 32 output rows go through its own part of the (now
+    // free) slice buffer, then out as whole rows, 16 bytes a lane: stores of 8
+    // bytes spread over a row made the L2 fetch the lines they partly wrote
+    constexpr int kRowB = NM * 64 + 16;  // staged row pitch in bytes (padded)
+    static_assert(kUpWaves * 32 * kRowB <= 2 * kUpRows * kUpPitch * 16, "staging fits");
+    char* st = &s_o[0][0] + wave * 32 * kRowB;
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const bf16x4 x = {(__bf16)acc[mt][4 * jj], (__bf16)acc[mt][4 * jj + 1],
+                          (__bf16)acc[mt][4 * jj + 2], (__bf16)acc[mt][4 * jj + 3]};
+        *reinterpret_cast<bf16x4*>(st + (lane & 31) * kRowB + (mt * 32 + 8 * jj + 4 * half) * 2) = x;
+      }
+    constexpr int kUnits = NM * 4;  // 16-byte units per output row
+#pragma unroll
+    for (int i = 0; i < 32 * kUnits / kWave; ++i) {
+      const int e = i * kWave + lane;
+      const int r = e / kUnits, un = e % kUnits;
+      const int row = rw + wave * 32 + r;
+      if (row < n_q)
+        *reinterpret_cast<uint4*>(out + ((int64_t)row * hq + h) * dv + un * 8) =
+            *reinterpret_cast<const uint4*>(st + r * kRowB + un * 16);
+    }
+    return;
+  }
   const int row = rw + wave * 32 + (lane & 31);
   if (row >= n_q) return;
-  const int dv = NM * 32;
   TO* op = out + ((int64_t)row * hq + h) * dv + 4 * half;
   // lane holds output channels mt * 32 + 8 jj + 4 half + (0..3) of its row
 #pragma unroll
