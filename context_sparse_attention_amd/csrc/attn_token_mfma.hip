@@ -299,6 +299,40 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_tok_attn(AttnKernelArgs a) {
 
   fence_a(o);
   const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (a.lse && half == 0)
+    a.lse[(int64_t)i * a.q.h + head] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  // bf16: the wave's 32 heads are 32 consecutive output rows.  Where the key
+  // tiles are large enough, they go through the wave's part of that (now free)
+  // buffer, at most 256 columns at a time, and out as whole row pieces, 16 bytes
+  // a lane, where 8-byte stores would spread each row over many instructions.
+  constexpr int kPart = DV > 256 ? 256 : DV;
+  constexpr int kRowB = kPart * 2 + 16;  // staged row pitch in bytes (padded)
+  constexpr bool kStage = sizeof(TO) == 2 && NW * 32 * kRowB <= (int)sizeof(s.k);
+  if constexpr (kStage) {
+    constexpr int kUnits = kPart / 8;  // 16-byte units of a row piece
+    char* st = reinterpret_cast<char*>(&s.k[0][0]) + wave * 32 * kRowB;
+    __bf16* wout = reinterpret_cast<__bf16*>(a.out) +
+                   ((int64_t)i * a.q.h + g * G + wave * 32) * DV;
+#pragma unroll
+    for (int pc = 0; pc < DV / kPart; ++pc) {
+#pragma unroll
+      for (int dt = pc * kPart / 32; dt < (pc + 1) * kPart / 32; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const bf16x4 x = {(__bf16)(o[dt][4 * jj] * inv), (__bf16)(o[dt][4 * jj + 1] * inv),
+                            (__bf16)(o[dt][4 * jj + 2] * inv), (__bf16)(o[dt][4 * jj + 3] * inv)};
+          *reinterpret_cast<bf16x4*>(st + (lane & 31) * kRowB +
+                                     (dt * 32 + 8 * jj + 4 * half - pc * kPart) * 2) = x;
+        }
+#pragma unroll
+      for (int e0 = 0; e0 < 32 * kUnits; e0 += kWave) {
+        const int r = (e0 + lane) / kUnits, un = (e0 + lane) % kUnits;
+        *reinterpret_cast<uint4*>(wout + (int64_t)r * DV + pc * kPart + un * 8) =
+            *reinterpret_cast<const uint4*>(st + r * kRowB + un * 16);
+      }
+    }
+    return;
+  }
   TO* out = reinterpret_cast<TO*>(a.out) + ((int64_t)i * a.q.h + head) * DV;
 #pragma unroll
   for (int dt = 0; dt < DV / 32; ++dt)
@@ -315,8 +349,6 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_tok_attn(AttnKernelArgs a) {
         *reinterpret_cast<bf16x4*>(out + d) = x;
       }
     }
-  if (a.lse && half == 0)
-    a.lse[(int64_t)i * a.q.h + head] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
 }
 
 template <int DQK, int DV, bool ALIAS, typename TO>
