@@ -733,21 +733,41 @@ __device__ inline void store4(__bf16* p, float a, float b, float c, float d) {
   *reinterpret_cast<bf16x4*>(p) = x;
 }
 
-// Writes this lane's half of a chunk summary: (m, l) and the normalized output
-// z / l in bf16.  Every summary written has l >= 1: the key that set the
-// reference maximum contributes 2^0.
+// Writes the chunk summaries of the wave's 32 (row, head) slots, for the lanes
+// with `ok`: (m, l) and the normalized output z / l in bf16.  Every summary
+// written has l >= 1: the key that set the reference maximum contributes 2^0.
+// The output rows go through the wave's part of the key tiles (free here: every
+// key loop ends with a barrier, and the next item's gathers start after
+// another) and out as whole rows, 16 bytes a lane, where 8-byte stores spread
+// over each row would leave the L2 with partly written lines.  Called by every
+// lane of the wave.
 template <int D>
-__device__ __forceinline__ void write_summary(const BmWs& w, int64_t p, const WaveState<D>& st,
-                                              int half) {
-  if (half == 0) w.part_ml[p] = make_float2(st.m, st.l);
-  const float inv = 1.f / st.l;
-  __bf16* o = w.part_o + p * D;
+__device__ __forceinline__ void write_summary(Lds<D>& s, const BmWs& w, int64_t p, bool ok,
+                                              const WaveState<D>& st, int lane, int wave) {
+  const int half = lane >> 5;
+  if (ok && half == 0) w.part_ml[p] = make_float2(st.m, st.l);
+  const float inv = ok ? 1.f / st.l : 0.f;
+  constexpr int kRowB = 2 * D + 16;  // staged row pitch in bytes (padded)
+  constexpr int kUnits = D / 8;      // 16-byte units of a row
+  static_assert(kWaves * kQW * kRowB <= (int)sizeof(s.k), "staging fits in the key tiles");
+  char* stg = reinterpret_cast<char*>(&s.k[0][0]) + wave * kQW * kRowB;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      store4(o + dt * 32 + 8 * jj + 4 * half, st.o[dt][4 * jj] * inv, st.o[dt][4 * jj + 1] * inv,
-             st.o[dt][4 * jj + 2] * inv, st.o[dt][4 * jj + 3] * inv);
+    for (int jj = 0; jj < 4; ++jj) {
+      const bf16x4 x = {(__bf16)(st.o[dt][4 * jj] * inv), (__bf16)(st.o[dt][4 * jj + 1] * inv),
+                        (__bf16)(st.o[dt][4 * jj + 2] * inv), (__bf16)(st.o[dt][4 * jj + 3] * inv)};
+      *reinterpret_cast<bf16x4*>(stg + (lane & 31) * kRowB + (dt * 32 + 8 * jj + 4 * half) * 2) = x;
+    }
+#pragma unroll
+  for (int e0 = 0; e0 < kQW * kUnits; e0 += kWave) {
+    const int r = (e0 + lane) / kUnits, un = (e0 + lane) % kUnits;
+    const int64_t pr = __shfl(p, r, kWave);
+    const int okr = __shfl((int)ok, r, kWave);
+    if (okr)
+      *reinterpret_cast<uint4*>(w.part_o + pr * D + un * 8) =
+          *reinterpret_cast<const uint4*>(stg + r * kRowB + un * 16);
+  }
 }
 
 template <int D>
@@ -785,7 +805,7 @@ __device__ __forceinline__ void list_item(Lds<D>& s, const AttnKernelArgs& a, co
   reset(st);
   const int2 b = w.bt.blocks[blk];
   run_keys<D, false>(s, a.k, a.v, g, b.x, b.y, wave * kQW < cnt, qf, a.scale_log2, st, 0, 0);
-  if (valid) write_summary<D>(w, p, st, half);
+  write_summary<D>(s, w, p, valid, st, lane, wave);
 }
 
 // Diagonal tile: TR = kTM / G consecutive rows x the G query heads of one key
@@ -888,8 +908,8 @@ __device__ __forceinline__ void diag_item(Lds<D>& s, int* s_own, int* s_pos, int
     }
     start = end;
   }
-  if (has_keys && own_slot >= 0)
-    write_summary<D>(w, (int64_t)pair * a.idx_width + own_slot, st, half);
+  write_summary<D>(s, w, (int64_t)pair * a.idx_width + own_slot, has_keys && own_slot >= 0, st,
+                   lane, wave);
 }
 
 // One persistent kernel for both kinds of chunk: workgroup b runs on XCD
