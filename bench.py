@@ -306,9 +306,13 @@ def main():
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     csa.trace_begin(4 * args.steps + 8)
     torch.cuda.synchronize()
-    # a ~10 ms spin on the stream first, so that the host has queued every step
-    # before the GPU reaches it: the traced kernel times then hold no launch gaps
-    torch.cuda._sleep(int(2e7))
+    # about 20 ms of HBM copies on the stream first, so that the host has queued
+    # every step before the GPU reaches it: the traced kernel times then hold no
+    # launch gaps.  Copies keep the clocks where the steps left them; a spin
+    # kernel let them drop, and the first traced kernels ran up to 15% slower.
+    fill = torch.empty((2, 1 << 28), dtype=torch.uint8, device="cuda")
+    for _ in range(200):
+        fill[1].copy_(fill[0])
     for s in range(args.steps):
         ev[s][0].record(stream)
         idx = select()
