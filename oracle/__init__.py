@@ -30,14 +30,17 @@ Parity status: every function here is pinned by a CPU test (tests/test_oracle_*)
 except the input-generation conventions, which belong to ``csa_inputs``.
 """
 
-from .layout import permitted_interval, row_intervals
+from .layout import permitted_interval
 from .moba import stream_blocks, pool_blocks, gate_candidates, gate_scores, select_blocks
 from .dsa import indexer_logits_row, select_tokens_row, indexer_topk
 from .attention import (
     NEUTRAL_M,
+    slot_span,
     slot_keys,
     selected_keys,
     attend,
+    attend_heads,
+    attend_spans,
     shard_forward,
     summary,
     merge,
@@ -48,7 +51,6 @@ from .mla import v_up_proj
 
 __all__ = [
     "permitted_interval",
-    "row_intervals",
     "stream_blocks",
     "pool_blocks",
     "gate_candidates",
@@ -58,9 +60,12 @@ __all__ = [
     "select_tokens_row",
     "indexer_topk",
     "NEUTRAL_M",
+    "slot_span",
     "slot_keys",
     "selected_keys",
     "attend",
+    "attend_heads",
+    "attend_spans",
     "shard_forward",
     "summary",
     "merge",

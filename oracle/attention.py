@@ -17,7 +17,8 @@ permitted key gets output 0 and log-sum-exp -inf; m and the log-sum-exp are in
 natural-log units; logits are x = scale * (q . k).
 
 Since merging summaries reaches exactly the softmax over the selected permitted
-keys, ``attend`` computes that softmax directly from its definition.
+keys, ``attend`` / ``attend_spans`` / ``attend_heads`` compute that softmax
+directly from its definition (one maximum over all selected keys, one sum).
 
 The selected key set of a (row, head) is the multiset union, over the slots of
 its index row, of each slot's permitted keys:
@@ -38,16 +39,26 @@ from .layout import permitted_interval
 NEUTRAL_M = -np.inf
 
 
-def slot_keys(mode, s, lo, hi_incl, seq_end, block_size=0):
-    """Global key positions contributed by one index slot."""
+def slot_span(mode, s, lo, hi_incl, seq_end, block_size=0):
+    """Keys contributed by one index slot, as the range [a, b) (empty when a == b).
+
+    A slot's keys are always consecutive: one token, or one block cut to the
+    row's permitted keys.
+    """
     s = int(s)
     if s < lo or s > hi_incl:
-        return np.zeros(0, np.int64)
+        return s, s
     if mode == "token":
-        return np.array([s], np.int64)
+        return s, s + 1
     if (s - lo) % block_size:
-        return np.zeros(0, np.int64)
-    return np.arange(s, min(s + block_size, seq_end, hi_incl + 1), dtype=np.int64)
+        return s, s
+    return s, min(s + block_size, seq_end, hi_incl + 1)
+
+
+def slot_keys(mode, s, lo, hi_incl, seq_end, block_size=0):
+    """Global key positions contributed by one index slot."""
+    a, b = slot_span(mode, s, lo, hi_incl, seq_end, block_size)
+    return np.arange(a, b, dtype=np.int64)
 
 
 def selected_keys(mode, slots, interval, block_size=0):
@@ -63,12 +74,56 @@ def attend(qv, kmat, vmat, scale):
     """Softmax attention of one query over the given keys: (o [dv], lse)."""
     if kmat.shape[0] == 0:
         return np.zeros(vmat.shape[1]), -np.inf
-    x = scale * (kmat.astype(np.float64) @ qv.astype(np.float64))
+    x = scale * (np.asarray(kmat, np.float64) @ np.asarray(qv, np.float64))
     m = x.max()
     e = np.exp(x - m)
     ell = e.sum()
-    o = (e @ vmat.astype(np.float64)) / ell
+    o = (e @ np.asarray(vmat, np.float64)) / ell
     return o, m + np.log(ell)
+
+
+def attend_heads(qmat, kmat, vmat, scale):
+    """Softmax attention of several queries over one shared key set.
+
+    qmat [nh, Dqk]; returns (o [nh, Dv], lse [nh]).  Each query's softmax is the
+    same definition as ``attend``; the logits of all queries are one matrix
+    product.  Used where every query head of a row reads the same selection
+    (one token-index row per query token).
+    """
+    nh = qmat.shape[0]
+    if kmat.shape[0] == 0:
+        return np.zeros((nh, vmat.shape[1])), np.full(nh, -np.inf)
+    x = scale * (np.asarray(qmat, np.float64) @ np.asarray(kmat, np.float64).T)  # [nh, n]
+    m = x.max(axis=1)
+    e = np.exp(x - m[:, None])
+    ell = e.sum(axis=1)
+    o = (e @ np.asarray(vmat, np.float64)) / ell[:, None]
+    return o, m + np.log(ell)
+
+
+def attend_spans(qv, kg, vg, spans, scale):
+    """Softmax attention of one query over the keys of ``spans`` (slot order).
+
+    kg [n_kv, Dqk] and vg [n_kv, Dv] are one key head's keys and values; the
+    selected keys are the multiset union of the ranges [a, b) in ``spans``.
+    The same definition as ``attend``, with the keys read slot by slot instead
+    of gathered: logits of every selected key, their one maximum M, then
+    l = sum_j exp(x_j - M) and o = sum_j exp(x_j - M) v_j / l, the sums taken
+    slot by slot, key by key.  Returns (o [Dv], lse).
+    """
+    spans = [(a, b) for a, b in spans if b > a]
+    if not spans:
+        return np.zeros(vg.shape[1]), -np.inf
+    qv = np.asarray(qv, np.float64)
+    x = [scale * (np.asarray(kg[a:b], np.float64) @ qv) for a, b in spans]
+    m = max(xs.max() for xs in x)
+    e = [np.exp(xs - m) for xs in x]
+    ell = 0.0
+    o = np.zeros(vg.shape[1])
+    for es, (a, b) in zip(e, spans):
+        ell += es.sum()
+        o += es @ np.asarray(vg[a:b], np.float64)
+    return o / ell, m + np.log(ell)
 
 
 def shard_forward(q, k, v, q_pos, q_seq, cu_seqlens, mode, idx, scale, block_size=0,
@@ -88,11 +143,19 @@ def shard_forward(q, k, v, q_pos, q_seq, cu_seqlens, mode, idx, scale, block_siz
     lse = np.full((len(rows), hq), -np.inf)
     for r, i in enumerate(rows):
         iv = permitted_interval(int(q_pos[i]), int(q_seq[i]), cu_seqlens)
+        if idx.shape[1] == 1:
+            # one selection for the whole row: gather its keys once per key head
+            keys = selected_keys(mode, idx[i, 0], iv, block_size)
+            for g in range(hkv):
+                heads = slice(g * group, (g + 1) * group)
+                out[r, heads], lse[r, heads] = attend_heads(q[i, heads], k[keys, g],
+                                                            v[keys, g], scale)
+            continue
         for h in range(hq):
-            slots = idx[i, 0 if idx.shape[1] == 1 else h]
-            keys = selected_keys(mode, slots, iv, block_size)
             g = h // group
-            out[r, h], lse[r, h] = attend(q[i, h], k[keys, g], v[keys, g], scale)
+            spans = [] if iv is None else [slot_span(mode, sl, *iv, block_size)
+                                           for sl in idx[i, h]]
+            out[r, h], lse[r, h] = attend_spans(q[i, h], k[:, g], v[:, g], spans, scale)
     return out, lse
 
 

@@ -24,7 +24,3 @@ def permitted_interval(pos, seq, cu_seqlens):
         return None
     return lo, int(pos), end
 
-
-def row_intervals(q_pos, q_seq, cu_seqlens):
-    """Per-row permitted intervals; None for rows with no permitted keys."""
-    return [permitted_interval(int(p), int(s), cu_seqlens) for p, s in zip(q_pos, q_seq)]

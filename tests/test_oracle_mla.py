@@ -73,4 +73,6 @@ def test_after_attention_equals_attention_over_projected_values():
     v_proj = np.einsum("jc,hdc->jhd", c[:, 0, :], w)
     direct, lse_b = oracle.shard_forward(q, k_rep, v_proj, q_pos, q_seq, cu, "token", idx, scale)
     np.testing.assert_allclose(up, direct, rtol=1e-11, atol=1e-12)
-    np.testing.assert_array_equal(lse_a, lse_b)
+    # the two runs group the heads differently (one key head against three), so
+    # their fp64 logits are summed in different orders
+    np.testing.assert_allclose(lse_a, lse_b, rtol=1e-14, atol=1e-14)
