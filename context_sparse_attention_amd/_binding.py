@@ -131,39 +131,66 @@ def _workspace(nbytes, device):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def moba_gate_topk(q, k, layout, block_size, topk, return_score=False):
-    """idx [n_q, Hq, topk+1] int32 (block start positions), optionally the gate scores."""
+def _given(t, shape, dtype, dev, name):
+    """A caller-supplied output tensor, checked for shape, dtype, device and contiguity."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != dev or \
+            not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous {dtype} tensor of shape "
+                         f"{tuple(shape)} on {dev}")
+    return t
+
+
+def _out(t, shape, dtype, dev, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    return _given(t, shape, dtype, dev, name)
+
+
+def moba_gate_topk(q, k, layout, block_size, topk, return_score=False, idx=None,
+                   score=None):
+    """idx [n_q, Hq, topk+1] int32 (block start positions), optionally the gate scores.
+
+    ``idx`` / ``score`` may be given as preallocated outputs (every element is written).
+    """
     dev = q.device
-    idx = torch.empty((layout.n_q, q.shape[1], topk + 1), dtype=torch.int32, device=dev)
-    score = torch.empty(idx.shape, dtype=torch.float32, device=dev) if return_score else None
+    shape = (layout.n_q, q.shape[1], topk + 1)
+    idx = _out(idx, shape, torch.int32, dev, "idx")
+    if return_score or score is not None:
+        score = _out(score, shape, torch.float32, dev, "score")
     ws_bytes = lib.moba_gate_topk_workspace_size(layout.c, k.shape[1], k.shape[2], block_size)
     ws = _workspace(ws_bytes, dev)
     _check(lib.moba_gate_topk(ctypes.byref(_tensor3(q)), ctypes.byref(_tensor3(k)), layout.c,
                               block_size, topk, idx.data_ptr(), _ptr(score), ws.data_ptr(),
                               ws.numel(), _stream()))
-    return (idx, score) if return_score else idx
+    return (idx, score) if (return_score or score is not None) else idx
 
 
-def dsa_indexer_topk(iq, ik, w, layout, topk, return_score=False):
-    """idx [n_q, topk] int32 (key positions), optionally the selected logits."""
+def dsa_indexer_topk(iq, ik, w, layout, topk, return_score=False, idx=None, score=None):
+    """idx [n_q, topk] int32 (key positions), optionally the selected logits.
+
+    ``idx`` / ``score`` may be given as preallocated outputs (every element is written).
+    """
     dev = iq.device
     if w.dtype != torch.float32 or w.stride(1) != 1:
         raise ValueError("w must be float32 with a contiguous head dimension")
-    idx = torch.empty((layout.n_q, topk), dtype=torch.int32, device=dev)
-    score = torch.empty(idx.shape, dtype=torch.float32, device=dev) if return_score else None
+    shape = (layout.n_q, topk)
+    idx = _out(idx, shape, torch.int32, dev, "idx")
+    if return_score or score is not None:
+        score = _out(score, shape, torch.float32, dev, "score")
     ws_bytes = lib.dsa_indexer_topk_workspace_size(layout.c, topk)
     ws = _workspace(ws_bytes, dev)
     _check(lib.dsa_indexer_topk(ctypes.byref(_tensor3(iq)), ctypes.byref(_tensor3(ik)),
                                 w.data_ptr(), w.stride(0), layout.c, topk, idx.data_ptr(),
                                 _ptr(score), ws.data_ptr(), ws.numel(), _stream()))
-    return (idx, score) if return_score else idx
+    return (idx, score) if (return_score or score is not None) else idx
 
 
 def sparse_attn_fwd_shard(q, k, v, layout, mode, idx, block_size=0, softmax_scale=None,
-                          out_dtype=None, return_lse=True):
+                          out_dtype=None, return_lse=True, out=None, lse=None):
     """out [n_q, Hq, Dv] (and lse [n_q, Hq]) of the shard's rows over their selected chunks.
 
     ``idx`` is [n_q, idx_heads, W] (or [n_q, W] for idx_heads = 1), int32, contiguous.
+    ``out`` / ``lse`` may be given as preallocated outputs (every element is written).
     """
     dev = q.device
     if idx.dim() == 2:
@@ -172,10 +199,13 @@ def sparse_attn_fwd_shard(q, k, v, layout, mode, idx, block_size=0, softmax_scal
         raise ValueError("idx must be a contiguous int32 tensor")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(q.shape[2])
-    out_dtype = out_dtype or q.dtype
     hq, dv = q.shape[1], v.shape[2]
-    out = torch.empty((layout.n_q, hq, dv), dtype=out_dtype, device=dev)
-    lse = torch.empty((layout.n_q, hq), dtype=torch.float32, device=dev) if return_lse else None
+    if out is not None:
+        out_dtype = out.dtype
+    out_dtype = out_dtype or q.dtype
+    out = _out(out, (layout.n_q, hq, dv), out_dtype, dev, "out")
+    if return_lse or lse is not None:
+        lse = _out(lse, (layout.n_q, hq), torch.float32, dev, "lse")
     ws_bytes = lib.sparse_attn_fwd_shard_workspace_size(layout.c, mode, hq, k.shape[1], dv,
                                                         idx.shape[2], block_size)
     ws = _workspace(ws_bytes, dev)
@@ -184,7 +214,7 @@ def sparse_attn_fwd_shard(q, k, v, layout, mode, idx, block_size=0, softmax_scal
                                      idx.shape[1], idx.shape[2], block_size,
                                      float(softmax_scale), out.data_ptr(), _dtype_code(out),
                                      _ptr(lse), ws.data_ptr(), ws.numel(), _stream()))
-    return (out, lse) if return_lse else out
+    return (out, lse) if (return_lse or lse is not None) else out
 
 
 def summary_merge(m, l, z, finalize=True, merged=False, o_dtype=torch.float32):

@@ -14,9 +14,24 @@ import numpy as np
 import torch
 
 import oracle
+from oracle_pool import classify_row, REL_MARGIN  # noqa: F401
 
-REL_MARGIN = 1e-3
 TOL = {"bf16": 2e-2, "f32": 1e-5}
+# relative bound on the gate's fp32 block scores: the block mean is summed in
+# fp32 and split into two bf16 parts (~2^-17), and the dot product is an fp32
+# sum of D products; 5e-5 of sum_d |q_d| mean_t |k_td| covers both
+GATE_SCORE_REL = 5e-5
+# relative bound on the indexer's fp32 logits (exact bf16 products, fp32 sums
+# over D_I and over the heads), of sum_h w_h sum_d |iq_hd| |ik_jd|
+INDEXER_SCORE_REL = 5e-5
+SENTINEL = -7777  # pre-filled into index outputs: every element must be overwritten
+
+
+def poisoned(shape, dtype):
+    """A device tensor pre-filled with NaN (floating point) or SENTINEL (int32)."""
+    if dtype == torch.int32:
+        return torch.full(shape, SENTINEL, dtype=dtype, device="cuda")
+    return torch.full(shape, float("nan"), dtype=dtype, device="cuda")
 
 
 def dev_tensor(x, dtype):
@@ -36,34 +51,6 @@ def upload(w):
         d["w"] = torch.from_numpy(w.w).to("cuda")
     d["layout"] = csa.Layout(w.q_pos, w.q_seq, w.cu_seqlens)
     return d
-
-
-def classify_row(scores, gpu_set, ora_set, k):
-    """Compare one (row, head) selection with the margin criterion.
-
-    scores: oracle candidate scores (float64) indexed like the candidate ids in
-    gpu_set / ora_set (sets of candidate positions 0..n-1).
-    Returns "exact", "near_tie_ok" or a failure string.
-    """
-    n = len(scores)
-    kept = min(k, n)
-    if len(gpu_set) != kept:
-        return f"fail: {len(gpu_set)} kept, {kept} expected"
-    if gpu_set == ora_set:
-        return "exact"
-    if n <= k:
-        return "fail: short history must take every candidate"
-    srt = np.sort(scores)[::-1]
-    sk, sk1 = srt[k - 1], srt[k]
-    denom = max(abs(sk), abs(sk1))
-    rel = (sk - sk1) / denom if denom > 0 else 0.0
-    if rel > REL_MARGIN:
-        return f"fail: margin {rel:.2e} but selections differ"
-    band = REL_MARGIN * abs(sk)
-    for j in gpu_set ^ ora_set:
-        if abs(scores[j] - sk) > band:
-            return f"fail: candidate {j} (score {scores[j]:.6g}) outside the tie band"
-    return "near_tie_ok"
 
 
 def check_moba_indices(w, gpu_idx, gate=None):
@@ -133,6 +120,43 @@ def check_token_indices(w, rows, gpu_idx_rows):
             counts[res] += 1
     assert not fails, f"{len(fails)} index failures, first: {fails[:5]}"
     return counts
+
+
+def check_moba_scores(w, gate, gpu_idx, gpu_score):
+    """The gate's score output: +inf for the own block, -inf for padding, and for
+    each selected candidate block the oracle's score within GATE_SCORE_REL of
+    sum_d |q_d| mean_t |k_td| (the block's mean absolute key).  Returns the
+    worst absolute error and the number of scores compared."""
+    starts = gate["starts"]
+    _, lengths, _, _ = oracle.stream_blocks(w.cu_seqlens, w.block_size)
+    absmean = oracle.pool_blocks(np.abs(w.k), starts, lengths)  # [n_blocks, Hkv, D]
+    group = w.hq // w.hkv
+    kv = np.arange(w.hq) // group
+    worst, n = 0.0, 0
+    for i in range(w.n_q):
+        row, sc = gpu_idx[i], gpu_score[i]
+        pad = row == -1
+        assert np.isneginf(sc[pad]).all(), f"row {i}: padding scores are not -inf"
+        if gate["n_cand"][i] < 0:
+            continue
+        own = row == int(starts[gate["own"][i]])
+        assert np.isposinf(sc[own]).all(), f"row {i}: own-block scores are not +inf"
+        sel = ~pad & ~own
+        if not sel.any():
+            continue
+        h_of, s_of = np.nonzero(sel)
+        blk = np.searchsorted(starts, row[sel])
+        c = blk - int(gate["first"][i])
+        ref = gate["scores"][i, h_of, c]
+        a = (np.abs(w.q[i, h_of].astype(np.float64)) *
+             absmean[blk, kv[h_of]]).sum(axis=-1)
+        err = np.abs(sc[sel].astype(np.float64) - ref)
+        bad = err > GATE_SCORE_REL * a
+        assert not bad.any(), (f"row {i} head {h_of[bad][0]}: gate score error "
+                               f"{err[bad][0]:.3e} > {GATE_SCORE_REL * a[bad][0]:.3e}")
+        worst = max(worst, float(err.max()))
+        n += int(sel.sum())
+    return worst, n
 
 
 def sample_rows(n_q, count, seed=0, must=()):

@@ -2,9 +2,13 @@
 
 Inputs are the seeded workloads of ``csa_inputs``; the oracle reads the same
 values.  Index outputs follow the margin criterion and outputs the tolerances
-of tests/parity.py.  Small cases check every row; the five named workloads run
-at full size in the launch configuration the benchmark uses and check every
-selection (MoBA) or sampled rows (DSA indexer, attention outputs).
+of tests/parity.py.  Every output tensor is pre-filled with NaN (index
+outputs with a sentinel) so that an element the GPU never writes fails.  Small
+cases and the five named workloads at full size (in the launch configuration
+the benchmark uses) check every row: every selection against the margin
+criterion, every selected score against the oracle's, and every (row, head)
+output and log-sum-exp against the oracle evaluated on the GPU's selection
+(the full-size oracle runs in worker processes, tests/oracle_pool.py).
 """
 
 import numpy as np
@@ -12,9 +16,11 @@ import pytest
 import torch
 
 import oracle
-from csa_inputs import make_workload, tiny_block_workload, tiny_token_workload
-from parity import (TOL, upload, check_moba_indices, check_token_indices, sample_rows,
-                    dev_tensor)
+from csa_inputs import (make_workload, tiny_block_workload, tiny_token_workload,
+                        contiguous_positions, zigzag_positions)
+from parity import (TOL, upload, check_moba_indices, check_moba_scores, check_token_indices,
+                    poisoned, INDEXER_SCORE_REL)
+from oracle_pool import OraclePool, run_local, _dsa_check
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -28,12 +34,39 @@ def _say(*a):
 
 
 def _attn(w, d, idx, out_dtype=None, mode=None):
+    """Attention into NaN-filled out / lse tensors; (out as float32 numpy, lse)."""
     mode = (csa.CSA_SEL_BLOCK if w.mode == "block" else csa.CSA_SEL_TOKEN) if mode is None else mode
-    out, lse = csa.sparse_attn_fwd_shard(d["q"], d["k"], d["v"], d["layout"], mode, idx,
-                                         block_size=w.block_size, softmax_scale=w.scale,
-                                         out_dtype=out_dtype)
+    out_dtype = out_dtype or d["q"].dtype
+    out = poisoned((w.n_q, w.hq, w.dv), out_dtype)
+    lse = poisoned((w.n_q, w.hq), torch.float32)
+    csa.sparse_attn_fwd_shard(d["q"], d["k"], d["v"], d["layout"], mode, idx,
+                              block_size=w.block_size, softmax_scale=w.scale, out=out, lse=lse)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def _gate(w, d):
+    """Gate into sentinel / NaN-filled idx and score tensors (numpy results)."""
+    shape = (w.n_q, w.hq, w.topk + 1)
+    idx, score = csa.moba_gate_topk(d["q"], d["k"], d["layout"], w.block_size, w.topk,
+                                    idx=poisoned(shape, torch.int32),
+                                    score=poisoned(shape, torch.float32))
+    torch.cuda.synchronize()
+    return idx, idx.cpu().numpy(), score.cpu().numpy()
+
+
+def _indexer(w, d):
+    shape = (w.n_q, w.topk)
+    idx, score = csa.dsa_indexer_topk(d["iq"], d["ik"], d["w"], d["layout"], w.topk,
+                                      idx=poisoned(shape, torch.int32),
+                                      score=poisoned(shape, torch.float32))
+    torch.cuda.synchronize()
+    return idx, idx.cpu().numpy(), score.cpu().numpy()
+
+
+def _dsa_arrays(w, idx_np, score_np):
+    return dict(iq=w.iq, ik=w.ik, w=w.w, q_pos=w.q_pos, q_seq=w.q_seq, cu=w.cu_seqlens,
+                idx=idx_np, score=score_np)
 
 
 def _check_out(w, idx_np, out, lse, rows, tol):
@@ -74,11 +107,11 @@ def test_tiny_block_gate_and_attention(case, dtype):
     w = tiny_block_workload(dtype=dtype, **TINY_BLOCK[case])
     _say("tiny block", case, dtype, w.q.shape, w.k.shape)
     d = upload(w)
-    idx = csa.moba_gate_topk(d["q"], d["k"], d["layout"], w.block_size, w.topk)
-    torch.cuda.synchronize()
-    idx_np = idx.cpu().numpy()
-    counts = check_moba_indices(w, idx_np)
+    idx, idx_np, score_np = _gate(w, d)
+    gate = oracle.gate_scores(w.q, w.k, w.q_pos, w.q_seq, w.cu_seqlens, w.block_size)
+    counts = check_moba_indices(w, idx_np, gate)
     assert counts["exact"] > 0
+    check_moba_scores(w, gate, idx_np, score_np)
     for out_dtype in (torch.float32, d["q"].dtype):
         out, lse = _attn(w, d, idx, out_dtype=out_dtype)
         tol = TOL[dtype] if out_dtype == torch.float32 else TOL["bf16"]
@@ -104,23 +137,35 @@ def test_tiny_block_arbitrary_slots(dtype, block):
     _check_out(w, idx, out, lse, list(range(w.n_q)), TOL[dtype])
 
 
+TINY_TOKEN = [
+    # general-shape kernel (16 heads)
+    dict(hq=16, dqk=64, dv=64, hi=4, di=32, topk=37, lengths=(300, 212)),
+    # MFMA kernel, one wave per workgroup (32 heads)
+    dict(hq=32, dqk=128, dv=128, hi=4, di=64, topk=50, lengths=(400,)),
+    # MFMA kernel, two waves (64 heads), absorbed-MLA widths
+    dict(hq=64, dqk=576, dv=512, hi=8, di=128, topk=100, lengths=(700,)),
+    # MFMA kernel, four waves (128 heads), absorbed-MLA widths
+    dict(hq=128, dqk=576, dv=512, hi=8, di=128, topk=70, lengths=(200, 150)),
+]
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("shape", [dict(hq=16, dqk=64, dv=64, hi=4, di=32, topk=37,
-                                        lengths=(300, 212)),
-                                   dict(hq=64, dqk=576, dv=512, hi=8, di=128, topk=100,
-                                        lengths=(700,))])
-def test_tiny_token_indexer_and_attention(shape, dtype):
-    w = tiny_token_workload(seed=7, dtype=dtype, **shape)
-    _say("tiny token", shape, dtype)
+@pytest.mark.parametrize("shape", range(len(TINY_TOKEN)))
+def test_tiny_token_indexer_and_attention(shape, dtype, out):
+    w = tiny_token_workload(seed=7, dtype=dtype, **TINY_TOKEN[shape])
+    _say("tiny token", TINY_TOKEN[shape], dtype, "out", out)
     d = upload(w)
-    idx, score = csa.dsa_indexer_topk(d["iq"], d["ik"], d["w"], d["layout"], w.topk,
-                                      return_score=True)
-    torch.cuda.synchronize()
-    idx_np = idx.cpu().numpy()
+    idx, idx_np, score_np = _indexer(w, d)
     rows = list(range(w.n_q))
-    check_token_indices(w, rows, idx_np)
-    out, lse = _attn(w, d, idx, out_dtype=torch.float32)
-    _check_out(w, idx_np[:, None, :], out, lse, rows, TOL[dtype])
+    res = run_local(_dsa_arrays(w, idx_np, score_np), _dsa_check, rows,
+                    dict(topk=w.topk, score_rel=INDEXER_SCORE_REL))
+    assert res["n_fail"] == 0, res["fails"]
+    assert res["counts"]["exact"] > 0
+    out_dtype = torch.float32 if out == "f32" else torch.bfloat16
+    tol = TOL[dtype] if out == "f32" else TOL["bf16"]
+    got, lse = _attn(w, d, idx, out_dtype=out_dtype)
+    _check_out(w, idx_np[:, None, :], got, lse, rows, tol)
 
 
 def test_token_mode_per_head_index_and_pads():
@@ -332,8 +377,28 @@ def test_graph_capture_replays_match_eager(mode):
 
 
 # --------------------------------------------------------------------------------
-# the five named workloads at full size
+# the five named workloads at full size: every row
 # --------------------------------------------------------------------------------
+
+def _attn_arrays(w, idx_np, outs):
+    a = dict(q=w.q, k=w.k, v=w.value, q_pos=w.q_pos, q_seq=w.q_seq, cu=w.cu_seqlens,
+             idx=idx_np if idx_np.ndim == 3 else idx_np[:, None, :])
+    a.update(outs)
+    return a
+
+
+def _pool_attn_check(w, idx_np, outs, targets):
+    with OraclePool(_attn_arrays(w, idx_np, outs)) as pool:
+        _say(w.name, "oracle workers", pool.processes)
+        res = pool.attn_check(range(w.n_q), dict(mode=w.mode, scale=w.scale,
+                                                 block_size=w.block_size, targets=targets))
+    for (name, _, tol), r in zip(targets, res):
+        _say(w.name, name, "rows", w.n_q, "(row, head) pairs", r["pairs"], "without keys",
+             r["no_key_pairs"], "max abs err", f"{r['max_err']:.3e}", "max lse err",
+             f"{r['max_lse_err']:.3e}", "tol", tol)
+        assert not r["fails"], r["fails"][:5]
+        assert r["pairs"] == w.n_q * w.hq
+
 
 @pytest.mark.parametrize("name", ["dense_f32", "moba_mha_8k", "moba_gqa_zigzag_32k",
                                   "moba_thd_64k"])
@@ -341,22 +406,21 @@ def test_named_block_workload(name):
     w = make_workload(name)
     _say("workload", name, w.q.shape, w.k.shape)
     d = upload(w)
-    idx = csa.moba_gate_topk(d["q"], d["k"], d["layout"], w.block_size, w.topk)
-    torch.cuda.synchronize()
-    idx_np = idx.cpu().numpy()
-    counts = check_moba_indices(w, idx_np)
-    _say(name, "index categories", counts)
-    # rows: sequence starts (own block only, partially masked), shard edges, random
-    cu = w.cu_seqlens
-    starts = [i for i in range(w.n_q) if int(w.q_pos[i]) in set(cu[:-1].tolist())]
-    rows = sample_rows(w.n_q, 48, seed=1, must=[0, w.n_q - 1, w.n_q // 2, *starts[:8]])
-    out, lse = _attn(w, d, idx, out_dtype=torch.float32)
-    err = _check_out(w, idx_np, out, lse, rows, TOL[w.dtype])
-    _say(name, "fp32-out max abs err", err)
+    idx, idx_np, score_np = _gate(w, d)
+    gate = oracle.gate_scores(w.q, w.k, w.q_pos, w.q_seq, w.cu_seqlens, w.block_size)
+    counts = check_moba_indices(w, idx_np, gate)
+    _say(name, "index categories over", w.n_q, "rows x", w.hq, "heads:", counts)
+    worst, n = check_moba_scores(w, gate, idx_np, score_np)
+    _say(name, "gate scores compared", n, "max abs err", f"{worst:.3e}")
+    outs, targets = {}, []
+    out_f, lse_f = _attn(w, d, idx, out_dtype=torch.float32)
+    outs.update(out_f32=out_f, lse_f32=lse_f)
+    targets.append(("out_f32", "lse_f32", TOL[w.dtype]))
     if w.dtype == "bf16":
         out_b, lse_b = _attn(w, d, idx, out_dtype=torch.bfloat16)
-        err_b = _check_out(w, idx_np, out_b, lse_b, rows, TOL["bf16"])
-        _say(name, "bf16-out max abs err", err_b)
+        outs.update(out_bf16=out_b, lse_bf16=lse_b)
+        targets.append(("out_bf16", "lse_bf16", TOL["bf16"]))
+    _pool_attn_check(w, idx_np, outs, targets)
 
 
 def test_named_dsa_workload():
@@ -364,12 +428,52 @@ def test_named_dsa_workload():
     _say("workload dsa_mla_16k")
     d = upload(w)
     assert d["v"].data_ptr() == d["k"].data_ptr()  # aliased latent value
-    idx = csa.dsa_indexer_topk(d["iq"], d["ik"], d["w"], d["layout"], w.topk)
-    torch.cuda.synchronize()
-    idx_np = idx.cpu().numpy()
-    rows = sample_rows(w.n_q, 12, seed=2, must=[0, w.n_q - 1])
-    counts = check_token_indices(w, rows, idx_np[rows])
-    _say("dsa index categories", counts)
-    out, lse = _attn(w, d, idx, out_dtype=torch.bfloat16)
-    err = _check_out(w, idx_np[:, None, :], out, lse, rows, TOL["bf16"])
-    _say("dsa bf16-out max abs err", err)
+    idx, idx_np, score_np = _indexer(w, d)
+    with OraclePool(_dsa_arrays(w, idx_np, score_np)) as pool:
+        res = pool.dsa_check(range(w.n_q), dict(topk=w.topk, score_rel=INDEXER_SCORE_REL))
+    _say("dsa indexer over", w.n_q, "rows:", res["counts"], "failures", res["n_fail"],
+         "max score err", f"{res['max_score_err']:.3e}")
+    assert res["n_fail"] == 0, res["fails"]
+    assert sum(res["counts"].values()) == w.n_q
+    out_b, lse_b = _attn(w, d, idx, out_dtype=torch.bfloat16)
+    _pool_attn_check(w, idx_np, dict(out_bf16=out_b, lse_bf16=lse_b),
+                     [("out_bf16", "lse_bf16", TOL["bf16"])])
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+def test_shards_stitch_to_the_full_run(layout):
+    """Megatron-LM issue #4878, "Strategy: allgather CP mode", planned test: a
+    shard at its causal offset equals the matching slice of a full single-rank
+    run.  Every rank of a cp=4 split (contiguous or zigzag) is run on its own
+    and the shards, stitched back by global position, are compared with the
+    cp=1 run of the same stream: selections bit for bit, outputs within the
+    bf16 tolerance (and reported when bitwise equal)."""
+    cp = 4
+    w = tiny_block_workload(seed=41, layout="all", lengths=(4096,), hq=8, hkv=2, d=128,
+                            block=256, topk=3, dtype="bf16")
+    _say("stitch", layout)
+    full = upload(w)
+    idx_full, idx_full_np, score_full = _gate(w, full)
+    out_full, lse_full = _attn(w, full, idx_full, out_dtype=torch.bfloat16)
+    seen = np.zeros(w.n_q, np.int64)
+    bitwise = True
+    make = contiguous_positions if layout == "contiguous" else zigzag_positions
+    for rank in range(cp):
+        pos = make(w.n_kv, cp, rank)
+        seen[pos] += 1
+        sw = tiny_block_workload(seed=41, layout="all", lengths=(4096,), hq=8, hkv=2, d=128,
+                                 block=256, topk=3, dtype="bf16")
+        sw.q, sw.q_pos, sw.q_seq = w.q[pos], pos.astype(np.int32), w.q_seq[pos]
+        sd = upload(sw)
+        idx_s, idx_s_np, score_s = _gate(sw, sd)
+        assert np.array_equal(idx_s_np, idx_full_np[pos]), f"rank {rank}: selections differ"
+        assert np.array_equal(score_s, score_full[pos]), f"rank {rank}: gate scores differ"
+        out_s, lse_s = _attn(sw, sd, idx_s, out_dtype=torch.bfloat16)
+        assert np.isfinite(out_s).all() and not np.isnan(lse_s).any()
+        err = np.abs(out_s - out_full[pos]).max()
+        assert err <= TOL["bf16"], f"rank {rank}: max abs err {err:.3e}"
+        np.testing.assert_allclose(lse_s, lse_full[pos], rtol=0, atol=1e-4)
+        bitwise &= bool(np.array_equal(out_s, out_full[pos]) and
+                        np.array_equal(lse_s, lse_full[pos]))
+    assert (seen == 1).all()
+    _say("stitch", layout, "shards equal the full run bit for bit:", bitwise)
