@@ -48,6 +48,7 @@ from .attention import (
     merge_parts,
 )
 from .mla import v_up_proj
+from .backward import shard_backward, loss
 
 __all__ = [
     "permitted_interval",
@@ -72,4 +73,6 @@ __all__ = [
     "finalize",
     "merge_parts",
     "v_up_proj",
+    "shard_backward",
+    "loss",
 ]

@@ -1,0 +1,75 @@
+"""Gradients of the shard attention with the selection held fixed (oracle, fp64;
+test infrastructure).
+
+"Context parallel attention: exchange keys and merge softmax globally",
+paragraph on positions and masks: a correct forward does not prove training;
+the backward pass must send the gradients of keys and values back to their
+owners.  Megatron-LM issue #4878, "Strategy: allgather CP mode", step on the
+backward: gradients of the gathered keys and values are computed locally and
+then reduce-scattered to the ranks that own them (the reduction across ranks
+is out of this one-GPU path; this computes one shard's contribution).
+
+Reading taken: the selection (indices) is a discrete choice and is held fixed;
+the loss is L = sum_{i,h} dO[i,h] . O[i,h].  For one (row i, head h) with the
+multiset S of selected permitted keys (the forward's definition, a repeated
+slot counting its keys again), logits x_j = scale * q . k_j, weights
+P_j = exp(x_j - lse) and O = sum_j P_j v_j, the chain rule gives
+
+    dv_j += P_j dO
+    dP_j  = dO . v_j
+    dx_j  = P_j (dP_j - sum_l P_l dP_l)          (softmax Jacobian)
+    dq   += scale sum_j dx_j k_j
+    dk_j += scale dx_j q
+
+summed over every occurrence of j in S and over every (row, head) whose
+selection holds j; query head h feeds key/value head h // (Hq / Hkv).  A
+(row, head) without selected keys contributes nothing.  When the value is the
+first Dv columns of the key (absorbed MLA), dk and dv are returned separately
+and the gradient of the shared tensor is dk + dv on those columns.
+"""
+
+import numpy as np
+
+from .layout import permitted_interval
+from .attention import selected_keys
+
+
+def shard_backward(q, k, v, q_pos, q_seq, cu_seqlens, mode, idx, scale, dout, block_size=0):
+    """(dq [n_q, Hq, Dqk], dk [n_kv, Hkv, Dqk], dv [n_kv, Hkv, Dv]) in float64.
+
+    Arguments as ``shard_forward``; dout [n_q, Hq, Dv] is dL/dO.
+    """
+    n_q, hq, dqk = q.shape
+    hkv = k.shape[1]
+    group = hq // hkv
+    dq = np.zeros((n_q, hq, dqk))
+    dk = np.zeros((k.shape[0], hkv, dqk))
+    dv = np.zeros((v.shape[0], hkv, v.shape[2]))
+    for i in range(n_q):
+        iv = permitted_interval(int(q_pos[i]), int(q_seq[i]), cu_seqlens)
+        for h in range(hq):
+            keys = selected_keys(mode, idx[i, 0 if idx.shape[1] == 1 else h], iv, block_size)
+            if len(keys) == 0:
+                continue
+            g = h // group
+            qv = np.asarray(q[i, h], np.float64)
+            do = np.asarray(dout[i, h], np.float64)
+            kmat = np.asarray(k[keys, g], np.float64)
+            vmat = np.asarray(v[keys, g], np.float64)
+            x = scale * (kmat @ qv)
+            m = x.max()
+            p = np.exp(x - m)
+            p /= p.sum()                      # P_j = exp(x_j - lse)
+            dp = vmat @ do                    # dP_j
+            dx = p * (dp - p @ dp)            # softmax Jacobian
+            dq[i, h] = scale * (dx @ kmat)
+            np.add.at(dk[:, g], keys, scale * dx[:, None] * qv[None, :])
+            np.add.at(dv[:, g], keys, p[:, None] * do[None, :])
+    return dq, dk, dv
+
+
+def loss(q, k, v, q_pos, q_seq, cu_seqlens, mode, idx, scale, dout, block_size=0):
+    """L = sum dO . O of the forward (for finite-difference pins)."""
+    from .attention import shard_forward
+    out, _ = shard_forward(q, k, v, q_pos, q_seq, cu_seqlens, mode, idx, scale, block_size)
+    return float((np.asarray(dout, np.float64) * out).sum())
