@@ -12,6 +12,8 @@ importing this package raises.
 from ._binding import (
     Layout,
     moba_gate_topk,
+    moba_gate_topk_noalloc,
+    GATE_SCRATCH_BYTES,
     dsa_indexer_topk,
     sparse_attn_fwd_shard,
     summary_merge,
@@ -28,6 +30,8 @@ from ._binding import (
 __all__ = [
     "Layout",
     "moba_gate_topk",
+    "moba_gate_topk_noalloc",
+    "GATE_SCRATCH_BYTES",
     "dsa_indexer_topk",
     "sparse_attn_fwd_shard",
     "summary_merge",

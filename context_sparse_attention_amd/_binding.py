@@ -53,6 +53,8 @@ lib.moba_gate_topk_workspace_size.restype = _sz
 lib.moba_gate_topk_workspace_size.argtypes = [_LP, _i32, _i32, _i32]
 lib.moba_gate_topk.restype = ctypes.c_int
 lib.moba_gate_topk.argtypes = [_T3, _T3, _LP, _i32, _i32, _P, _P, _P, _sz, _P]
+lib.moba_gate_topk_noalloc.restype = ctypes.c_int
+lib.moba_gate_topk_noalloc.argtypes = [_T3, _T3, _LP, _i32, _i32, _P, _P, _P]
 lib.dsa_indexer_topk_workspace_size.restype = _sz
 lib.dsa_indexer_topk_workspace_size.argtypes = [_LP, _i32]
 lib.dsa_indexer_topk.restype = ctypes.c_int
@@ -163,6 +165,23 @@ def moba_gate_topk(q, k, layout, block_size, topk, return_score=False, idx=None,
                               block_size, topk, idx.data_ptr(), _ptr(score), ws.data_ptr(),
                               ws.numel(), _stream()))
     return (idx, score) if (return_score or score is not None) else idx
+
+
+def moba_gate_topk_noalloc(q, k, layout, block_size, topk, idx, score=None):
+    """moba_gate_topk into caller-given outputs, with the library's fixed scratch
+    instead of a workspace (nothing is allocated); returns idx (and score)."""
+    dev = q.device
+    shape = (layout.n_q, q.shape[1], topk + 1)
+    _given(idx, shape, torch.int32, dev, "idx")
+    if score is not None:
+        _given(score, shape, torch.float32, dev, "score")
+    _check(lib.moba_gate_topk_noalloc(ctypes.byref(_tensor3(q)), ctypes.byref(_tensor3(k)),
+                                      layout.c, block_size, topk, idx.data_ptr(), _ptr(score),
+                                      _stream()))
+    return idx if score is None else (idx, score)
+
+
+GATE_SCRATCH_BYTES = 16 * 1024 * 1024  # CSA_GATE_SCRATCH_BYTES of include/csa.h
 
 
 def dsa_indexer_topk(iq, ik, w, layout, topk, return_score=False, idx=None, score=None):

@@ -9,9 +9,19 @@
 #include <stdio.h>
 
 #include <exception>
+#include <mutex>
 #include <string>
 
 #include "common.hpp"
+
+// Fixed scratch of moba_gate_topk_noalloc: one copy per device, held until the
+// process ends.  Host code never uses the array's name as an address (on the
+// host it is only a stand-in); it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current (device_scratch below).  Every no-alloc gate call on a device shares
+// that device's copy; the gate kernels write every scratch byte they read
+// before reading it, so nothing needs clearing between calls.
+static __device__ __align__(256) char scratch[CSA_GATE_SCRATCH_BYTES];
 
 namespace csa {
 namespace {
@@ -93,6 +103,65 @@ csa_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   return CSA_OK;
 }
 
+// Host checks and kernel arguments of a gate call (everything but the workspace).
+csa_status gate_args(const csa_tensor3* q, const csa_tensor3* k, const csa_layout* L,
+                     int32_t block_size, int32_t topk, int32_t* idx, float* score,
+                     MobaGateArgs* a, size_t* need) {
+  csa_status st;
+  if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_layout(L)))
+    return st;
+  if (q->dtype != k->dtype) return fail(CSA_ERR_INVALID_ARG, "q and k dtypes differ");
+  if (q->n != L->n_q) return fail(CSA_ERR_INVALID_ARG, "q has %lld rows, layout n_q %d",
+                                  (long long)q->n, L->n_q);
+  if (k->n != L->n_kv) return fail(CSA_ERR_INVALID_ARG, "k has %lld tokens, layout n_kv %d",
+                                   (long long)k->n, L->n_kv);
+  if (q->d != k->d) return fail(CSA_ERR_INVALID_ARG, "q and k head dims differ");
+  if (q->h % k->h) return fail(CSA_ERR_INVALID_ARG, "Hq %d not a multiple of Hkv %d", q->h, k->h);
+  if (q->d > 256) return fail(CSA_ERR_UNSUPPORTED, "gate head dim %d > 256", q->d);
+  if (block_size < 1) return fail(CSA_ERR_INVALID_ARG, "block_size %d", block_size);
+  if (topk < 0 || topk > 32) return fail(CSA_ERR_UNSUPPORTED, "topk %d outside [0, 32]", topk);
+  if (L->n_q > 0 && !idx) return fail(CSA_ERR_INVALID_ARG, "null idx");
+  if ((int64_t)L->n_q * q->h * (topk + 1) >= ((int64_t)1 << 31))
+    return fail(CSA_ERR_UNSUPPORTED, "index output too large");
+  const int64_t nb = count_blocks(L->cu_seqlens_host, L->n_seq, block_size);
+  if (nb >= ((int64_t)1 << 30)) return fail(CSA_ERR_UNSUPPORTED, "too many blocks");
+  *need = moba_gate_ws_bytes(L->n_seq, (int)nb, k->h, k->d, block_size);
+  a->q = make_view(q);
+  a->k = make_view(k);
+  a->L = make_dev_layout(L);
+  a->block_size = block_size;
+  a->topk = topk;
+  a->n_blocks = (int)nb;
+  a->dtype = q->dtype;
+  a->idx = idx;
+  a->score = score;
+  a->ws = nullptr;
+  return CSA_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+csa_status device_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(CSA_ERR_UNSUPPORTED, "device id %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || ((uintptr_t)p & 255u))
+      return fail(CSA_ERR_HIP, "scratch symbol address %p not 256-byte aligned", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return CSA_OK;
+}
+
 template <typename F>
 csa_status guarded(F&& f) {
   try {
@@ -124,39 +193,36 @@ csa_status moba_gate_topk(const csa_tensor3* q, const csa_tensor3* k, const csa_
                           int32_t block_size, int32_t topk, int32_t* idx, float* score,
                           void* ws, size_t ws_bytes, void* stream) {
   return guarded([&]() -> csa_status {
-    csa_status st;
-    if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_layout(L)))
-      return st;
-    if (q->dtype != k->dtype) return fail(CSA_ERR_INVALID_ARG, "q and k dtypes differ");
-    if (q->n != L->n_q) return fail(CSA_ERR_INVALID_ARG, "q has %lld rows, layout n_q %d",
-                                    (long long)q->n, L->n_q);
-    if (k->n != L->n_kv) return fail(CSA_ERR_INVALID_ARG, "k has %lld tokens, layout n_kv %d",
-                                     (long long)k->n, L->n_kv);
-    if (q->d != k->d) return fail(CSA_ERR_INVALID_ARG, "q and k head dims differ");
-    if (q->h % k->h) return fail(CSA_ERR_INVALID_ARG, "Hq %d not a multiple of Hkv %d", q->h, k->h);
-    if (q->d > 256) return fail(CSA_ERR_UNSUPPORTED, "gate head dim %d > 256", q->d);
-    if (block_size < 1) return fail(CSA_ERR_INVALID_ARG, "block_size %d", block_size);
-    if (topk < 0 || topk > 32) return fail(CSA_ERR_UNSUPPORTED, "topk %d outside [0, 32]", topk);
-    if (L->n_q > 0 && !idx) return fail(CSA_ERR_INVALID_ARG, "null idx");
-    if ((int64_t)L->n_q * q->h * (topk + 1) >= ((int64_t)1 << 31))
-      return fail(CSA_ERR_UNSUPPORTED, "index output too large");
-    const int64_t nb = count_blocks(L->cu_seqlens_host, L->n_seq, block_size);
-    if (nb >= ((int64_t)1 << 30)) return fail(CSA_ERR_UNSUPPORTED, "too many blocks");
-    const size_t need = moba_gate_ws_bytes(L->n_seq, (int)nb, k->h, k->d, block_size);
-    if ((st = check_ws(ws, ws_bytes, need))) return st;
     MobaGateArgs a;
-    a.q = make_view(q);
-    a.k = make_view(k);
-    a.L = make_dev_layout(L);
-    a.block_size = block_size;
-    a.topk = topk;
-    a.n_blocks = (int)nb;
-    a.dtype = q->dtype;
-    a.idx = idx;
-    a.score = score;
+    size_t need = 0;
+    csa_status st;
+    if ((st = gate_args(q, k, L, block_size, topk, idx, score, &a, &need))) return st;
+    if ((st = check_ws(ws, ws_bytes, need))) return st;
     a.ws = ws;
     hipError_t e = launch_moba_gate(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "moba_gate_topk");
+    return CSA_OK;
+  });
+}
+
+csa_status moba_gate_topk_noalloc(const csa_tensor3* q, const csa_tensor3* k,
+                                  const csa_layout* L, int32_t block_size, int32_t topk,
+                                  int32_t* idx, float* score, void* stream) {
+  return guarded([&]() -> csa_status {
+    MobaGateArgs a;
+    size_t need = 0;
+    csa_status st;
+    if ((st = gate_args(q, k, L, block_size, topk, idx, score, &a, &need))) return st;
+    if (need > (size_t)CSA_GATE_SCRATCH_BYTES)
+      return fail(CSA_ERR_UNSUPPORTED,
+                  "moba_gate_topk_noalloc: this shape needs %zu bytes of scratch, more than "
+                  "the library's fixed %d (use moba_gate_topk with a workspace)",
+                  need, (int)CSA_GATE_SCRATCH_BYTES);
+    void* scratch_ptr = nullptr;
+    if ((st = device_scratch(&scratch_ptr))) return st;
+    a.ws = scratch_ptr;
+    hipError_t e = launch_moba_gate(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "moba_gate_topk_noalloc");
     return CSA_OK;
   });
 }

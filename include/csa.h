@@ -126,6 +126,26 @@ csa_status moba_gate_topk(const csa_tensor3* q, const csa_tensor3* k, const csa_
                           void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * moba_gate_topk_noalloc - moba_gate_topk without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, serving loops
+ * that forbid allocation, harnesses without an allocator).
+ *
+ * Same arguments, results and errors as moba_gate_topk, minus ws / ws_bytes.  The
+ * scratch it needs lives in a fixed device array of CSA_GATE_SCRATCH_BYTES per GPU,
+ * inside the library, held from the first call on that GPU until the process ends;
+ * this call allocates nothing.  A request whose workspace would exceed that size
+ * (moba_gate_topk_workspace_size() > CSA_GATE_SCRATCH_BYTES) returns
+ * CSA_ERR_UNSUPPORTED and enqueues nothing.  All calls on one GPU share its scratch:
+ * calls that may overlap on one GPU (different streams, or host threads) race and
+ * must be ordered by the caller.  The first call on a GPU looks up that GPU's copy
+ * (hipGetSymbolAddress) with the GPU current; a failure there returns CSA_ERR_HIP.
+ * ------------------------------------------------------------------------------- */
+#define CSA_GATE_SCRATCH_BYTES (16 * 1024 * 1024)
+csa_status moba_gate_topk_noalloc(const csa_tensor3* q, const csa_tensor3* k,
+                                  const csa_layout* L, int32_t block_size, int32_t topk,
+                                  int32_t* idx, float* score, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * dsa_indexer_topk - DSA-style token indexer and top-k token selection
  * [MLM#3674 Description, MLM#4878 Strategy].
  *

@@ -153,3 +153,18 @@ def test_up_projection_rejects_bad_arguments():
     assert call(out_dtype=7)[0] == 1
     assert call(out=None)[0] == 1
     assert call(out=(1 << 20) + 8)[0] == 1           # misaligned output
+
+
+def test_noalloc_gate_rejects_shapes_beyond_its_scratch_on_the_host():
+    # 8192 one-token blocks x 8 heads x 128 dims of block means: beyond the fixed
+    # scratch, so the call returns before touching the device
+    L = FakeLayout([0, 8192], 64)
+    q, k = t3(64, 8, 128), t3(8192, 8, 128)
+    assert B.lib.moba_gate_topk_workspace_size(L.c, 8, 128, 1) > B.GATE_SCRATCH_BYTES
+    st = B.lib.moba_gate_topk_noalloc(ctypes.byref(q), ctypes.byref(k), L.c, 1, 2, 1 << 20,
+                                      None, None)
+    assert st == 2 and "scratch" in B.lib.csa_last_error().decode()
+    # ordinary argument errors are the workspace call's
+    st = B.lib.moba_gate_topk_noalloc(ctypes.byref(q), ctypes.byref(t3(8192, 3, 128)), L.c,
+                                      64, 2, 1 << 20, None, None)
+    assert st == 1
