@@ -47,6 +47,26 @@ def shard_backward(q, k, v, q_pos, q_seq, cu_seqlens, mode, idx, scale, dout, bl
     dv = np.zeros((v.shape[0], hkv, v.shape[2]))
     for i in range(n_q):
         iv = permitted_interval(int(q_pos[i]), int(q_seq[i]), cu_seqlens)
+        if idx.shape[1] == 1:
+            # one selection for the whole row: each key head's G query heads at once
+            keys = selected_keys(mode, idx[i, 0], iv, block_size)
+            if len(keys) == 0:
+                continue
+            for g in range(hkv):
+                heads = slice(g * group, (g + 1) * group)
+                qm = np.asarray(q[i, heads], np.float64)            # [G, Dqk]
+                do = np.asarray(dout[i, heads], np.float64)         # [G, Dv]
+                kmat = np.asarray(k[keys, g], np.float64)
+                vmat = np.asarray(v[keys, g], np.float64)
+                x = scale * (qm @ kmat.T)                           # [G, n]
+                p = np.exp(x - x.max(axis=1, keepdims=True))
+                p /= p.sum(axis=1, keepdims=True)
+                dp = do @ vmat.T
+                dx = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dq[i, heads] = scale * (dx @ kmat)
+                np.add.at(dk[:, g], keys, scale * (dx.T @ qm))
+                np.add.at(dv[:, g], keys, p.T @ do)
+            continue
         for h in range(hq):
             keys = selected_keys(mode, idx[i, 0 if idx.shape[1] == 1 else h], iv, block_size)
             if len(keys) == 0:
