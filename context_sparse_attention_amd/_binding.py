@@ -64,6 +64,11 @@ lib.sparse_attn_fwd_shard_workspace_size.argtypes = [_LP, _i32, _i32, _i32, _i32
 lib.sparse_attn_fwd_shard.restype = ctypes.c_int
 lib.sparse_attn_fwd_shard.argtypes = [_T3, _T3, _T3, _LP, _i32, _P, _i32, _i32, _i32, _f32,
                                       _P, _i32, _P, _P, _sz, _P]
+lib.sparse_attn_bwd_shard_workspace_size.restype = _sz
+lib.sparse_attn_bwd_shard_workspace_size.argtypes = [_LP, _i32, _i32, _i32, _i32, _i32, _i32]
+lib.sparse_attn_bwd_shard.restype = ctypes.c_int
+lib.sparse_attn_bwd_shard.argtypes = [_T3, _T3, _T3, _LP, _i32, _P, _i32, _i32, _i32, _f32,
+                                      _T3, _T3, _P, _P, _P, _P, _P, _sz, _P]
 lib.csa_trace_begin.restype = ctypes.c_int
 lib.csa_trace_begin.argtypes = [ctypes.c_int]
 lib.csa_trace_collect.restype = ctypes.c_int
@@ -234,6 +239,39 @@ def sparse_attn_fwd_shard(q, k, v, layout, mode, idx, block_size=0, softmax_scal
                                      float(softmax_scale), out.data_ptr(), _dtype_code(out),
                                      _ptr(lse), ws.data_ptr(), ws.numel(), _stream()))
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def sparse_attn_bwd_shard(q, k, v, layout, mode, idx, out, dout, lse, block_size=0,
+                          softmax_scale=None, dq=None, dk=None, dv=None):
+    """(dq, dk, dv) float32 of the forward's arguments, output, lse and dL/dout.
+
+    ``idx`` as in sparse_attn_fwd_shard.  ``dq`` / ``dk`` / ``dv`` may be given as
+    preallocated float32 outputs (every element is written).
+    """
+    dev = q.device
+    if idx.dim() == 2:
+        idx = idx.unsqueeze(1)
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous int32 tensor")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(q.shape[2])
+    hq, hkv = q.shape[1], k.shape[1]
+    dq = _out(dq, (layout.n_q, hq, q.shape[2]), torch.float32, dev, "dq")
+    dk = _out(dk, (layout.n_kv, hkv, k.shape[2]), torch.float32, dev, "dk")
+    dv = _out(dv, (layout.n_kv, hkv, v.shape[2]), torch.float32, dev, "dv")
+    ws_bytes = lib.sparse_attn_bwd_shard_workspace_size(layout.c, mode, hq, hkv, idx.shape[1],
+                                                        idx.shape[2], block_size)
+    ws = _workspace(ws_bytes, dev)
+    _check(lib.sparse_attn_bwd_shard(ctypes.byref(_tensor3(q)), ctypes.byref(_tensor3(k)),
+                                     ctypes.byref(_tensor3(v)), layout.c, mode, idx.data_ptr(),
+                                     idx.shape[1], idx.shape[2], block_size,
+                                     float(softmax_scale), ctypes.byref(_tensor3(out)),
+                                     ctypes.byref(_tensor3(dout)), lse.data_ptr(),
+                                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+                                     ws.numel(), _stream()))
+    return dq, dk, dv
 
 
 def summary_merge(m, l, z, finalize=True, merged=False, o_dtype=torch.float32):

@@ -369,6 +369,101 @@ csa_status sparse_attn_fwd_shard(const csa_tensor3* q, const csa_tensor3* k,
   });
 }
 
+size_t sparse_attn_bwd_shard_workspace_size(const csa_layout* L, int32_t mode, int32_t hq,
+                                            int32_t hkv, int32_t idx_heads, int32_t idx_width,
+                                            int32_t block_size) {
+  if (!L || !L->cu_seqlens_host || L->n_seq < 1 || L->n_q < 0 || L->n_kv < 0 || hq < 1 ||
+      hkv < 1 || idx_heads < 1 || idx_width < 1)
+    return 0;
+  int64_t nb = 0;
+  if (mode == CSA_SEL_BLOCK) {
+    if (block_size < 1) return 0;
+    nb = count_blocks(L->cu_seqlens_host, L->n_seq, block_size);
+  }
+  return attn_bwd_ws_bytes(L->n_q, L->n_kv, L->n_seq, (int)nb, mode, hq, hkv, idx_heads,
+                           idx_width);
+}
+
+csa_status sparse_attn_bwd_shard(const csa_tensor3* q, const csa_tensor3* k,
+                                 const csa_tensor3* v, const csa_layout* L, int32_t mode,
+                                 const int32_t* idx, int32_t idx_heads, int32_t idx_width,
+                                 int32_t block_size, float softmax_scale,
+                                 const csa_tensor3* out, const csa_tensor3* dout,
+                                 const float* lse, float* dq, float* dk, float* dv, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  return guarded([&]() -> csa_status {
+    csa_status st;
+    if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) ||
+        (st = check_tensor(v, "v")) || (st = check_tensor(out, "out")) ||
+        (st = check_tensor(dout, "dout")) || (st = check_layout(L)))
+      return st;
+    if (q->dtype != k->dtype || k->dtype != v->dtype)
+      return fail(CSA_ERR_INVALID_ARG, "q, k, v dtypes differ");
+    if (q->n != L->n_q) return fail(CSA_ERR_INVALID_ARG, "q rows %lld != n_q %d",
+                                    (long long)q->n, L->n_q);
+    if (k->n != L->n_kv || v->n != L->n_kv)
+      return fail(CSA_ERR_INVALID_ARG, "k/v tokens != n_kv %d", L->n_kv);
+    if (q->d != k->d) return fail(CSA_ERR_INVALID_ARG, "q and k head dims differ");
+    if (k->h != v->h) return fail(CSA_ERR_INVALID_ARG, "k and v head counts differ");
+    if (q->h % k->h) return fail(CSA_ERR_INVALID_ARG, "Hq %d not a multiple of Hkv %d", q->h, k->h);
+    if (q->d > 576) return fail(CSA_ERR_UNSUPPORTED, "head dim %d > 576", q->d);
+    if (v->d > 512) return fail(CSA_ERR_UNSUPPORTED, "value dim %d > 512", v->d);
+    for (const csa_tensor3* t : {out, dout})
+      if (t->n != L->n_q || t->h != q->h || t->d != v->d)
+        return fail(CSA_ERR_INVALID_ARG, "out / dout must be [n_q, Hq, Dv] = [%d, %d, %d]",
+                    L->n_q, q->h, v->d);
+    if (mode != CSA_SEL_BLOCK && mode != CSA_SEL_TOKEN)
+      return fail(CSA_ERR_INVALID_ARG, "mode %d", mode);
+    if (mode == CSA_SEL_BLOCK && block_size < 1)
+      return fail(CSA_ERR_INVALID_ARG, "block_size %d", block_size);
+    if (idx_heads != 1 && idx_heads != q->h)
+      return fail(CSA_ERR_INVALID_ARG, "idx_heads %d must be 1 or Hq %d", idx_heads, q->h);
+    if (idx_width < 1) return fail(CSA_ERR_INVALID_ARG, "idx_width %d", idx_width);
+    if (!isfinite(softmax_scale)) return fail(CSA_ERR_INVALID_ARG, "softmax_scale not finite");
+    if (L->n_q > 0 && (!idx || !lse || !dq))
+      return fail(CSA_ERR_INVALID_ARG, "null idx, lse or dq");
+    if (L->n_kv > 0 && (!dk || !dv)) return fail(CSA_ERR_INVALID_ARG, "null dk or dv");
+    if ((int64_t)L->n_q * idx_heads * idx_width >= ((int64_t)1 << 31) ||
+        (int64_t)L->n_q * q->h >= ((int64_t)1 << 31) ||
+        (int64_t)L->n_kv * k->h * 576 >= ((int64_t)1 << 40))
+      return fail(CSA_ERR_UNSUPPORTED, "shard too large for int32 index rows");
+    int64_t nb = 0;
+    if (mode == CSA_SEL_BLOCK) nb = count_blocks(L->cu_seqlens_host, L->n_seq, block_size);
+    if (nb >= ((int64_t)1 << 30)) return fail(CSA_ERR_UNSUPPORTED, "too many blocks");
+    if ((mode == CSA_SEL_TOKEN ? (int64_t)L->n_kv : nb) * (idx_heads == 1 ? 1 : k->h) >=
+        ((int64_t)1 << 30))
+      return fail(CSA_ERR_UNSUPPORTED, "too many key lists");
+    const size_t need = attn_bwd_ws_bytes(L->n_q, L->n_kv, L->n_seq, (int)nb, mode, q->h,
+                                          k->h, idx_heads, idx_width);
+    if ((st = check_ws(ws, ws_bytes, need))) return st;
+    AttnBwdArgs a;
+    a.q = make_view(q);
+    a.k = make_view(k);
+    a.v = make_view(v);
+    a.o = make_view(out);
+    a.dout = make_view(dout);
+    a.o_dtype = out->dtype;
+    a.dout_dtype = dout->dtype;
+    a.L = make_dev_layout(L);
+    a.mode = mode;
+    a.idx_heads = idx_heads;
+    a.idx_width = idx_width;
+    a.block_size = block_size;
+    a.n_blocks = (int)nb;
+    a.dtype = q->dtype;
+    a.idx = idx;
+    a.lse = lse;
+    a.scale = softmax_scale;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.ws = ws;
+    hipError_t e = launch_attn_backward(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "sparse_attn_bwd_shard");
+    return CSA_OK;
+  });
+}
+
 csa_status summary_merge(int32_t n_parts, int64_t n_rows, int32_t dv, const float* m,
                          const float* l, const float* z, float* m_out, float* l_out,
                          float* z_out, void* o_out, int32_t o_dtype, float* lse_out,

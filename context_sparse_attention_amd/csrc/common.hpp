@@ -186,6 +186,22 @@ size_t attn_ws_bytes(int n_q, int n_seq, int n_blocks, int mode, int hq, int hkv
                      int idx_width);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
 
+struct AttnBwdArgs {
+  View q, k, v;
+  View o, dout;  // forward output and its gradient [n_q, Hq, Dv]
+  int o_dtype, dout_dtype;
+  DevLayout L;
+  int mode, idx_heads, idx_width, block_size, n_blocks, dtype;
+  const int32_t* idx;
+  const float* lse;
+  float scale;
+  float *dq, *dk, *dv;
+  void* ws;
+};
+size_t attn_bwd_ws_bytes(int n_q, int n_kv, int n_seq, int n_blocks, int mode, int hq, int hkv,
+                         int idx_heads, int idx_width);
+hipError_t launch_attn_backward(const AttnBwdArgs& a, hipStream_t stream);
+
 struct MergeArgs {
   int n_parts;
   int64_t n_rows;

@@ -206,6 +206,47 @@ csa_status sparse_attn_fwd_shard(const csa_tensor3* q, const csa_tensor3* k,
                                  void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * sparse_attn_bwd_shard - gradients of sparse_attn_fwd_shard with the selection held
+ * fixed [CPA, paragraph on positions and masks: the backward returns key and value
+ * gradients to their owners; MLM#4878 "Strategy: allgather CP mode", backward step:
+ * the gathered keys' and values' gradients are computed per rank, then
+ * reduce-scattered (that reduction is the caller's)].
+ *
+ * With dO = dout, the forward's lse, P_j = exp(softmax_scale * q . k_j - lse) and
+ * D = dO . out over each (row, head)'s selected keys (the same multiset as the
+ * forward):
+ *   dq[i,h]   = scale * sum_j P_j (dO . v_j - D) k_j
+ *   dk[j,g]  += scale * P_j (dO . v_j - D) q[i,h]
+ *   dv[j,g]  += P_j dO[i,h]
+ * summed over every (row, head) whose selection holds key j, with g = h / (Hq/Hkv).
+ * fp32 arithmetic; each key's sums run over its selecting (row, head) pairs in
+ * ascending order: bitwise reproducible, no floating-point atomics.
+ *
+ *  q, k, v, idx, idx_heads, idx_width, block_size, softmax_scale, L, mode: as in
+ *     sparse_attn_fwd_shard (the forward's arguments).  When v aliases k (absorbed
+ *     MLA) dk and dv are still separate outputs; the gradient of the shared tensor
+ *     is dk plus dv on its first Dv columns.
+ *  out, dout [n_q, Hq, Dv] (f32 or bf16 each): the forward's output and the loss's
+ *     gradient with respect to it.  lse [n_q, Hq] f32: the forward's log-sum-exp
+ *     (natural log; -inf for a (row, head) without keys, which gets dq = 0).
+ *  dq [n_q, Hq, Dqk], dk [n_kv, Hkv, Dqk], dv [n_kv, Hkv, Dv]: f32, contiguous,
+ *     every element written (0 where nothing contributes).
+ *  ws: at least sparse_attn_bwd_shard_workspace_size() bytes, 256-byte aligned (it
+ *     holds D, the block table and the key lists: about 4 bytes per index slot).
+ *  n_q * Hq and n_q * idx_heads * idx_width must stay below 2^31.
+ * ------------------------------------------------------------------------------- */
+size_t sparse_attn_bwd_shard_workspace_size(const csa_layout* L, int32_t mode, int32_t hq,
+                                            int32_t hkv, int32_t idx_heads, int32_t idx_width,
+                                            int32_t block_size);
+csa_status sparse_attn_bwd_shard(const csa_tensor3* q, const csa_tensor3* k,
+                                 const csa_tensor3* v, const csa_layout* L, int32_t mode,
+                                 const int32_t* idx, int32_t idx_heads, int32_t idx_width,
+                                 int32_t block_size, float softmax_scale,
+                                 const csa_tensor3* out, const csa_tensor3* dout,
+                                 const float* lse, float* dq, float* dk, float* dv, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * summary_merge - merge P chunk summaries per row [CPA, summary paragraph].
  *
  * Part p of row r is (m[p,r], l[p,r], z[p,r,:]) with m in natural-log units.

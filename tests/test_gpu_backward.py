@@ -1,0 +1,217 @@
+"""GPU parity of sparse_attn_bwd_shard against the fp64 oracle (MI355X only).
+
+The forward runs first (its output and log-sum-exp feed the backward, as in
+training); dO is seeded N(0, 1).  Every dq, dk and dv element is compared with
+``oracle.shard_backward`` on the same selection: max-abs error within 1e-5 for
+fp32 inputs and 2e-2 for bf16 inputs, times max(1, the largest |element| of the
+oracle's tensor) - a gradient element sums many (row, head) terms, so its fp32
+rounding scales with the gradient's size.  Outputs are pre-filled with NaN so that an element the
+GPU never writes fails.  At full size (the DSA and the 32K GQA workloads) the
+oracle's dq of sampled rows is compared, and two identities hold at any size:
+for each key head, the dk rows sum to zero (the softmax Jacobian's rows sum to
+zero) and the dv rows sum to the dO rows of the (row, head) pairs that have
+keys (each such softmax sums to one).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from csa_inputs import make_workload, tiny_block_workload, tiny_token_workload
+from parity import TOL, upload, poisoned
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+if torch.cuda.is_available():
+    import context_sparse_attention_amd as csa
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _fwd_bwd(w, d, idx, dout_np, out_dtype=torch.float32):
+    mode = csa.CSA_SEL_BLOCK if w.mode == "block" else csa.CSA_SEL_TOKEN
+    out, lse = csa.sparse_attn_fwd_shard(d["q"], d["k"], d["v"], d["layout"], mode, idx,
+                                         block_size=w.block_size, softmax_scale=w.scale,
+                                         out_dtype=out_dtype)
+    dout = torch.from_numpy(dout_np.astype(np.float32)).cuda().to(out_dtype)
+    dq = poisoned((w.n_q, w.hq, w.dqk), torch.float32)
+    dk = poisoned((w.n_kv, w.hkv, w.dqk), torch.float32)
+    dv = poisoned((w.n_kv, w.hkv, w.dv), torch.float32)
+    csa.sparse_attn_bwd_shard(d["q"], d["k"], d["v"], d["layout"], mode, idx, out, dout, lse,
+                              block_size=w.block_size, softmax_scale=w.scale, dq=dq, dk=dk,
+                              dv=dv)
+    torch.cuda.synchronize()
+    return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy(), dout.float().cpu().numpy()
+
+
+def _compare(w, idx_np, dout, got, tol, label):
+    dq, dk, dv = got
+    for name, a in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert np.isfinite(a).all(), f"{label}: {name} has unwritten or non-finite elements"
+    ref = oracle.shard_backward(w.q, w.k, w.value, w.q_pos, w.q_seq, w.cu_seqlens, w.mode,
+                                idx_np, w.scale, dout, w.block_size)
+    errs = {}
+    for name, a, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        # a gradient element sums many (row, head) terms: its fp32 rounding grows
+        # with the tensor's scale, so the bar is relative to its largest element
+        scale = max(1.0, float(np.abs(r).max()))
+        errs[name] = (float(np.abs(a - r).max()), scale)
+        assert errs[name][0] <= tol * scale, \
+            f"{label}: {name} max abs err {errs[name][0]:.3e} > {tol} x {scale:.3g}"
+    _say(label, {k: f"{v[0]:.2e} (scale {v[1]:.3g})" for k, v in errs.items()})
+
+
+BLOCK_CASES = [
+    dict(seed=60, lengths=(300, 212), layout="all", hq=4, hkv=2, d=64, block=64, topk=2),
+    dict(seed=61, lengths=(512,), layout="zigzag", cp=4, rank=1, hq=8, hkv=2, d=128, block=64,
+         topk=3),
+    dict(seed=62, lengths=(77, 300, 19, 116), layout="all", hq=4, hkv=4, d=128, block=64,
+         topk=4),
+    dict(seed=63, lengths=(300, 212), layout="all", hq=4, hkv=2, d=64, block=48, topk=3),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", range(len(BLOCK_CASES)))
+def test_block_backward_matches_oracle(case, dtype):
+    w = tiny_block_workload(dtype=dtype, **BLOCK_CASES[case])
+    _say("block backward", case, dtype, w.q.shape, w.k.shape)
+    d = upload(w)
+    idx = csa.moba_gate_topk(d["q"], d["k"], d["layout"], w.block_size, w.topk)
+    idx_np = idx.cpu().numpy()
+    dout = np.random.default_rng(case).standard_normal((w.n_q, w.hq, w.dv))
+    got = _fwd_bwd(w, d, idx, dout)
+    _compare(w, idx_np, got[3], got[:3], TOL[dtype], f"block {case} {dtype}")
+
+
+def test_block_backward_caller_slots_and_bf16_output():
+    """Pads, misaligned, future and repeated slots; rows without keys; the forward's
+    output in bf16 (D then uses the rounded output: the bf16 tolerance)."""
+    w = tiny_block_workload(seed=64, layout="all", lengths=(300, 420, 180), hq=4, hkv=2, d=64,
+                            block=64, topk=2, dtype="bf16")
+    q_seq = w.q_seq.copy()
+    q_seq[7] = 9
+    w.q_seq = q_seq
+    rng = np.random.default_rng(64)
+    W = 6
+    idx_np = rng.integers(-3, w.n_kv + 3, size=(w.n_q, w.hq, W)).astype(np.int32)
+    for i in range(w.n_q):
+        lo = int(w.cu_seqlens[w.q_seq[i]]) if 0 <= w.q_seq[i] < 3 else 0
+        for s in range(0, W, 2):
+            idx_np[i, :, s] = lo + w.block_size * rng.integers(0, 5, size=w.hq)
+    idx_np[::3, :, 1] = idx_np[::3, :, 0]
+    _say("block backward caller slots")
+    d = upload(w)
+    idx = torch.from_numpy(idx_np).cuda()
+    dout = rng.standard_normal((w.n_q, w.hq, w.dv))
+    got = _fwd_bwd(w, d, idx, dout, out_dtype=torch.bfloat16)
+    assert not got[0][7].any()
+    _compare(w, idx_np, got[3], got[:3], TOL["bf16"], "caller slots")
+
+
+TOKEN_CASES = [
+    dict(hq=16, dqk=64, dv=64, hi=4, di=32, topk=37, lengths=(300, 212)),
+    dict(hq=64, dqk=576, dv=512, hi=8, di=128, topk=100, lengths=(700,)),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", range(len(TOKEN_CASES)))
+def test_token_backward_matches_oracle(case, dtype):
+    """Indexer selection shared by all heads; the value aliases the key's first
+    columns (absorbed MLA), with dk and dv returned separately."""
+    w = tiny_token_workload(seed=65 + case, dtype=dtype, **TOKEN_CASES[case])
+    _say("token backward", case, dtype)
+    d = upload(w)
+    idx = csa.dsa_indexer_topk(d["iq"], d["ik"], d["w"], d["layout"], w.topk)
+    idx_np = idx.cpu().numpy()[:, None, :]
+    dout = np.random.default_rng(case).standard_normal((w.n_q, w.hq, w.dv))
+    got = _fwd_bwd(w, d, idx, dout)
+    _compare(w, idx_np, got[3], got[:3], TOL[dtype], f"token {case} {dtype}")
+
+
+def test_token_backward_per_head_index_with_pads_and_repeats():
+    w = tiny_token_workload(seed=67, hq=8, dqk=64, dv=64, lengths=(256,), dtype="bf16")
+    rng = np.random.default_rng(67)
+    idx_np = rng.integers(-5, w.n_kv + 5, size=(w.n_q, w.hq, 70)).astype(np.int32)
+    idx_np[:, :, 5] = idx_np[:, :, 4]
+    _say("token backward per-head idx")
+    d = upload(w)
+    dout = rng.standard_normal((w.n_q, w.hq, w.dv))
+    got = _fwd_bwd(w, d, torch.from_numpy(idx_np).cuda(), dout)
+    _compare(w, idx_np, got[3], got[:3], TOL["bf16"], "token per-head")
+
+
+def test_backward_is_bitwise_reproducible():
+    w = tiny_block_workload(seed=68, layout="all", lengths=(1000, 537), hq=8, hkv=2, d=128,
+                            block=64, topk=3, dtype="bf16")
+    _say("backward determinism")
+    d = upload(w)
+    idx = csa.moba_gate_topk(d["q"], d["k"], d["layout"], w.block_size, w.topk)
+    dout = np.random.default_rng(68).standard_normal((w.n_q, w.hq, w.dv))
+    a = _fwd_bwd(w, d, idx, dout)
+    b = _fwd_bwd(w, d, idx, dout)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def _identities(w, dq, dk, dv, dout, lse, label):
+    """Key-head sums: sum_j dk[j, g] = 0 and sum_j dv[j, g] = sum of dO over the
+    (row, head) pairs of key head g that have keys."""
+    group = w.hq // w.hkv
+    has = np.isfinite(lse)
+    for g in range(w.hkv):
+        hs = slice(g * group, (g + 1) * group)
+        dsum = (dout[:, hs] * has[:, hs, None]).sum(axis=(0, 1))
+        vs = dv[:, g].astype(np.float64).sum(axis=0)
+        assert np.abs(vs - dsum).max() <= 1e-3 * max(1.0, np.abs(dv[:, g]).sum(axis=0).max())
+        ks = dk[:, g].astype(np.float64).sum(axis=0)
+        assert np.abs(ks).max() <= 1e-3 * max(1.0, np.abs(dk[:, g]).sum(axis=0).max())
+    _say(label, "key-head sums hold")
+
+
+@pytest.mark.parametrize("name", ["moba_gqa_zigzag_32k", "dsa_mla_16k"])
+def test_full_size_backward(name):
+    w = make_workload(name)
+    _say("full-size backward", name)
+    d = upload(w)
+    if w.mode == "block":
+        idx = csa.moba_gate_topk(d["q"], d["k"], d["layout"], w.block_size, w.topk)
+        idx_np = idx.cpu().numpy()
+    else:
+        idx = csa.dsa_indexer_topk(d["iq"], d["ik"], d["w"], d["layout"], w.topk)
+        idx_np = idx.cpu().numpy()[:, None, :]
+    mode = csa.CSA_SEL_BLOCK if w.mode == "block" else csa.CSA_SEL_TOKEN
+    out, lse = csa.sparse_attn_fwd_shard(d["q"], d["k"], d["v"], d["layout"], mode, idx,
+                                         block_size=w.block_size, softmax_scale=w.scale,
+                                         out_dtype=torch.float32)
+    dout_np = (np.random.default_rng(7).standard_normal((w.n_q, w.hq, w.dv))
+               .astype(np.float32))
+    dout = torch.from_numpy(dout_np).cuda()
+    dq = poisoned((w.n_q, w.hq, w.dqk), torch.float32)
+    dk = poisoned((w.n_kv, w.hkv, w.dqk), torch.float32)
+    dv = poisoned((w.n_kv, w.hkv, w.dv), torch.float32)
+    csa.sparse_attn_bwd_shard(d["q"], d["k"], d["v"], d["layout"], mode, idx, out, dout, lse,
+                              block_size=w.block_size, softmax_scale=w.scale, dq=dq, dk=dk,
+                              dv=dv)
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+    lse_np = lse.cpu().numpy()
+    for n_, a in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert np.isfinite(a).all(), f"{n_} has unwritten or non-finite elements"
+    _identities(w, dq, dk, dv, dout_np.astype(np.float64), lse_np, name)
+    # dq of sampled rows: the oracle's backward restricted to those rows (their dk
+    # and dv contributions are ignored here)
+    rows = np.unique(np.concatenate([[0, w.n_q - 1, w.n_q // 2],
+                                     np.random.default_rng(8).choice(w.n_q, 13, replace=False)]))
+    sub_idx = idx_np[rows]
+    ref_dq, _, _ = oracle.shard_backward(w.q[rows], w.k, w.value, w.q_pos[rows], w.q_seq[rows],
+                                         w.cu_seqlens, w.mode, sub_idx, w.scale, dout_np[rows],
+                                         w.block_size)
+    err = float(np.abs(dq[rows] - ref_dq).max())
+    _say(name, "dq rows", len(rows), "max abs err", f"{err:.3e}")
+    assert err <= TOL["bf16"]
