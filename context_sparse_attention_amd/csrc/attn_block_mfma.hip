@@ -1058,10 +1058,12 @@ hipError_t launch_d(const AttnKernelArgs& a, int n_blocks, void* ws, hipStream_t
   const int64_t pairs = (int64_t)a.L.n_q * hq;
   const int per_wg = kHistThreads / (D / 8);
   const dim3 mgrid((unsigned)((pairs + per_wg - 1) / per_wg));
+  trace_begin(stream, "k_bm_merge", &slot);
   if (a.out_dtype == CSA_BF16)
     hipLaunchKernelGGL((k_bm_merge<D, __bf16>), mgrid, dim3(kHistThreads), 0, stream, a, w);
   else
     hipLaunchKernelGGL((k_bm_merge<D, float>), mgrid, dim3(kHistThreads), 0, stream, a, w);
+  trace_end(stream, slot);
   return hipGetLastError();
 }
 

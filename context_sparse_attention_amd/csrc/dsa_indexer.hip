@@ -840,15 +840,19 @@ hipError_t launch_typed(const DsaArgs& a, hipStream_t stream) {
     }
   }
   trace_end(stream, slot);
+  trace_begin(stream, "k_dsa_select_reg", &slot);
   const int grid = a.L.n_q;  // one row per workgroup
   hipLaunchKernelGGL(k_dsa_select_reg, dim3(grid), dim3(kRgThreads), 0, stream, a.L, a.topk,
                      logits, a.idx, a.score);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.max_span <= kRgSpan) return e;
-  // rows longer than the register-resident span
-  hipLaunchKernelGGL(k_dsa_select, dim3(a.L.n_q), dim3(kSelThreads), 0, stream, a.L,
-                     a.topk, logits, a.idx, a.score, kRgSpan);
-  return hipGetLastError();
+  if (e == hipSuccess && a.max_span > kRgSpan) {
+    // rows longer than the register-resident span
+    hipLaunchKernelGGL(k_dsa_select, dim3(a.L.n_q), dim3(kSelThreads), 0, stream, a.L,
+                       a.topk, logits, a.idx, a.score, kRgSpan);
+    e = hipGetLastError();
+  }
+  trace_end(stream, slot);
+  return e;
 }
 
 }  // namespace
