@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=20.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cold", action="store_true")
+    p.add_argument("--no-backward", action="store_true",
+                   help="skip the backward stage (sparse_attn_bwd_shard) of the headline")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device-to-device copy of known size (the reference "
                         "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -287,7 +289,58 @@ def _q(xs, p):
     return float(np.percentile(np.asarray(xs, np.float64), p))
 
 
-def measure(torch, csa, w, steps, warmup, cold=True, up_proj=False, timed_steps=None):
+def backward_stage(torch, csa, w, q, k, v, lay, idx, mode, out_dtype, reps=1):
+    """sparse_attn_bwd_shard after the forward on the step's selection: the mean time
+    of `reps` calls (events around each call, after one untimed call), its kernels,
+    and the algorithmic rate.  Algorithmic flops per selected pair: the logits
+    recomputed (2 Dqk), dP (2 Dv), dV (2 Dv), dQ (2 Dqk) and dK (2 Dqk), priced
+    against the fp32 vector peak (the kernels run on the vector ALUs)."""
+    out, lse = csa.sparse_attn_fwd_shard(q, k, v, lay, mode, idx, block_size=w.block_size,
+                                         softmax_scale=w.scale, out_dtype=out_dtype)
+    dout = torch.randn(out.shape, generator=torch.Generator(device="cuda").manual_seed(1),
+                       device="cuda", dtype=torch.float32).to(out_dtype)
+    ws_bytes = csa.lib.sparse_attn_bwd_shard_workspace_size(
+        lay.c, mode, w.hq, w.hkv, 1 if idx.dim() == 2 else idx.shape[1],
+        idx.shape[-1], w.block_size)
+    dq = torch.empty((w.n_q, w.hq, w.dqk), dtype=torch.float32, device="cuda")
+    dk = torch.empty((w.n_kv, w.hkv, w.dqk), dtype=torch.float32, device="cuda")
+    dv = torch.empty((w.n_kv, w.hkv, w.dv), dtype=torch.float32, device="cuda")
+
+    def call():
+        csa.sparse_attn_bwd_shard(q, k, v, lay, mode, idx, out, dout, lse,
+                                  block_size=w.block_size, softmax_scale=w.scale, dq=dq, dk=dk,
+                                  dv=dv)
+
+    call()
+    torch.cuda.synchronize()
+    csa.trace_begin(8 * reps + 8)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for r in range(reps):
+        call()
+        ev[r + 1].record(stream)
+    torch.cuda.synchronize()
+    traced = csa.trace_collect()
+    csa.trace_begin(0)
+    ms = [ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]
+    kern = {}
+    for name, t in traced:
+        kern.setdefault(name, []).append(t)
+    pairs = effective_pairs(w.mode, w.cu_seqlens, w.q_seq, w.q_pos, w.hq, w.block_size,
+                            idx.cpu().numpy())
+    flops = pairs * 2.0 * (3 * w.dqk + 2 * w.dv)
+    mean = float(np.mean(ms))
+    return {"call": "sparse_attn_bwd_shard", "ms": mean, "ms_min": float(np.min(ms)),
+            "alg_gflop": flops / 1e9, "TFLOPs": flops / (mean * 1e-3) / 1e12,
+            "bound": "alu", "peak": PEAK_FP32_TFLOPS,
+            "frac": flops / (mean * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+            "kernels_ms": {k_: float(np.mean(v_)) for k_, v_ in kern.items()},
+            "reps": reps}
+
+
+def measure(torch, csa, w, steps, warmup, cold=True, up_proj=False, timed_steps=None,
+            backward=False):
     """Everything measured on one workload; returns a dict (headline fields included)."""
     dev = "cuda"
 
@@ -436,6 +489,10 @@ def measure(torch, csa, w, steps, warmup, cold=True, up_proj=False, timed_steps=
                   "GBs": up_bytes / (up_ms * 1e-3) / 1e9,
                   "frac_hbm": up_bytes / (up_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
+    bwd_res = None
+    if backward:
+        bwd_res = backward_stage(torch, csa, w, q, k, v, lay, select(), mode, out_dtype)
+
     att_med, sel_med = _q(att_ms, 50), _q(sel_ms, 50)
     for dom in ("k_bm_attn", "k_tok_attn", "k_attn_generic"):
         if dom in kern:
@@ -478,6 +535,7 @@ def measure(torch, csa, w, steps, warmup, cold=True, up_proj=False, timed_steps=
         "graph_replays_checked": replays,
         "cold": cold_res,
         "v_up_proj": up_res,
+        "backward": bwd_res,
         "peak": peak,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
     }
@@ -528,7 +586,7 @@ def main():
 
     w = make_workload(args.workload)
     head = measure(torch, csa, w, args.steps, args.warmup, cold=not args.no_cold, up_proj=True,
-                   timed_steps=args.steps)
+                   timed_steps=args.steps, backward=not args.no_backward)
     stages[w.name] = head
     dom = head["attention_kernel"]
     result = {

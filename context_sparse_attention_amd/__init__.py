@@ -16,6 +16,7 @@ from ._binding import (
     GATE_SCRATCH_BYTES,
     dsa_indexer_topk,
     sparse_attn_fwd_shard,
+    sparse_attn_fwd_shard_kernel,
     sparse_attn_bwd_shard,
     summary_merge,
     mla_v_up_proj,
@@ -35,6 +36,7 @@ __all__ = [
     "GATE_SCRATCH_BYTES",
     "dsa_indexer_topk",
     "sparse_attn_fwd_shard",
+    "sparse_attn_fwd_shard_kernel",
     "sparse_attn_bwd_shard",
     "summary_merge",
     "mla_v_up_proj",

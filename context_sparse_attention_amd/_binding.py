@@ -69,6 +69,9 @@ lib.sparse_attn_bwd_shard_workspace_size.argtypes = [_LP, _i32, _i32, _i32, _i32
 lib.sparse_attn_bwd_shard.restype = ctypes.c_int
 lib.sparse_attn_bwd_shard.argtypes = [_T3, _T3, _T3, _LP, _i32, _P, _i32, _i32, _i32, _f32,
                                       _T3, _T3, _P, _P, _P, _P, _P, _sz, _P]
+lib.sparse_attn_fwd_shard_kernel.restype = ctypes.c_char_p
+lib.sparse_attn_fwd_shard_kernel.argtypes = [_T3, _T3, _T3, _LP, _i32, _i32, _i32, _i32, _f32,
+                                             _i32]
 lib.csa_trace_begin.restype = ctypes.c_int
 lib.csa_trace_begin.argtypes = [ctypes.c_int]
 lib.csa_trace_collect.restype = ctypes.c_int
@@ -239,6 +242,22 @@ def sparse_attn_fwd_shard(q, k, v, layout, mode, idx, block_size=0, softmax_scal
                                      float(softmax_scale), out.data_ptr(), _dtype_code(out),
                                      _ptr(lse), ws.data_ptr(), ws.numel(), _stream()))
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def sparse_attn_fwd_shard_kernel(q, k, v, layout, mode, idx_heads, idx_width, block_size=0,
+                                 softmax_scale=None, out_dtype=None):
+    """The kernel family sparse_attn_fwd_shard runs for these arguments:
+    "block_mfma", "token_mfma" or "generic"."""
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(q.shape[2])
+    out_dtype = out_dtype or q.dtype
+    name = lib.sparse_attn_fwd_shard_kernel(
+        ctypes.byref(_tensor3(q)), ctypes.byref(_tensor3(k)), ctypes.byref(_tensor3(v)),
+        layout.c, mode, idx_heads, idx_width, block_size, float(softmax_scale),
+        CSA_BF16 if out_dtype == torch.bfloat16 else CSA_F32)
+    if name is None:
+        raise CsaError(1, lib.csa_last_error().decode())
+    return name.decode()
 
 
 def sparse_attn_bwd_shard(q, k, v, layout, mode, idx, out, dout, lse, block_size=0,

@@ -162,6 +162,61 @@ csa_status device_scratch(void** ptr) {
   return CSA_OK;
 }
 
+// Host checks and kernel arguments of an attention call (everything but the
+// index, output, lse and workspace pointers).
+csa_status attn_args(const csa_tensor3* q, const csa_tensor3* k, const csa_tensor3* v,
+                     const csa_layout* L, int32_t mode, int32_t idx_heads, int32_t idx_width,
+                     int32_t block_size, float softmax_scale, int32_t out_dtype, AttnArgs* a) {
+  csa_status st;
+  if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) ||
+      (st = check_tensor(v, "v")) || (st = check_layout(L)))
+    return st;
+  if (q->dtype != k->dtype || k->dtype != v->dtype)
+    return fail(CSA_ERR_INVALID_ARG, "q, k, v dtypes differ");
+  if (q->n != L->n_q) return fail(CSA_ERR_INVALID_ARG, "q rows %lld != n_q %d",
+                                  (long long)q->n, L->n_q);
+  if (k->n != L->n_kv || v->n != L->n_kv)
+    return fail(CSA_ERR_INVALID_ARG, "k/v tokens != n_kv %d", L->n_kv);
+  if (q->d != k->d) return fail(CSA_ERR_INVALID_ARG, "q and k head dims differ");
+  if (k->h != v->h) return fail(CSA_ERR_INVALID_ARG, "k and v head counts differ");
+  if (q->h % k->h) return fail(CSA_ERR_INVALID_ARG, "Hq %d not a multiple of Hkv %d", q->h, k->h);
+  if (q->d > 576) return fail(CSA_ERR_UNSUPPORTED, "head dim %d > 576", q->d);
+  if (v->d > 512) return fail(CSA_ERR_UNSUPPORTED, "value dim %d > 512", v->d);
+  if (mode != CSA_SEL_BLOCK && mode != CSA_SEL_TOKEN)
+    return fail(CSA_ERR_INVALID_ARG, "mode %d", mode);
+  if (mode == CSA_SEL_BLOCK && block_size < 1)
+    return fail(CSA_ERR_INVALID_ARG, "block_size %d", block_size);
+  if (idx_heads != 1 && idx_heads != q->h)
+    return fail(CSA_ERR_INVALID_ARG, "idx_heads %d must be 1 or Hq %d", idx_heads, q->h);
+  if (idx_width < 1) return fail(CSA_ERR_INVALID_ARG, "idx_width %d", idx_width);
+  if (out_dtype != CSA_F32 && out_dtype != CSA_BF16)
+    return fail(CSA_ERR_INVALID_ARG, "out_dtype %d", out_dtype);
+  if (!isfinite(softmax_scale)) return fail(CSA_ERR_INVALID_ARG, "softmax_scale not finite");
+  if ((int64_t)L->n_q * idx_heads * idx_width >= ((int64_t)1 << 31) ||
+      (int64_t)L->n_q * q->h * idx_width >= ((int64_t)1 << 31))
+    return fail(CSA_ERR_UNSUPPORTED, "index too large");
+  int64_t nb = 0;
+  if (mode == CSA_SEL_BLOCK) nb = count_blocks(L->cu_seqlens_host, L->n_seq, block_size);
+  if (nb >= ((int64_t)1 << 30)) return fail(CSA_ERR_UNSUPPORTED, "too many blocks");
+  a->q = make_view(q);
+  a->k = make_view(k);
+  a->v = make_view(v);
+  a->L = make_dev_layout(L);
+  a->mode = mode;
+  a->idx_heads = idx_heads;
+  a->idx_width = idx_width;
+  a->block_size = block_size;
+  a->n_blocks = (int)nb;
+  a->dtype = q->dtype;
+  a->out_dtype = out_dtype;
+  a->idx = nullptr;
+  a->scale = softmax_scale;
+  a->out = nullptr;
+  a->lse = nullptr;
+  a->ws = nullptr;
+  return CSA_OK;
+}
+
 template <typename F>
 csa_status guarded(F&& f) {
   try {
@@ -310,56 +365,17 @@ csa_status sparse_attn_fwd_shard(const csa_tensor3* q, const csa_tensor3* k,
                                  int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
                                  void* stream) {
   return guarded([&]() -> csa_status {
+    AttnArgs a;
     csa_status st;
-    if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) ||
-        (st = check_tensor(v, "v")) || (st = check_layout(L)))
+    if ((st = attn_args(q, k, v, L, mode, idx_heads, idx_width, block_size, softmax_scale,
+                        out_dtype, &a)))
       return st;
-    if (q->dtype != k->dtype || k->dtype != v->dtype)
-      return fail(CSA_ERR_INVALID_ARG, "q, k, v dtypes differ");
-    if (q->n != L->n_q) return fail(CSA_ERR_INVALID_ARG, "q rows %lld != n_q %d",
-                                    (long long)q->n, L->n_q);
-    if (k->n != L->n_kv || v->n != L->n_kv)
-      return fail(CSA_ERR_INVALID_ARG, "k/v tokens != n_kv %d", L->n_kv);
-    if (q->d != k->d) return fail(CSA_ERR_INVALID_ARG, "q and k head dims differ");
-    if (k->h != v->h) return fail(CSA_ERR_INVALID_ARG, "k and v head counts differ");
-    if (q->h % k->h) return fail(CSA_ERR_INVALID_ARG, "Hq %d not a multiple of Hkv %d", q->h, k->h);
-    if (q->d > 576) return fail(CSA_ERR_UNSUPPORTED, "head dim %d > 576", q->d);
-    if (v->d > 512) return fail(CSA_ERR_UNSUPPORTED, "value dim %d > 512", v->d);
-    if (mode != CSA_SEL_BLOCK && mode != CSA_SEL_TOKEN)
-      return fail(CSA_ERR_INVALID_ARG, "mode %d", mode);
-    if (mode == CSA_SEL_BLOCK && block_size < 1)
-      return fail(CSA_ERR_INVALID_ARG, "block_size %d", block_size);
-    if (idx_heads != 1 && idx_heads != q->h)
-      return fail(CSA_ERR_INVALID_ARG, "idx_heads %d must be 1 or Hq %d", idx_heads, q->h);
-    if (idx_width < 1) return fail(CSA_ERR_INVALID_ARG, "idx_width %d", idx_width);
-    if (out_dtype != CSA_F32 && out_dtype != CSA_BF16)
-      return fail(CSA_ERR_INVALID_ARG, "out_dtype %d", out_dtype);
-    if (!isfinite(softmax_scale)) return fail(CSA_ERR_INVALID_ARG, "softmax_scale not finite");
     if (L->n_q > 0 && (!idx || !out)) return fail(CSA_ERR_INVALID_ARG, "null idx or out");
     if (out && !aligned16(out)) return fail(CSA_ERR_INVALID_ARG, "out not 16-byte aligned");
-    if ((int64_t)L->n_q * idx_heads * idx_width >= ((int64_t)1 << 31) ||
-        (int64_t)L->n_q * q->h * idx_width >= ((int64_t)1 << 31))
-      return fail(CSA_ERR_UNSUPPORTED, "index too large");
-    int64_t nb = 0;
-    if (mode == CSA_SEL_BLOCK) nb = count_blocks(L->cu_seqlens_host, L->n_seq, block_size);
-    if (nb >= ((int64_t)1 << 30)) return fail(CSA_ERR_UNSUPPORTED, "too many blocks");
-    const size_t need = attn_ws_bytes(L->n_q, L->n_seq, (int)nb, mode, q->h, k->h, v->d,
+    const size_t need = attn_ws_bytes(L->n_q, L->n_seq, a.n_blocks, mode, q->h, k->h, v->d,
                                       idx_width);
     if ((st = check_ws(ws, ws_bytes, need))) return st;
-    AttnArgs a;
-    a.q = make_view(q);
-    a.k = make_view(k);
-    a.v = make_view(v);
-    a.L = make_dev_layout(L);
-    a.mode = mode;
-    a.idx_heads = idx_heads;
-    a.idx_width = idx_width;
-    a.block_size = block_size;
-    a.n_blocks = (int)nb;
-    a.dtype = q->dtype;
-    a.out_dtype = out_dtype;
     a.idx = idx;
-    a.scale = softmax_scale;
     a.out = out;
     a.lse = lse;
     a.ws = ws;
@@ -367,6 +383,24 @@ csa_status sparse_attn_fwd_shard(const csa_tensor3* q, const csa_tensor3* k,
     if (e != hipSuccess) return hip_fail(e, "sparse_attn_fwd_shard");
     return CSA_OK;
   });
+}
+
+const char* sparse_attn_fwd_shard_kernel(const csa_tensor3* q, const csa_tensor3* k,
+                                         const csa_tensor3* v, const csa_layout* L,
+                                         int32_t mode, int32_t idx_heads, int32_t idx_width,
+                                         int32_t block_size, float softmax_scale,
+                                         int32_t out_dtype) {
+  const char* name = nullptr;
+  guarded([&]() -> csa_status {
+    AttnArgs a;
+    csa_status st;
+    if ((st = attn_args(q, k, v, L, mode, idx_heads, idx_width, block_size, softmax_scale,
+                        out_dtype, &a)))
+      return st;
+    name = attention_kernel_family(a);
+    return CSA_OK;
+  });
+  return name;
 }
 
 size_t sparse_attn_bwd_shard_workspace_size(const csa_layout* L, int32_t mode, int32_t hq,

@@ -10,7 +10,8 @@ size_t attn_ws_bytes(int n_q, int n_seq, int n_blocks, int mode, int hq, int hkv
   return 256;
 }
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
+namespace {
+AttnKernelArgs kernel_args(const AttnArgs& a) {
   AttnKernelArgs k;
   k.q = a.q;
   k.k = a.k;
@@ -26,6 +27,19 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
   k.scale_log2 = a.scale * 1.4426950408889634f;
   k.out = a.out;
   k.lse = a.lse;
+  return k;
+}
+}  // namespace
+
+const char* attention_kernel_family(const AttnArgs& a) {
+  const AttnKernelArgs k = kernel_args(a);
+  if (attn_block_mfma_supported(k, a.n_blocks)) return "block_mfma";
+  if (attn_token_mfma_supported(k)) return "token_mfma";
+  return "generic";
+}
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
+  const AttnKernelArgs k = kernel_args(a);
   if (attn_block_mfma_supported(k, a.n_blocks)) return launch_attn_block_mfma(k, a.n_blocks, a.ws, stream);
   if (attn_token_mfma_supported(k)) return launch_attn_token_mfma(k, stream);
   return launch_attn_generic(k, stream);

@@ -36,6 +36,7 @@
 // in the B-operand layout of the O^T = V^T P^T product (the contraction index
 // is permuted consistently on both operands).  V is stored transposed in LDS.
 #include "attention.hpp"
+#include "gather.hpp"
 
 namespace csa {
 
@@ -472,29 +473,6 @@ struct Lds {
   __bf16 k[2][kTN * kKP];
   __bf16 v[2][kTN * kVR];
 };
-
-// One global_load_lds_dwordx4: 1 KiB of LDS from m0 on, lane l writing bytes
-// [16 l, 16 l + 16), read from base + off.  Issued as assembly so that the
-// compiler does not see an LDS store: it would otherwise wait for the gather
-// before every later LDS read of the tile being computed.  The gathered tile
-// is read only after the explicit wait and barrier that close the tile during
-// which it was issued.  The kernels of this file have no other use of m0.
-__device__ __forceinline__ void gather16(uint32_t off, const char* base, uint32_t lds_dst) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(off), "s"(base), "s"(lds_dst)
-               : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(0) (gfx9 encoding, the other counters left alone)
-__device__ __forceinline__ void wait_gathers() {
-  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  typedef __attribute__((address_space(3))) const char* lds_bytes;
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_bytes)p));
-}
 
 // The gather of one key/value tile, split over the workgroup's waves in 1 KiB
 // chunks: chunk c of a tile is issued by wave c % kWaves.  Lane l of chunk c

@@ -23,6 +23,7 @@
 // rescaled.  Chunk summaries merge exactly as in "Context parallel attention:
 // exchange keys and merge softmax globally" (chunk summary paragraph).
 #include "attention.hpp"
+#include "gather.hpp"
 #include "mfma.hpp"
 
 namespace csa {
@@ -75,11 +76,6 @@ __device__ __forceinline__ bf16x4 read_tr(const __bf16* lds_base, int byte_off) 
   return __builtin_bit_cast(bf16x4, x);
 }
 
-// Gathers one tile straight into LDS with global_load_lds_dwordx4: an
-// instruction fills 1 KiB of LDS, lane l writing bytes [16 l, 16 l + 16) of
-// it, so each lane loads the 16 bytes that the padded, swizzled layout puts at
-// its destination (pad slots re-read unit 0 of their row).  The tile sizes are
-// whole KiBs (32 rows of 2 (D + 16) bytes).  No registers hold the data.
 // x * s for an accumulator value that stays in an accumulator register
 // (VALU instructions cannot read accumulator registers directly).
 __device__ __forceinline__ float acc_scale(float x, float s) {
@@ -93,18 +89,13 @@ __device__ __forceinline__ float acc_scale(float x, float s) {
   return y;
 }
 
-// One global_load_lds_dwordx4 (1 KiB of LDS from m0 on, 16 bytes per lane).
-// Issued as assembly so that the compiler does not see an LDS store: it would
-// otherwise wait for the gather before every later LDS read of the current
-// tile.  The gathered tile is read only after the explicit wait and barrier at
-// the end of the tile that issued it.  This kernel has no other use of m0.
-__device__ __forceinline__ void gather16(const void* src, uint32_t lds_dst) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(lds_dst)
-               : "memory", "m0");
-}
-
+// Gathers one tile straight into LDS with global_load_lds_dwordx4: an
+// instruction fills 1 KiB of LDS, lane l writing bytes [16 l, 16 l + 16) of
+// it, so each lane loads the 16 bytes that the padded, swizzled layout puts at
+// its destination (pad slots re-read unit 0 of their row).  The tile sizes are
+// whole KiBs (32 rows of 2 (D + 16) bytes).  No registers hold the data.
+// (gather16_addr of gather.hpp: one instruction per KiB, the source as a
+// 64-bit address per lane, since a chunk spans rows of different tokens).
 template <int D>
 __device__ __forceinline__ void issue_tile(const View& T, int g, const int* keys, __bf16* tile,
                                            int wave, int nwaves) {
@@ -121,7 +112,7 @@ __device__ __forceinline__ void issue_tile(const View& T, int g, const int* keys
     const __bf16* src = elem_ptr<__bf16>(T, keys[row], g) + u * 8;
     const uint32_t dst = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((lds_bytes)(void*)tile + ch * 1024));
-    gather16(src, __builtin_amdgcn_readfirstlane(dst));
+    gather16_addr(src, __builtin_amdgcn_readfirstlane(dst));
   }
 }
 

@@ -185,6 +185,8 @@ struct AttnArgs {
 size_t attn_ws_bytes(int n_q, int n_seq, int n_blocks, int mode, int hq, int hkv, int dv,
                      int idx_width);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+// "block_mfma", "token_mfma" or "generic": the kernel family launch_attention picks
+const char* attention_kernel_family(const AttnArgs& a);
 
 struct AttnBwdArgs {
   View q, k, v;

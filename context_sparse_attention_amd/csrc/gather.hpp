@@ -21,6 +21,15 @@ __device__ __forceinline__ void gather16(uint32_t off, const char* base, uint32_
                : "memory", "m0");
 }
 
+// The same gather with a full 64-bit address per lane (rows of different
+// tokens within one 1 KiB chunk, where no common base exists).
+__device__ __forceinline__ void gather16_addr(const void* src, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_dst)
+               : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(0) (gfx9 encoding, the other counters left alone)
 __device__ __forceinline__ void wait_gathers() {
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));

@@ -206,6 +206,26 @@ csa_status sparse_attn_fwd_shard(const csa_tensor3* q, const csa_tensor3* k,
                                  void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * sparse_attn_fwd_shard_kernel - which kernel family sparse_attn_fwd_shard runs for
+ * these arguments (the data pointers are not read; only shapes, dtypes and the
+ * layout's host sequence starts are):
+ *   "block_mfma"  block mode on the matrix cores: bf16, D = Dqk = Dv in {64, 128},
+ *                 block_size a multiple of 64, a power-of-two group Hq/Hkv <= 128,
+ *                 idx_width <= 64, at most 16384 (key head, block) lists;
+ *   "token_mfma"  token mode on the matrix cores: bf16, one index row per token,
+ *                 (Dqk, Dv) in {(576, 512), (128, 128), (64, 64)}, Hq/Hkv in
+ *                 {32, 64, 128};
+ *   "generic"     everything else: one wavefront per (row, head), fp32 arithmetic.
+ * A positive softmax_scale is required by both MFMA families.  Returns a static
+ * string, or NULL (with csa_last_error set) when the arguments would be rejected.
+ * ------------------------------------------------------------------------------- */
+const char* sparse_attn_fwd_shard_kernel(const csa_tensor3* q, const csa_tensor3* k,
+                                         const csa_tensor3* v, const csa_layout* L,
+                                         int32_t mode, int32_t idx_heads, int32_t idx_width,
+                                         int32_t block_size, float softmax_scale,
+                                         int32_t out_dtype);
+
+/* ---------------------------------------------------------------------------------
  * sparse_attn_bwd_shard - gradients of sparse_attn_fwd_shard with the selection held
  * fixed [CPA, paragraph on positions and masks: the backward returns key and value
  * gradients to their owners; MLM#4878 "Strategy: allgather CP mode", backward step:

@@ -168,3 +168,33 @@ def test_noalloc_gate_rejects_shapes_beyond_its_scratch_on_the_host():
     st = B.lib.moba_gate_topk_noalloc(ctypes.byref(q), ctypes.byref(t3(8192, 3, 128)), L.c,
                                       64, 2, 1 << 20, None, None)
     assert st == 1
+
+
+def kernel_of(q, k, v, L, mode, idx_heads, width, block=0, scale=0.1, out=B.CSA_BF16):
+    name = B.lib.sparse_attn_fwd_shard_kernel(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                                              L.c, mode, idx_heads, width, block, scale, out)
+    return None if name is None else name.decode()
+
+
+def test_kernel_family_query_names_the_path_each_shape_takes():
+    # the DSA shard: 128 heads over one 576-wide latent key, value = its first 512 columns
+    L = FakeLayout([0, 16384], 4096)
+    k = t3(16384, 1, 576)
+    v = t3(16384, 1, 512, sn=576, sh=576)
+    assert kernel_of(t3(4096, 128, 576), k, v, L, B.CSA_SEL_TOKEN, 1, 2048) == "token_mfma"
+    # per-head index rows in token mode: the general kernel
+    assert kernel_of(t3(4096, 128, 576), k, v, L, B.CSA_SEL_TOKEN, 128, 16) == "generic"
+    # the 32K GQA MoBA shard
+    L = FakeLayout([0, 32768], 8192)
+    kv = t3(32768, 8, 128)
+    assert kernel_of(t3(8192, 32, 128), kv, kv, L, B.CSA_SEL_BLOCK, 32, 5, 1024) == "block_mfma"
+    # blocks not a multiple of 64, fp32 inputs, or a non-positive scale: the general kernel
+    assert kernel_of(t3(8192, 32, 128), kv, kv, L, B.CSA_SEL_BLOCK, 32, 5, 48) == "generic"
+    f32 = t3(32768, 8, 128, dtype=B.CSA_F32)
+    assert kernel_of(t3(8192, 32, 128, dtype=B.CSA_F32), f32, f32, L, B.CSA_SEL_BLOCK, 32, 5,
+                     1024) == "generic"
+    assert kernel_of(t3(8192, 32, 128), kv, kv, L, B.CSA_SEL_BLOCK, 32, 5, 1024,
+                     scale=-0.1) == "generic"
+    # rejected arguments: NULL and an error text
+    assert kernel_of(t3(8192, 32, 128), kv, kv, L, 7, 32, 5, 1024) is None
+    assert "mode" in B.lib.csa_last_error().decode()

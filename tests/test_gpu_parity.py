@@ -406,6 +406,11 @@ def test_named_block_workload(name):
     w = make_workload(name)
     _say("workload", name, w.q.shape, w.k.shape)
     d = upload(w)
+    family = csa.sparse_attn_fwd_shard_kernel(d["q"], d["k"], d["v"], d["layout"],
+                                              csa.CSA_SEL_BLOCK, w.hq, w.topk + 1,
+                                              w.block_size, w.scale)
+    _say(name, "attention kernel family", family)
+    assert family == ("generic" if w.dtype == "f32" else "block_mfma")
     idx, idx_np, score_np = _gate(w, d)
     gate = oracle.gate_scores(w.q, w.k, w.q_pos, w.q_seq, w.cu_seqlens, w.block_size)
     counts = check_moba_indices(w, idx_np, gate)
@@ -428,6 +433,10 @@ def test_named_dsa_workload():
     _say("workload dsa_mla_16k")
     d = upload(w)
     assert d["v"].data_ptr() == d["k"].data_ptr()  # aliased latent value
+    family = csa.sparse_attn_fwd_shard_kernel(d["q"], d["k"], d["v"], d["layout"],
+                                              csa.CSA_SEL_TOKEN, 1, w.topk, 0, w.scale)
+    _say("dsa attention kernel family", family)
+    assert family == "token_mfma"
     idx, idx_np, score_np = _indexer(w, d)
     with OraclePool(_dsa_arrays(w, idx_np, score_np)) as pool:
         res = pool.dsa_check(range(w.n_q), dict(topk=w.topk, score_rel=INDEXER_SCORE_REL))
