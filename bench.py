@@ -294,14 +294,14 @@ def backward_stage(torch, csa, w, q, k, v, lay, idx, mode, out_dtype, reps=1):
     of `reps` calls (events around each call, after one untimed call), its kernels,
     and the algorithmic rate.  Algorithmic flops per selected pair: the logits
     recomputed (2 Dqk), dP (2 Dv), dV (2 Dv), dQ (2 Dqk) and dK (2 Dqk), priced
-    against the fp32 vector peak (the kernels run on the vector ALUs)."""
+    against the bf16 dense MFMA peak for the matrix-core kernels and against the
+    fp32 vector peak for the vector-ALU ones."""
     out, lse = csa.sparse_attn_fwd_shard(q, k, v, lay, mode, idx, block_size=w.block_size,
                                          softmax_scale=w.scale, out_dtype=out_dtype)
     dout = torch.randn(out.shape, generator=torch.Generator(device="cuda").manual_seed(1),
                        device="cuda", dtype=torch.float32).to(out_dtype)
-    ws_bytes = csa.lib.sparse_attn_bwd_shard_workspace_size(
-        lay.c, mode, w.hq, w.hkv, 1 if idx.dim() == 2 else idx.shape[1],
-        idx.shape[-1], w.block_size)
+    ws_bytes = csa.sparse_attn_bwd_shard_workspace_size(
+        q, k, v, lay, mode, 1 if idx.dim() == 2 else idx.shape[1], idx.shape[-1], w.block_size)
     dq = torch.empty((w.n_q, w.hq, w.dqk), dtype=torch.float32, device="cuda")
     dk = torch.empty((w.n_kv, w.hkv, w.dqk), dtype=torch.float32, device="cuda")
     dv = torch.empty((w.n_kv, w.hkv, w.dv), dtype=torch.float32, device="cuda")
@@ -331,10 +331,17 @@ def backward_stage(torch, csa, w, q, k, v, lay, idx, mode, out_dtype, reps=1):
                             idx.cpu().numpy())
     flops = pairs * 2.0 * (3 * w.dqk + 2 * w.dv)
     mean = float(np.mean(ms))
-    return {"call": "sparse_attn_bwd_shard", "ms": mean, "ms_min": float(np.min(ms)),
-            "alg_gflop": flops / 1e9, "TFLOPs": flops / (mean * 1e-3) / 1e12,
-            "bound": "alu", "peak": PEAK_FP32_TFLOPS,
-            "frac": flops / (mean * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+    family = csa.sparse_attn_bwd_shard_kernel(q, k, v, lay, mode,
+                                              1 if idx.dim() == 2 else idx.shape[1],
+                                              idx.shape[-1], w.block_size)
+    # the matrix-core kernels price against the bf16 dense peak, the vector-ALU
+    # ones against the fp32 vector peak
+    peak = PEAK_BF16_TFLOPS if family == "block_mfma" else PEAK_FP32_TFLOPS
+    return {"call": "sparse_attn_bwd_shard", "kernel_family": family, "ms": mean,
+            "ms_min": float(np.min(ms)), "alg_gflop": flops / 1e9,
+            "TFLOPs": flops / (mean * 1e-3) / 1e12,
+            "bound": "mfma" if family == "block_mfma" else "alu", "peak": peak,
+            "frac": flops / (mean * 1e-3) / 1e12 / peak,
             "kernels_ms": {k_: float(np.mean(v_)) for k_, v_ in kern.items()},
             "reps": reps}
 

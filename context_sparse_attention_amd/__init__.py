@@ -17,6 +17,8 @@ from ._binding import (
     dsa_indexer_topk,
     sparse_attn_fwd_shard,
     sparse_attn_fwd_shard_kernel,
+    sparse_attn_bwd_shard_kernel,
+    sparse_attn_bwd_shard_workspace_size,
     sparse_attn_bwd_shard,
     summary_merge,
     mla_v_up_proj,
@@ -37,6 +39,8 @@ __all__ = [
     "dsa_indexer_topk",
     "sparse_attn_fwd_shard",
     "sparse_attn_fwd_shard_kernel",
+    "sparse_attn_bwd_shard_kernel",
+    "sparse_attn_bwd_shard_workspace_size",
     "sparse_attn_bwd_shard",
     "summary_merge",
     "mla_v_up_proj",

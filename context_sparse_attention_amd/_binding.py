@@ -65,7 +65,11 @@ lib.sparse_attn_fwd_shard.restype = ctypes.c_int
 lib.sparse_attn_fwd_shard.argtypes = [_T3, _T3, _T3, _LP, _i32, _P, _i32, _i32, _i32, _f32,
                                       _P, _i32, _P, _P, _sz, _P]
 lib.sparse_attn_bwd_shard_workspace_size.restype = _sz
-lib.sparse_attn_bwd_shard_workspace_size.argtypes = [_LP, _i32, _i32, _i32, _i32, _i32, _i32]
+lib.sparse_attn_bwd_shard_workspace_size.argtypes = [_LP, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                     _i32, _i32, _i32]
+lib.sparse_attn_bwd_shard_kernel.restype = ctypes.c_char_p
+lib.sparse_attn_bwd_shard_kernel.argtypes = [_LP, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                             _i32, _i32]
 lib.sparse_attn_bwd_shard.restype = ctypes.c_int
 lib.sparse_attn_bwd_shard.argtypes = [_T3, _T3, _T3, _LP, _i32, _P, _i32, _i32, _i32, _f32,
                                       _T3, _T3, _P, _P, _P, _P, _P, _sz, _P]
@@ -260,6 +264,24 @@ def sparse_attn_fwd_shard_kernel(q, k, v, layout, mode, idx_heads, idx_width, bl
     return name.decode()
 
 
+def sparse_attn_bwd_shard_workspace_size(q, k, v, layout, mode, idx_heads, idx_width,
+                                         block_size=0):
+    """Workspace bytes of sparse_attn_bwd_shard for these tensors' shapes and dtype."""
+    return lib.sparse_attn_bwd_shard_workspace_size(
+        layout.c, mode, _dtype_code(q), q.shape[1], k.shape[1], q.shape[2], v.shape[2],
+        idx_heads, idx_width, block_size)
+
+
+def sparse_attn_bwd_shard_kernel(q, k, v, layout, mode, idx_heads, idx_width, block_size=0):
+    """The kernel family sparse_attn_bwd_shard runs: "block_mfma" or "generic"."""
+    name = lib.sparse_attn_bwd_shard_kernel(
+        layout.c, mode, _dtype_code(q), q.shape[1], k.shape[1], q.shape[2], v.shape[2],
+        idx_heads, idx_width, block_size)
+    if name is None:
+        raise CsaError(1, lib.csa_last_error().decode())
+    return name.decode()
+
+
 def sparse_attn_bwd_shard(q, k, v, layout, mode, idx, out, dout, lse, block_size=0,
                           softmax_scale=None, dq=None, dk=None, dv=None):
     """(dq, dk, dv) float32 of the forward's arguments, output, lse and dL/dout.
@@ -280,8 +302,8 @@ def sparse_attn_bwd_shard(q, k, v, layout, mode, idx, out, dout, lse, block_size
     dq = _out(dq, (layout.n_q, hq, q.shape[2]), torch.float32, dev, "dq")
     dk = _out(dk, (layout.n_kv, hkv, k.shape[2]), torch.float32, dev, "dk")
     dv = _out(dv, (layout.n_kv, hkv, v.shape[2]), torch.float32, dev, "dv")
-    ws_bytes = lib.sparse_attn_bwd_shard_workspace_size(layout.c, mode, hq, hkv, idx.shape[1],
-                                                        idx.shape[2], block_size)
+    ws_bytes = sparse_attn_bwd_shard_workspace_size(q, k, v, layout, mode, idx.shape[1],
+                                                    idx.shape[2], block_size)
     ws = _workspace(ws_bytes, dev)
     _check(lib.sparse_attn_bwd_shard(ctypes.byref(_tensor3(q)), ctypes.byref(_tensor3(k)),
                                      ctypes.byref(_tensor3(v)), layout.c, mode, idx.data_ptr(),

@@ -403,19 +403,43 @@ const char* sparse_attn_fwd_shard_kernel(const csa_tensor3* q, const csa_tensor3
   return name;
 }
 
-size_t sparse_attn_bwd_shard_workspace_size(const csa_layout* L, int32_t mode, int32_t hq,
-                                            int32_t hkv, int32_t idx_heads, int32_t idx_width,
-                                            int32_t block_size) {
+// Block count of a backward's shape arguments, or -1 when they are malformed.
+static int64_t bwd_shape_blocks(const csa_layout* L, int32_t mode, int32_t dtype, int32_t hq,
+                                int32_t hkv, int32_t dqk, int32_t dv, int32_t idx_heads,
+                                int32_t idx_width, int32_t block_size) {
   if (!L || !L->cu_seqlens_host || L->n_seq < 1 || L->n_q < 0 || L->n_kv < 0 || hq < 1 ||
-      hkv < 1 || idx_heads < 1 || idx_width < 1)
-    return 0;
-  int64_t nb = 0;
-  if (mode == CSA_SEL_BLOCK) {
-    if (block_size < 1) return 0;
-    nb = count_blocks(L->cu_seqlens_host, L->n_seq, block_size);
+      hkv < 1 || dqk < 1 || dv < 1 || idx_heads < 1 || idx_width < 1 ||
+      (dtype != CSA_F32 && dtype != CSA_BF16) || (mode != CSA_SEL_BLOCK && mode != CSA_SEL_TOKEN))
+    return -1;
+  if (mode != CSA_SEL_BLOCK) return 0;
+  if (block_size < 1) return -1;
+  const int64_t nb = count_blocks(L->cu_seqlens_host, L->n_seq, block_size);
+  return nb >= ((int64_t)1 << 30) ? -1 : nb;
+}
+
+size_t sparse_attn_bwd_shard_workspace_size(const csa_layout* L, int32_t mode, int32_t dtype,
+                                            int32_t hq, int32_t hkv, int32_t dqk, int32_t dv,
+                                            int32_t idx_heads, int32_t idx_width,
+                                            int32_t block_size) {
+  const int64_t nb =
+      bwd_shape_blocks(L, mode, dtype, hq, hkv, dqk, dv, idx_heads, idx_width, block_size);
+  if (nb < 0) return 0;
+  return attn_bwd_ws_bytes(L->n_q, L->n_kv, L->n_seq, (int)nb, mode, dtype, hq, hkv, dqk, dv,
+                           idx_heads, idx_width, block_size);
+}
+
+const char* sparse_attn_bwd_shard_kernel(const csa_layout* L, int32_t mode, int32_t dtype,
+                                         int32_t hq, int32_t hkv, int32_t dqk, int32_t dv,
+                                         int32_t idx_heads, int32_t idx_width,
+                                         int32_t block_size) {
+  const int64_t nb =
+      bwd_shape_blocks(L, mode, dtype, hq, hkv, dqk, dv, idx_heads, idx_width, block_size);
+  if (nb < 0) {
+    fail(CSA_ERR_INVALID_ARG, "sparse_attn_bwd_shard_kernel: malformed arguments");
+    return nullptr;
   }
-  return attn_bwd_ws_bytes(L->n_q, L->n_kv, L->n_seq, (int)nb, mode, hq, hkv, idx_heads,
-                           idx_width);
+  return attn_bwd_kernel_family(L->n_q, L->n_kv, (int)nb, mode, dtype, hq, hkv, dqk, dv,
+                                idx_heads, idx_width, block_size);
 }
 
 csa_status sparse_attn_bwd_shard(const csa_tensor3* q, const csa_tensor3* k,
@@ -467,8 +491,9 @@ csa_status sparse_attn_bwd_shard(const csa_tensor3* q, const csa_tensor3* k,
     if ((mode == CSA_SEL_TOKEN ? (int64_t)L->n_kv : nb) * (idx_heads == 1 ? 1 : k->h) >=
         ((int64_t)1 << 30))
       return fail(CSA_ERR_UNSUPPORTED, "too many key lists");
-    const size_t need = attn_bwd_ws_bytes(L->n_q, L->n_kv, L->n_seq, (int)nb, mode, q->h,
-                                          k->h, idx_heads, idx_width);
+    const size_t need = attn_bwd_ws_bytes(L->n_q, L->n_kv, L->n_seq, (int)nb, mode, q->dtype,
+                                          q->h, k->h, q->d, v->d, idx_heads, idx_width,
+                                          block_size);
     if ((st = check_ws(ws, ws_bytes, need))) return st;
     AttnBwdArgs a;
     a.q = make_view(q);

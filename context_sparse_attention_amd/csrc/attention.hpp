@@ -31,4 +31,31 @@ hipError_t launch_attn_block_mfma(const AttnKernelArgs& a, int n_blocks, void* w
 bool attn_token_mfma_supported(const AttnKernelArgs& a);
 hipError_t launch_attn_token_mfma(const AttnKernelArgs& a, hipStream_t stream);
 
+// Block-mode backward on the matrix cores, over the per-(key head, block) lists
+// of flat slot ids that launch_attn_backward builds: bf16, D = Dqk = Dv in
+// {64, 128}, one index row per query head.
+struct BwMfmaArgs {
+  View q, k, v, dout;
+  int dout_dtype;
+  DevLayout L;
+  const int32_t* idx;
+  int idx_width, block_size, n_blocks, n_lists, n_sub;
+  BlockTable bt;
+  const int32_t* list_off;  // [n_lists + 1]
+  const int32_t* entries;   // flat slot ids, list by list, ascending
+  const float* lse;
+  const float* delta;       // dO . O per (row, head)
+  float scale, scale_log2;
+  float *dq, *dk, *dv;
+  float* dq_part;           // [n_q * Hq * idx_width, D]: one dQ partial per slot
+  int2* tiles;              // [max_tiles] (list, first entry) of 128-entry chunks
+  int32_t* n_tiles;
+  int64_t max_tiles;
+};
+int attn_bwd_block_mfma_subtiles(int block_size);
+int64_t attn_bwd_block_mfma_max_tiles(int64_t n_entries, int64_t n_lists);
+bool attn_bwd_block_mfma_supported(int mode, int dtype, int dqk, int dv, int hq, int idx_heads,
+                                   int block_size, int64_t n_lists, int64_t n_entries);
+hipError_t launch_attn_bwd_block_mfma(const BwMfmaArgs& a, hipStream_t stream);
+
 }  // namespace csa

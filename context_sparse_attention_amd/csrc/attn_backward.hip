@@ -17,14 +17,18 @@
 // dK/dV need, per key, the index rows that selected it: the selection is
 // inverted into lists, one per chunk (a key in token mode, a block in block
 // mode; per key head when every query head has its own index row).  The lists
-// hold index-row ids in ascending order, so each key's sums run in a fixed
-// order and the results are bitwise reproducible without floating-point
-// atomics:
+// hold flat slot ids (index row * width + slot) in ascending order, so each
+// key's sums run in a fixed order and the results are bitwise reproducible
+// without floating-point atomics:
 //   k_bwd_hist   each wave counts its consecutive index rows' entries per list
 //   k_scan_*     exclusive scan of the counts, list-major then wave
-//   k_bwd_fill   each wave places its index rows one at a time, in order (all
-//                entries of one index row are equal, so their order is moot)
-// All arithmetic is fp32 on the vector ALUs (exact bf16 inputs widened).
+//   k_bwd_fill   each wave places its index rows one at a time, in order (a
+//                row's entries in one list are its repeated slots, whose order
+//                does not change any sum)
+// bf16 block mode with D in {64, 128} and one index row per query head runs the
+// matrix-core kernels of attn_backward_mfma.hip over these lists; every other
+// case runs k_bwd_dq / k_bwd_dkdv below, fp32 on the vector ALUs (exact bf16
+// inputs widened).
 #include <algorithm>
 
 #include "attention.hpp"
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(kBwThreads) void k_bwd_fill(BwArgs a) {
       const int c = slot_list(a, rk, hi, slots[s]);
       if (c >= 0) {
         const int pos = atomicAdd(&a.hist[(int64_t)c * a.R + r], 1);
-        a.entries[pos] = (int32_t)e;
+        a.entries[pos] = (int32_t)(e * a.idx_width + s);  // flat slot id
       }
     }
     // every cursor update of this index row has returned before the next row's
@@ -372,7 +376,7 @@ __global__ __launch_bounds__(kBwThreads) void k_bwd_dkdv(BwArgs a, int gdt) {
     float dx = 0.f, p = 0.f;
     int item = -1;  // i * hq + h
     if (it < n_items) {
-      const int e = a.entries[e0 + (int)(it / per_entry)];
+      const int e = a.entries[e0 + (int)(it / per_entry)] / a.idx_width;  // index row
       const int i = e / a.idx_heads;
       const int h = a.idx_heads == 1 ? g * G + (int)(it % per_entry) : e % a.idx_heads;
       const RowKeys r = row_keys(a.L, i);
@@ -440,10 +444,13 @@ __global__ __launch_bounds__(kBwThreads) void k_bwd_dkdv(BwArgs a, int gdt) {
 struct BwLayout {
   int n_lists, R, rows_per_range, n_tiles;
   int64_t n_hist, n_entries;
+  bool mfma;           // block mode on the matrix cores
+  int64_t max_tiles;   // its dQ chunks
+  int64_t n_part;      // its dQ partials (floats)
 };
 
-BwLayout bw_layout(int n_q, int n_kv, int n_blocks, int mode, int hkv, int idx_heads,
-                   int idx_width) {
+BwLayout bw_layout(int n_q, int n_kv, int n_blocks, int mode, int dtype, int hq, int hkv,
+                   int dqk, int dv, int idx_heads, int idx_width, int block_size) {
   BwLayout b;
   const int64_t chunks = mode == CSA_SEL_TOKEN ? n_kv : n_blocks;
   b.n_lists = (int)((idx_heads == 1 ? 1 : hkv) * chunks);
@@ -457,6 +464,10 @@ BwLayout bw_layout(int n_q, int n_kv, int n_blocks, int mode, int hkv, int idx_h
   b.n_hist = (int64_t)b.n_lists * b.R;
   b.n_tiles = (int)((b.n_hist + kScanTile - 1) / kScanTile);
   b.n_entries = n_rows * idx_width;
+  b.mfma = attn_bwd_block_mfma_supported(mode, dtype, dqk, dv, hq, idx_heads, block_size,
+                                         b.n_lists, b.n_entries);
+  b.max_tiles = b.mfma ? attn_bwd_block_mfma_max_tiles(b.n_entries, b.n_lists) : 0;
+  b.n_part = b.mfma ? b.n_entries * dqk : 0;
   return b;
 }
 
@@ -464,6 +475,9 @@ struct BwWs {
   float* delta;
   BlockTable bt;
   int32_t *hist, *list_off, *totals, *entries;
+  float* dq_part;
+  int2* tiles;
+  int32_t* n_tiles;
 };
 
 BwWs carve_bw(void* base, const BwLayout& b, int n_q, int hq, int n_seq, int n_blocks,
@@ -478,6 +492,9 @@ BwWs carve_bw(void* base, const BwLayout& b, int n_q, int hq, int n_seq, int n_b
   w.list_off = c.take<int32_t>(b.n_lists + 1);
   w.totals = c.take<int32_t>(b.n_tiles + 1);
   w.entries = c.take<int32_t>(std::max<int64_t>(1, b.n_entries));
+  w.dq_part = c.take<float>(b.n_part);
+  w.tiles = c.take<int2>(b.max_tiles);
+  w.n_tiles = c.take<int32_t>(b.mfma ? 1 : 0);
   if (used) *used = c.used;
   return w;
 }
@@ -488,12 +505,23 @@ unsigned grid_for(int64_t items, int per_block) {
 
 }  // namespace
 
-size_t attn_bwd_ws_bytes(int n_q, int n_kv, int n_seq, int n_blocks, int mode, int hq, int hkv,
-                         int idx_heads, int idx_width) {
-  const BwLayout b = bw_layout(n_q, n_kv, n_blocks, mode, hkv, idx_heads, idx_width);
+size_t attn_bwd_ws_bytes(int n_q, int n_kv, int n_seq, int n_blocks, int mode, int dtype, int hq,
+                         int hkv, int dqk, int dv, int idx_heads, int idx_width, int block_size) {
+  const BwLayout b = bw_layout(n_q, n_kv, n_blocks, mode, dtype, hq, hkv, dqk, dv, idx_heads,
+                               idx_width, block_size);
   size_t used = 0;
   carve_bw(nullptr, b, n_q, hq, n_seq, n_blocks, &used);
   return align_up(used, 256);
+}
+
+const char* attn_bwd_kernel_family(int n_q, int n_kv, int n_blocks, int mode, int dtype, int hq,
+                                   int hkv, int dqk, int dv, int idx_heads, int idx_width,
+                                   int block_size) {
+  return bw_layout(n_q, n_kv, n_blocks, mode, dtype, hq, hkv, dqk, dv, idx_heads, idx_width,
+                   block_size)
+                 .mfma
+             ? "block_mfma"
+             : "generic";
 }
 
 hipError_t launch_attn_backward(const AttnBwdArgs& x, hipStream_t stream) {
@@ -516,8 +544,8 @@ hipError_t launch_attn_backward(const AttnBwdArgs& x, hipStream_t stream) {
   a.dq = x.dq;
   a.dk = x.dk;
   a.dv = x.dv;
-  const BwLayout b = bw_layout(x.L.n_q, x.L.n_kv, x.n_blocks, x.mode, x.k.h, x.idx_heads,
-                               x.idx_width);
+  const BwLayout b = bw_layout(x.L.n_q, x.L.n_kv, x.n_blocks, x.mode, x.dtype, x.q.h, x.k.h,
+                               x.q.d, x.v.d, x.idx_heads, x.idx_width, x.block_size);
   BwWs w = carve_bw(x.ws, b, x.L.n_q, x.q.h, x.L.n_seq, x.n_blocks, nullptr);
   a.delta = w.delta;
   a.bt = w.bt;
@@ -559,11 +587,43 @@ hipError_t launch_attn_backward(const AttnBwdArgs& x, hipStream_t stream) {
     hipLaunchKernelGGL(k_scan_add, dim3(b.n_tiles), dim3(kBwThreads), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  int slot;
   if (pairs > 0) {
     hipLaunchKernelGGL(k_bwd_fill, dim3(grid_for(b.R, kBwWaves)), dim3(kBwThreads), 0, stream,
                        a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (b.mfma) {
+    BwMfmaArgs m;
+    m.q = x.q;
+    m.k = x.k;
+    m.v = x.v;
+    m.dout = x.dout;
+    m.dout_dtype = x.dout_dtype;
+    m.L = x.L;
+    m.idx = x.idx;
+    m.idx_width = x.idx_width;
+    m.block_size = x.block_size;
+    m.n_blocks = x.n_blocks;
+    m.n_lists = b.n_lists;
+    m.n_sub = attn_bwd_block_mfma_subtiles(x.block_size);
+    m.bt = w.bt;
+    m.list_off = w.list_off;
+    m.entries = w.entries;
+    m.lse = x.lse;
+    m.delta = w.delta;
+    m.scale = x.scale;
+    m.scale_log2 = x.scale * kLog2e;
+    m.dq = x.dq;
+    m.dk = x.dk;
+    m.dv = x.dv;
+    m.dq_part = w.dq_part;
+    m.tiles = w.tiles;
+    m.n_tiles = w.n_tiles;
+    m.max_tiles = b.max_tiles;
+    return launch_attn_bwd_block_mfma(m, stream);
+  }
+  int slot;
+  if (pairs > 0) {
     trace_begin(stream, "k_bwd_dq", &slot);
     if (x.dtype == CSA_BF16)
       hipLaunchKernelGGL(k_bwd_dq<__bf16>, dim3(grid_for(pairs, kBwWaves)), dim3(kBwThreads),

@@ -200,9 +200,13 @@ struct AttnBwdArgs {
   float *dq, *dk, *dv;
   void* ws;
 };
-size_t attn_bwd_ws_bytes(int n_q, int n_kv, int n_seq, int n_blocks, int mode, int hq, int hkv,
-                         int idx_heads, int idx_width);
+size_t attn_bwd_ws_bytes(int n_q, int n_kv, int n_seq, int n_blocks, int mode, int dtype, int hq,
+                         int hkv, int dqk, int dv, int idx_heads, int idx_width, int block_size);
 hipError_t launch_attn_backward(const AttnBwdArgs& a, hipStream_t stream);
+// "block_mfma" or "generic": the kernel family launch_attn_backward picks
+const char* attn_bwd_kernel_family(int n_q, int n_kv, int n_blocks, int mode, int dtype, int hq,
+                                   int hkv, int dqk, int dv, int idx_heads, int idx_width,
+                                   int block_size);
 
 struct MergeArgs {
   int n_parts;

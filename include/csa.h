@@ -239,8 +239,12 @@ const char* sparse_attn_fwd_shard_kernel(const csa_tensor3* q, const csa_tensor3
  *   dk[j,g]  += scale * P_j (dO . v_j - D) q[i,h]
  *   dv[j,g]  += P_j dO[i,h]
  * summed over every (row, head) whose selection holds key j, with g = h / (Hq/Hkv).
- * fp32 arithmetic; each key's sums run over its selecting (row, head) pairs in
- * ascending order: bitwise reproducible, no floating-point atomics.
+ * Each key's sums run over its selecting (row, head) pairs in ascending order and
+ * each dq over its slots in order: bitwise reproducible, no floating-point atomics.
+ * bf16 block mode with D = Dqk = Dv in {64, 128} and idx_heads = Hq runs on the
+ * matrix cores ("block_mfma": P and dS rounded to bf16 as operands, as P is in
+ * the forward; fp32 accumulation); every other case runs fp32 arithmetic on the
+ * vector ALUs ("generic").
  *
  *  q, k, v, idx, idx_heads, idx_width, block_size, softmax_scale, L, mode: as in
  *     sparse_attn_fwd_shard (the forward's arguments).  When v aliases k (absorbed
@@ -252,12 +256,23 @@ const char* sparse_attn_fwd_shard_kernel(const csa_tensor3* q, const csa_tensor3
  *  dq [n_q, Hq, Dqk], dk [n_kv, Hkv, Dqk], dv [n_kv, Hkv, Dv]: f32, contiguous,
  *     every element written (0 where nothing contributes).
  *  ws: at least sparse_attn_bwd_shard_workspace_size() bytes, 256-byte aligned (it
- *     holds D, the block table and the key lists: about 4 bytes per index slot).
+ *     holds D, the block table and the key lists: about 4 bytes per index slot; on
+ *     the "block_mfma" path also one fp32 dq partial per slot, 4 * Dqk bytes).
  *  n_q * Hq and n_q * idx_heads * idx_width must stay below 2^31.
  * ------------------------------------------------------------------------------- */
-size_t sparse_attn_bwd_shard_workspace_size(const csa_layout* L, int32_t mode, int32_t hq,
-                                            int32_t hkv, int32_t idx_heads, int32_t idx_width,
+/* The workspace of a call with q [n_q, hq, dqk] and v [n_kv, hkv, dv] of dtype
+ * `dtype` (CSA_F32 or CSA_BF16) and the other arguments as in the call; 0 when
+ * they are malformed. */
+size_t sparse_attn_bwd_shard_workspace_size(const csa_layout* L, int32_t mode, int32_t dtype,
+                                            int32_t hq, int32_t hkv, int32_t dqk, int32_t dv,
+                                            int32_t idx_heads, int32_t idx_width,
                                             int32_t block_size);
+/* "block_mfma" or "generic": the kernel family such a call runs; NULL (with
+ * csa_last_error set) when the arguments are malformed. */
+const char* sparse_attn_bwd_shard_kernel(const csa_layout* L, int32_t mode, int32_t dtype,
+                                         int32_t hq, int32_t hkv, int32_t dqk, int32_t dv,
+                                         int32_t idx_heads, int32_t idx_width,
+                                         int32_t block_size);
 csa_status sparse_attn_bwd_shard(const csa_tensor3* q, const csa_tensor3* k,
                                  const csa_tensor3* v, const csa_layout* L, int32_t mode,
                                  const int32_t* idx, int32_t idx_heads, int32_t idx_width,

@@ -31,20 +31,42 @@ and the gradient of the shared tensor is dk + dv on those columns.
 import numpy as np
 
 from .layout import permitted_interval
-from .attention import selected_keys
+from .attention import selected_keys, slot_span
+
+
+def _scatter(dst, mode, slots, interval, block_size, rows):
+    """dst[key] += rows[t] for the t-th key of the row's selected multiset.
+
+    Block selections add one slot's span at a time (a span's keys are
+    distinct, so a slice add is exact; a repeated slot adds again); token
+    selections use an unbuffered add (np.add.at), which also adds repeats.
+    """
+    if mode == "token":
+        np.add.at(dst, selected_keys(mode, slots, interval, block_size), rows)
+        return
+    lo, hi_incl, seq_end = interval
+    t = 0
+    for s in slots:
+        a, b = slot_span(mode, s, lo, hi_incl, seq_end, block_size)
+        dst[a:b] += rows[t:t + (b - a)]
+        t += b - a
 
 
 def shard_backward(q, k, v, q_pos, q_seq, cu_seqlens, mode, idx, scale, dout, block_size=0):
     """(dq [n_q, Hq, Dqk], dk [n_kv, Hkv, Dqk], dv [n_kv, Hkv, Dv]) in float64.
 
-    Arguments as ``shard_forward``; dout [n_q, Hq, Dv] is dL/dO.
+    Arguments as ``shard_forward``; dout [n_q, Hq, Dv] is dL/dO.  Keys, values
+    and their gradients are held head-major ([Hkv, n_kv, D]) while they are
+    gathered and accumulated.
     """
     n_q, hq, dqk = q.shape
     hkv = k.shape[1]
     group = hq // hkv
+    kf = np.ascontiguousarray(np.asarray(k, np.float64).transpose(1, 0, 2))
+    vf = np.ascontiguousarray(np.asarray(v, np.float64).transpose(1, 0, 2))
     dq = np.zeros((n_q, hq, dqk))
-    dk = np.zeros((k.shape[0], hkv, dqk))
-    dv = np.zeros((v.shape[0], hkv, v.shape[2]))
+    dk = np.zeros_like(kf)
+    dv = np.zeros_like(vf)
     for i in range(n_q):
         iv = permitted_interval(int(q_pos[i]), int(q_seq[i]), cu_seqlens)
         if idx.shape[1] == 1:
@@ -56,26 +78,27 @@ def shard_backward(q, k, v, q_pos, q_seq, cu_seqlens, mode, idx, scale, dout, bl
                 heads = slice(g * group, (g + 1) * group)
                 qm = np.asarray(q[i, heads], np.float64)            # [G, Dqk]
                 do = np.asarray(dout[i, heads], np.float64)         # [G, Dv]
-                kmat = np.asarray(k[keys, g], np.float64)
-                vmat = np.asarray(v[keys, g], np.float64)
+                kmat = kf[g][keys]
+                vmat = vf[g][keys]
                 x = scale * (qm @ kmat.T)                           # [G, n]
                 p = np.exp(x - x.max(axis=1, keepdims=True))
                 p /= p.sum(axis=1, keepdims=True)
                 dp = do @ vmat.T
                 dx = p * (dp - (p * dp).sum(axis=1, keepdims=True))
                 dq[i, heads] = scale * (dx @ kmat)
-                np.add.at(dk[:, g], keys, scale * (dx.T @ qm))
-                np.add.at(dv[:, g], keys, p.T @ do)
+                _scatter(dk[g], mode, idx[i, 0], iv, block_size, scale * (dx.T @ qm))
+                _scatter(dv[g], mode, idx[i, 0], iv, block_size, p.T @ do)
             continue
         for h in range(hq):
-            keys = selected_keys(mode, idx[i, 0 if idx.shape[1] == 1 else h], iv, block_size)
+            slots = idx[i, h]
+            keys = selected_keys(mode, slots, iv, block_size)
             if len(keys) == 0:
                 continue
             g = h // group
             qv = np.asarray(q[i, h], np.float64)
             do = np.asarray(dout[i, h], np.float64)
-            kmat = np.asarray(k[keys, g], np.float64)
-            vmat = np.asarray(v[keys, g], np.float64)
+            kmat = kf[g][keys]
+            vmat = vf[g][keys]
             x = scale * (kmat @ qv)
             m = x.max()
             p = np.exp(x - m)
@@ -83,9 +106,9 @@ def shard_backward(q, k, v, q_pos, q_seq, cu_seqlens, mode, idx, scale, dout, bl
             dp = vmat @ do                    # dP_j
             dx = p * (dp - p @ dp)            # softmax Jacobian
             dq[i, h] = scale * (dx @ kmat)
-            np.add.at(dk[:, g], keys, scale * dx[:, None] * qv[None, :])
-            np.add.at(dv[:, g], keys, p[:, None] * do[None, :])
-    return dq, dk, dv
+            _scatter(dk[g], mode, slots, iv, block_size, scale * dx[:, None] * qv[None, :])
+            _scatter(dv[g], mode, slots, iv, block_size, p[:, None] * do[None, :])
+    return dq, dk.transpose(1, 0, 2), dv.transpose(1, 0, 2)
 
 
 def loss(q, k, v, q_pos, q_seq, cu_seqlens, mode, idx, scale, dout, block_size=0):

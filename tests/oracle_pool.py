@@ -194,6 +194,23 @@ def _dsa_check(args):
             "max_score_err": max_score_err}
 
 
+def _bwd_keys(args):
+    """Oracle dk, dv of the keys [a, a + n) of key head g, from the given rows
+    (their query heads of group g only); float64 [n, D] partial sums."""
+    rows, p = args
+    A = _A
+    g, a, n = p["g"], p["a"], p["n"]
+    G = A["q"].shape[1] // A["k_hm"].shape[0]
+    hs = slice(g * G, (g + 1) * G)
+    k = A["k_hm"][g:g + 1].transpose(1, 0, 2)
+    v = A["v_hm"][g:g + 1].transpose(1, 0, 2)
+    _, dk, dv = oracle.shard_backward(A["q"][rows][:, hs], k, v, A["q_pos"][rows],
+                                      A["q_seq"][rows], A["cu"], p["mode"],
+                                      A["idx"][rows][:, hs], p["scale"], A["dout"][rows][:, hs],
+                                      p["block_size"])
+    return np.array(dk[a:a + n, 0]), np.array(dv[a:a + n, 0])
+
+
 # ------------------------------------------------------------------------------
 # parent side
 # ------------------------------------------------------------------------------
@@ -268,6 +285,14 @@ class OraclePool:
                 out["fails"] += r["fails"]
             outs.append(out)
         return outs
+
+    def bwd_keys(self, rows, params):
+        """(dk, dv) float64 of keys [a, a + n) of key head g (``params``: g, a, n,
+        mode, scale, block_size) summed over ``rows``' contributions."""
+        parts = self.pool.map(_bwd_keys, [(c, params) for c in self.chunks(rows, 1)])
+        dk = sum(p[0] for p in parts)
+        dv = sum(p[1] for p in parts)
+        return dk, dv
 
     def dsa_check(self, rows, params):
         parts = self.pool.map(_dsa_check, [(c, params) for c in self.chunks(rows)])
