@@ -34,9 +34,19 @@ hipError_t launch_attn_token_mfma(const AttnKernelArgs& a, hipStream_t stream);
 // Block-mode backward on the matrix cores, over the per-(key head, block) lists
 // of flat slot ids that launch_attn_backward builds: bf16, D = Dqk = Dv in
 // {64, 128}, one index row per query head.
+struct BwEntryInfo {  // one list entry, as the dK/dV kernel reads it (32 bytes)
+  int64_t qoff;        // element offset of the query row (i, h)
+  int64_t goff;        // element offset of its bf16 dO row
+  float lse2;          // lse * log2(e)
+  float dl;            // D = dO . O
+  int32_t pos;         // q_pos[i]
+  int32_t pad;
+};
 struct BwMfmaArgs {
   View q, k, v, dout;
   int dout_dtype;
+  View g16;                 // dO in bf16: dout itself, or a rounded copy
+  BwEntryInfo* info;        // [entries + 128]
   DevLayout L;
   const int32_t* idx;
   int idx_width, block_size, n_blocks, n_lists, n_sub;
@@ -51,6 +61,8 @@ struct BwMfmaArgs {
   int2* tiles;              // [max_tiles] (list, first entry) of 128-entry chunks
   int32_t* n_tiles;
   int64_t max_tiles;
+  int64_t max_entries;      // n_q * Hq * idx_width (bounds the lists' total)
+  __bf16* dout16;           // [n_q, Hq, D]: room for the rounded dO
 };
 int attn_bwd_block_mfma_subtiles(int block_size);
 int64_t attn_bwd_block_mfma_max_tiles(int64_t n_entries, int64_t n_lists);

@@ -447,6 +447,8 @@ struct BwLayout {
   bool mfma;           // block mode on the matrix cores
   int64_t max_tiles;   // its dQ chunks
   int64_t n_part;      // its dQ partials (floats)
+  int64_t n_info;      // its entry records
+  int64_t n_dout16;    // its bf16 dO copy (elements)
 };
 
 BwLayout bw_layout(int n_q, int n_kv, int n_blocks, int mode, int dtype, int hq, int hkv,
@@ -468,6 +470,8 @@ BwLayout bw_layout(int n_q, int n_kv, int n_blocks, int mode, int dtype, int hq,
                                          b.n_lists, b.n_entries);
   b.max_tiles = b.mfma ? attn_bwd_block_mfma_max_tiles(b.n_entries, b.n_lists) : 0;
   b.n_part = b.mfma ? b.n_entries * dqk : 0;
+  b.n_info = b.mfma ? b.n_entries + 128 : 0;
+  b.n_dout16 = b.mfma ? (int64_t)n_q * hq * dqk : 0;
   return b;
 }
 
@@ -478,6 +482,8 @@ struct BwWs {
   float* dq_part;
   int2* tiles;
   int32_t* n_tiles;
+  BwEntryInfo* info;
+  __bf16* dout16;
 };
 
 BwWs carve_bw(void* base, const BwLayout& b, int n_q, int hq, int n_seq, int n_blocks,
@@ -495,6 +501,8 @@ BwWs carve_bw(void* base, const BwLayout& b, int n_q, int hq, int n_seq, int n_b
   w.dq_part = c.take<float>(b.n_part);
   w.tiles = c.take<int2>(b.max_tiles);
   w.n_tiles = c.take<int32_t>(b.mfma ? 1 : 0);
+  w.info = c.take<BwEntryInfo>(b.n_info);
+  w.dout16 = c.take<__bf16>(b.n_dout16);
   if (used) *used = c.used;
   return w;
 }
@@ -620,6 +628,10 @@ hipError_t launch_attn_backward(const AttnBwdArgs& x, hipStream_t stream) {
     m.tiles = w.tiles;
     m.n_tiles = w.n_tiles;
     m.max_tiles = b.max_tiles;
+    m.max_entries = b.n_entries;
+    m.info = w.info;
+    m.dout16 = w.dout16;
+    m.g16 = x.dout;
     return launch_attn_bwd_block_mfma(m, stream);
   }
   int slot;
