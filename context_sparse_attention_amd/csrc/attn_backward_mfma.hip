@@ -25,6 +25,7 @@
 
 #include "attention.hpp"
 #include "gather.hpp"
+#include "mfma.hpp"
 
 namespace csa {
 
@@ -262,11 +263,13 @@ __global__ __launch_bounds__(kDT, 1) void k_bwbm_dkdv(BwMfmaArgs a) {
       vf[ks] = *reinterpret_cast<const bf16x8*>(vp + 16 * ks + 8 * half);
     }
   }
-  f32x16 dkt[DB], dvt[DB];  // [head-dim block]: rows = head dims, columns = the wave's keys
+  // [head-dim block]: rows = head dims, columns = the wave's keys; held in AGPRs
+  // (the compiler otherwise copies them between register files every block)
+  f32x16 dkt[DB], dvt[DB];
 #pragma unroll
   for (int x = 0; x < DB; ++x) {
-    dkt[x] = f32x16{};
-    dvt[x] = f32x16{};
+    to_agpr(dkt[x], f32x16{});
+    to_agpr(dvt[x], f32x16{});
   }
   const int kl = lane & 31;
   // this lane's key, or one past every position when the lane holds no key
@@ -312,12 +315,14 @@ __global__ __launch_bounds__(kDT, 1) void k_bwbm_dkdv(BwMfmaArgs a) {
       for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
         for (int x = 0; x < DB; ++x) {
-          dvt[x] = mfma(sw_trfrag<D>(sg, 32 * qb, qs, 32 * x, lane), pb[qs], dvt[x]);
-          dkt[x] = mfma(sw_trfrag<D>(sq, 32 * qb, qs, 32 * x, lane), db[qs], dkt[x]);
+          mfma_a(dvt[x], sw_trfrag<D>(sg, 32 * qb, qs, 32 * x, lane), pb[qs]);
+          mfma_a(dkt[x], sw_trfrag<D>(sq, 32 * qb, qs, 32 * x, lane), db[qs]);
         }
     }
   }
   if (nk <= 0) return;
+  fence_a(dkt);
+  fence_a(dvt);
   // lane holds key (lane % 32), head dims 32 x + 8 (j / 4) + 4 half + (j % 4)
   if (kl < nk) {
     const int64_t row = ((int64_t)(k0 + kl) * a.k.h + g) * D;
