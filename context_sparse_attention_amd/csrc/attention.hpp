@@ -70,4 +70,30 @@ bool attn_bwd_block_mfma_supported(int mode, int dtype, int dqk, int dv, int hq,
                                    int block_size, int64_t n_lists, int64_t n_entries);
 hipError_t launch_attn_bwd_block_mfma(const BwMfmaArgs& a, hipStream_t stream);
 
+// Token-mode dK / dV on the matrix cores (one selection per token, bf16,
+// Dqk = 576, Dv = 512, Hq / Hkv a multiple of 32).
+struct BwTokArgs {
+  View q, k, v, dout;
+  int dout_dtype;
+  View g16;                 // dO in bf16: dout itself, or a rounded copy
+  DevLayout L;
+  const int32_t* idx;       // [n_q, idx_width]
+  int idx_width;
+  const float* lse;         // [n_q, Hq]
+  const float* delta;       // [n_q, Hq]
+  float scale, scale_log2;
+  float *dk, *dv;
+  uint16_t* cmap;           // [n_q, n_kvp] selection counts
+  int n_kvp;                // n_kv rounded up to 64
+  float* rec;               // [n_q, Hq / 32, 64]
+  float* part;              // [n_chunks, n_kvp, Hkv, 1088]
+  int n_chunks;
+  __bf16* dout16;           // [n_q, Hq, 512]: room for the rounded dO
+};
+bool attn_bwd_token_mfma_supported(int mode, int dtype, int dqk, int dv, int hq, int hkv,
+                                   int idx_heads, int idx_width);
+int attn_bwd_token_chunks(int n_q);
+int attn_bwd_token_kvp(int n_kv);
+hipError_t launch_attn_bwd_token_dkdv(const BwTokArgs& a, hipStream_t stream);
+
 }  // namespace csa

@@ -449,6 +449,11 @@ struct BwLayout {
   int64_t n_part;      // its dQ partials (floats)
   int64_t n_info;      // its entry records
   int64_t n_dout16;    // its bf16 dO copy (elements)
+  bool tok;            // token-mode dK / dV on the matrix cores (no lists)
+  int n_kvp, n_chunks;
+  int64_t n_cmap;      // its count map (uint16)
+  int64_t n_rec;       // its per-(row, head block) records (floats)
+  int64_t n_tpart;     // its per-row-chunk partial sums (floats)
 };
 
 BwLayout bw_layout(int n_q, int n_kv, int n_blocks, int mode, int dtype, int hq, int hkv,
@@ -472,6 +477,21 @@ BwLayout bw_layout(int n_q, int n_kv, int n_blocks, int mode, int dtype, int hq,
   b.n_part = b.mfma ? b.n_entries * dqk : 0;
   b.n_info = b.mfma ? b.n_entries + 128 : 0;
   b.n_dout16 = b.mfma ? (int64_t)n_q * hq * dqk : 0;
+  b.tok = attn_bwd_token_mfma_supported(mode, dtype, dqk, dv, hq, hkv, idx_heads, idx_width);
+  b.n_kvp = b.tok ? attn_bwd_token_kvp(n_kv) : 0;
+  b.n_chunks = b.tok ? attn_bwd_token_chunks(n_q) : 0;
+  b.n_cmap = b.tok ? (int64_t)n_q * b.n_kvp : 0;
+  b.n_rec = b.tok ? (int64_t)n_q * hq * 2 : 0;
+  b.n_tpart = b.tok ? (int64_t)b.n_chunks * b.n_kvp * hkv * (dqk + dv) : 0;
+  if (b.tok) {
+    b.n_dout16 = (int64_t)n_q * hq * dv;
+    // no key lists: the count map takes their place
+    b.n_lists = 0;
+    b.R = 1;
+    b.n_hist = 0;
+    b.n_tiles = 0;
+    b.n_entries = 0;
+  }
   return b;
 }
 
@@ -484,6 +504,8 @@ struct BwWs {
   int32_t* n_tiles;
   BwEntryInfo* info;
   __bf16* dout16;
+  uint16_t* cmap;
+  float *rec, *tpart;
 };
 
 BwWs carve_bw(void* base, const BwLayout& b, int n_q, int hq, int n_seq, int n_blocks,
@@ -503,6 +525,9 @@ BwWs carve_bw(void* base, const BwLayout& b, int n_q, int hq, int n_seq, int n_b
   w.n_tiles = c.take<int32_t>(b.mfma ? 1 : 0);
   w.info = c.take<BwEntryInfo>(b.n_info);
   w.dout16 = c.take<__bf16>(b.n_dout16);
+  w.cmap = c.take<uint16_t>(b.n_cmap);
+  w.rec = c.take<float>(b.n_rec);
+  w.tpart = c.take<float>(b.n_tpart);
   if (used) *used = c.used;
   return w;
 }
@@ -525,11 +550,9 @@ size_t attn_bwd_ws_bytes(int n_q, int n_kv, int n_seq, int n_blocks, int mode, i
 const char* attn_bwd_kernel_family(int n_q, int n_kv, int n_blocks, int mode, int dtype, int hq,
                                    int hkv, int dqk, int dv, int idx_heads, int idx_width,
                                    int block_size) {
-  return bw_layout(n_q, n_kv, n_blocks, mode, dtype, hq, hkv, dqk, dv, idx_heads, idx_width,
-                   block_size)
-                 .mfma
-             ? "block_mfma"
-             : "generic";
+  const BwLayout b = bw_layout(n_q, n_kv, n_blocks, mode, dtype, hq, hkv, dqk, dv, idx_heads,
+                               idx_width, block_size);
+  return b.mfma ? "block_mfma" : b.tok ? "token_mfma" : "generic";
 }
 
 hipError_t launch_attn_backward(const AttnBwdArgs& x, hipStream_t stream) {
@@ -581,6 +604,42 @@ hipError_t launch_attn_backward(const AttnBwdArgs& x, hipStream_t stream) {
     hipLaunchKernelGGL(k_bwd_delta, dim3(grid_for(pairs, kBwWaves)), dim3(kBwThreads), 0,
                        stream, a, x.o_dtype, x.dout_dtype);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (b.tok) {
+    BwTokArgs t;
+    t.q = x.q;
+    t.k = x.k;
+    t.v = x.v;
+    t.dout = x.dout;
+    t.dout_dtype = x.dout_dtype;
+    t.g16 = x.dout;
+    t.L = x.L;
+    t.idx = x.idx;
+    t.idx_width = x.idx_width;
+    t.lse = x.lse;
+    t.delta = w.delta;
+    t.scale = x.scale;
+    t.scale_log2 = x.scale * kLog2e;
+    t.dk = x.dk;
+    t.dv = x.dv;
+    t.cmap = w.cmap;
+    t.n_kvp = b.n_kvp;
+    t.rec = w.rec;
+    t.part = w.tpart;
+    t.n_chunks = b.n_chunks;
+    t.dout16 = w.dout16;
+    if ((e = launch_attn_bwd_token_dkdv(t, stream)) != hipSuccess) return e;
+    int slot;
+    if (pairs > 0) {  // dQ on the vector ALUs
+      trace_begin(stream, "k_bwd_dq", &slot);
+      hipLaunchKernelGGL(k_bwd_dq<__bf16>, dim3(grid_for(pairs, kBwWaves)), dim3(kBwThreads), 0,
+                         stream, a, x.dout_dtype);
+      trace_end(stream, slot);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  if (pairs > 0) {
     hipLaunchKernelGGL(k_bwd_hist, dim3(grid_for(b.R, kBwWaves)), dim3(kBwThreads), 0, stream,
                        a);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -39,10 +39,15 @@ def _scatter(dst, mode, slots, interval, block_size, rows):
 
     Block selections add one slot's span at a time (a span's keys are
     distinct, so a slice add is exact; a repeated slot adds again); token
-    selections use an unbuffered add (np.add.at), which also adds repeats.
+    selections add by index when their keys are distinct and otherwise use an
+    unbuffered add (np.add.at), which adds repeats again.
     """
     if mode == "token":
-        np.add.at(dst, selected_keys(mode, slots, interval, block_size), rows)
+        keys = selected_keys(mode, slots, interval, block_size)
+        if len(np.unique(keys)) == len(keys):
+            dst[keys] += rows          # distinct keys: one add each
+        else:
+            np.add.at(dst, keys, rows)
         return
     lo, hi_incl, seq_end = interval
     t = 0

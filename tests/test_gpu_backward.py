@@ -143,7 +143,9 @@ def test_token_backward_matches_oracle(case, dtype):
     _say("token backward", case, dtype)
     d = upload(w)
     idx = csa.dsa_indexer_topk(d["iq"], d["ik"], d["w"], d["layout"], w.topk)
-    assert _family(w, d, idx) == "generic"
+    # bf16 absorbed-MLA shape (576 / 512): dK and dV on the matrix cores
+    mla = dtype == "bf16" and (w.dqk, w.dv) == (576, 512)
+    assert _family(w, d, idx) == ("token_mfma" if mla else "generic")
     idx_np = idx.cpu().numpy()[:, None, :]
     dout = np.random.default_rng(case).standard_normal((w.n_q, w.hq, w.dv))
     got = _fwd_bwd(w, d, idx, dout)
@@ -248,6 +250,28 @@ def _check_lists(w, idx_np, dout_np, dk, dv, label):
                 assert err <= TOL["bf16"] * scale
 
 
+def _check_token_keys(w, idx_np, dout_np, dk, dv, label, n_ranges=2, width=2):
+    """dk, dv of sampled runs of `width` consecutive keys against the oracle on
+    every row whose selection holds one of them (seeded; keys some row selects)."""
+    sel = idx_np[:, 0]
+    chosen = np.unique(sel[sel >= 0])
+    rng = np.random.default_rng(10)
+    arrays = dict(q=w.q, k=w.k, v=w.value, q_pos=w.q_pos, q_seq=w.q_seq, cu=w.cu_seqlens,
+                  idx=idx_np, dout=dout_np)
+    with OraclePool(arrays) as pool:
+        for a in rng.choice(chosen[chosen < w.n_kv - width], n_ranges, replace=False):
+            a = int(a)
+            rows = np.where(((sel >= a) & (sel < a + width)).any(axis=1))[0]
+            rk, rv = pool.bwd_keys(rows, dict(g=0, a=a, n=width, mode=w.mode, scale=w.scale,
+                                              block_size=w.block_size))
+            for name, got, ref in (("dk", dk[a:a + width, 0], rk), ("dv", dv[a:a + width, 0], rv)):
+                scale = max(1.0, float(np.abs(ref).max()))
+                err = float(np.abs(got - ref).max())
+                _say(label, f"{name} of keys [{a}, {a + width}) ({len(rows)} rows)",
+                     f"err {err:.2e} (scale {scale:.3g})")
+                assert err <= TOL["bf16"] * scale
+
+
 @pytest.mark.parametrize("name", ["moba_mha_8k", "moba_gqa_zigzag_32k", "moba_thd_64k",
                                   "dsa_mla_16k"])
 def test_full_size_backward(name):
@@ -261,7 +285,7 @@ def test_full_size_backward(name):
         idx = csa.dsa_indexer_topk(d["iq"], d["ik"], d["w"], d["layout"], w.topk)
         idx_np = idx.cpu().numpy()[:, None, :]
     mode = csa.CSA_SEL_BLOCK if w.mode == "block" else csa.CSA_SEL_TOKEN
-    assert _family(w, d, idx) == ("block_mfma" if w.mode == "block" else "generic")
+    assert _family(w, d, idx) == ("block_mfma" if w.mode == "block" else "token_mfma")
     out, lse = csa.sparse_attn_fwd_shard(d["q"], d["k"], d["v"], d["layout"], mode, idx,
                                          block_size=w.block_size, softmax_scale=w.scale,
                                          out_dtype=torch.float32)
@@ -279,9 +303,13 @@ def test_full_size_backward(name):
     lse_np = lse.cpu().numpy()
     for n_, a in (("dq", dq), ("dk", dk), ("dv", dv)):
         assert np.isfinite(a).all(), f"{n_} has unwritten or non-finite elements"
-    if _family(w, d, idx) == "generic":
+    fam = _family(w, d, idx)
+    if fam == "generic":
         # fp32 operands: the key-head sums hold to fp32 rounding
         _identities(w, dq, dk, dv, dout_np.astype(np.float64), lse_np, name)
+    elif fam == "token_mfma":
+        # bf16 P and dS' operands (see below): sampled keys against the oracle
+        _check_token_keys(w, idx_np, dout_np, dk, dv, name)
     else:
         # bf16 P and dS operands: the sums hold only to bf16 rounding (sum_j P_j is
         # 1 within 2^-8), too loose a bar to test; whole key blocks are compared
