@@ -70,8 +70,8 @@ bool attn_bwd_block_mfma_supported(int mode, int dtype, int dqk, int dv, int hq,
                                    int block_size, int64_t n_lists, int64_t n_entries);
 hipError_t launch_attn_bwd_block_mfma(const BwMfmaArgs& a, hipStream_t stream);
 
-// Token-mode dK / dV on the matrix cores (one selection per token, bf16,
-// Dqk = 576, Dv = 512, Hq / Hkv a multiple of 32).
+// Token-mode backward on the matrix cores (one selection per token, bf16,
+// Dqk = 576, Dv = 512, Hq / Hkv in {32, 64, 128}, index width at most 4096).
 struct BwTokArgs {
   View q, k, v, dout;
   int dout_dtype;
@@ -89,11 +89,16 @@ struct BwTokArgs {
   float* part;              // [n_chunks, n_kvp, Hkv, 1088]
   int n_chunks;
   __bf16* dout16;           // [n_q, Hq, 512]: room for the rounded dO
+  __bf16* ds;               // [n_q, Hq, w32]: dS' per slot
+  int w32;                  // idx_width rounded up to 32
+  float* dq;
 };
 bool attn_bwd_token_mfma_supported(int mode, int dtype, int dqk, int dv, int hq, int hkv,
                                    int idx_heads, int idx_width);
 int attn_bwd_token_chunks(int n_q);
 int attn_bwd_token_kvp(int n_kv);
-hipError_t launch_attn_bwd_token_dkdv(const BwTokArgs& a, hipStream_t stream);
+int attn_bwd_token_w32(int idx_width);
+// dK, dV and dQ
+hipError_t launch_attn_bwd_token(const BwTokArgs& a, hipStream_t stream);
 
 }  // namespace csa

@@ -454,6 +454,8 @@ struct BwLayout {
   int64_t n_cmap;      // its count map (uint16)
   int64_t n_rec;       // its per-(row, head block) records (floats)
   int64_t n_tpart;     // its per-row-chunk partial sums (floats)
+  int64_t n_ds;        // its dS' per slot (bf16)
+  int w32;
 };
 
 BwLayout bw_layout(int n_q, int n_kv, int n_blocks, int mode, int dtype, int hq, int hkv,
@@ -483,6 +485,8 @@ BwLayout bw_layout(int n_q, int n_kv, int n_blocks, int mode, int dtype, int hq,
   b.n_cmap = b.tok ? (int64_t)n_q * b.n_kvp : 0;
   b.n_rec = b.tok ? (int64_t)n_q * hq * 2 : 0;
   b.n_tpart = b.tok ? (int64_t)b.n_chunks * b.n_kvp * hkv * (dqk + dv) : 0;
+  b.w32 = b.tok ? attn_bwd_token_w32(idx_width) : 0;
+  b.n_ds = b.tok ? (int64_t)n_q * hq * b.w32 : 0;
   if (b.tok) {
     b.n_dout16 = (int64_t)n_q * hq * dv;
     // no key lists: the count map takes their place
@@ -506,6 +510,7 @@ struct BwWs {
   __bf16* dout16;
   uint16_t* cmap;
   float *rec, *tpart;
+  __bf16* ds;
 };
 
 BwWs carve_bw(void* base, const BwLayout& b, int n_q, int hq, int n_seq, int n_blocks,
@@ -528,6 +533,7 @@ BwWs carve_bw(void* base, const BwLayout& b, int n_q, int hq, int n_seq, int n_b
   w.cmap = c.take<uint16_t>(b.n_cmap);
   w.rec = c.take<float>(b.n_rec);
   w.tpart = c.take<float>(b.n_tpart);
+  w.ds = c.take<__bf16>(b.n_ds);
   if (used) *used = c.used;
   return w;
 }
@@ -628,16 +634,10 @@ hipError_t launch_attn_backward(const AttnBwdArgs& x, hipStream_t stream) {
     t.part = w.tpart;
     t.n_chunks = b.n_chunks;
     t.dout16 = w.dout16;
-    if ((e = launch_attn_bwd_token_dkdv(t, stream)) != hipSuccess) return e;
-    int slot;
-    if (pairs > 0) {  // dQ on the vector ALUs
-      trace_begin(stream, "k_bwd_dq", &slot);
-      hipLaunchKernelGGL(k_bwd_dq<__bf16>, dim3(grid_for(pairs, kBwWaves)), dim3(kBwThreads), 0,
-                         stream, a, x.dout_dtype);
-      trace_end(stream, slot);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    return hipSuccess;
+    t.ds = w.ds;
+    t.w32 = b.w32;
+    t.dq = x.dq;
+    return launch_attn_bwd_token(t, stream);
   }
   if (pairs > 0) {
     hipLaunchKernelGGL(k_bwd_hist, dim3(grid_for(b.R, kBwWaves)), dim3(kBwThreads), 0, stream,

@@ -412,20 +412,244 @@ __global__ __launch_bounds__(256) void k_bwtm_reduce(BwTokArgs a) {
   else *reinterpret_cast<float4*>(a.dv + kh * kTV + (d4 - kTQ)) = acc;
 }
 
+// ---- dQ -----------------------------------------------------------------------------------
+// Two passes over each row's selected keys, 32 slots at a time gathered into LDS
+// and shared by the row's query heads of one key head (32 heads per wave):
+//   k_bwtm_ds  S^T = K Q^T and dP^T = V dO^T with the heads' Q and dO fragments in
+//              registers; dS' = P (dP - D) stored per slot in bf16 (0 for a slot
+//              that selects no permitted key)
+//   k_bwtm_dq  dQ = scale dS' K with the heads' dQ accumulators in registers
+// (one pass would need the Q, dO and dQ fragments of 32 heads at once: 560
+// registers, more than a wave has)
+constexpr int kDS = 32;       // slots per tile
+constexpr int kMaxW = 4096;   // index width whose slots are staged in LDS
+
+template <bool VA>
+struct DsLds {
+  __bf16 k[2][kDS * kTQ];
+  __bf16 v[VA ? 1 : 2][VA ? 8 : kDS * kTV];
+  int key[kMaxW];  // the row's slots: key, or -1 when it selects no permitted key
+};
+
+struct DqLds {
+  __bf16 k[2][kDS * kTQ];
+  __bf16 ds[2][4][32 * kDS];  // [stage][wave][head][slot]
+  int key[kMaxW];
+};
+
+// the row's slots into LDS (permitted key or -1); returns a key every gather may read
+__device__ __forceinline__ int stage_slots(const BwTokArgs& a, int i, int* key) {
+  const RowKeys r = row_keys(a.L, i);
+  for (int t = threadIdx.x; t < a.idx_width; t += blockDim.x) {
+    const int k = a.idx[(int64_t)i * a.idx_width + t];
+    key[t] = r.valid && k >= r.lo && k <= r.hi ? k : -1;
+  }
+  return r.valid ? r.lo : 0;
+}
+
+// gathers slot tile t's key rows (and value rows when V is not K's prefix) into
+// stage st: copies c = wave, wave + NW, ...
+template <bool VA>
+__device__ __forceinline__ void gather_tile(const BwTokArgs& a, int g, const int* key, int kfb,
+                                            int t, __bf16* kt, __bf16* vt, int nw, int wave,
+                                            int lane) {
+  const __bf16* kb = static_cast<const __bf16*>(a.k.data);
+  const __bf16* vb = static_cast<const __bf16*>(a.v.data);
+  constexpr int NC = kTQC + (VA ? 0 : kTGC);
+  for (int c = wave; c < NC; c += nw) {
+    if (c < kTQC) {
+      const int byte = 1024 * c + 16 * lane;
+      const int r = byte / (kTQ * 2);
+      const int pp = (byte % (kTQ * 2)) / 16;
+      const int slot = kDS * t + r;
+      int k = slot < a.idx_width ? key[slot] : -1;
+      k = k < 0 ? kfb : k;
+      const __bf16* src = kb + (int64_t)k * a.k.stride_n + (int64_t)g * a.k.stride_h + (pp ^ swq(r)) * 8;
+      gather16_addr(src, __builtin_amdgcn_readfirstlane(lds_addr(kt) + 1024 * c));
+    } else {
+      const int r = c - kTQC;
+      const int slot = kDS * t + r;
+      int k = slot < a.idx_width ? key[slot] : -1;
+      k = k < 0 ? kfb : k;
+      const __bf16* src = vb + (int64_t)k * a.v.stride_n + (int64_t)g * a.v.stride_h + (lane ^ swg(r)) * 8;
+      gather16_addr(src, __builtin_amdgcn_readfirstlane(lds_addr(vt) + 1024 * r));
+    }
+  }
+}
+
+// one workgroup per (row, key head); wave w takes query heads g G + 32 w ..
+template <bool VA>
+__global__ __launch_bounds__(256, 1) void k_bwtm_ds(BwTokArgs a) {
+  __shared__ DsLds<VA> s;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int nw = blockDim.x / kWave;
+  const int half = lane >> 5;
+  const int i = blockIdx.x / a.k.h, g = blockIdx.x % a.k.h;
+  const int hq = a.q.h, G = hq / a.k.h;
+  const int h = g * G + 32 * wave + (lane & 31);  // this lane's head (B-operand column)
+  const int kfb = stage_slots(a, i, s.key);
+  __syncthreads();
+  const int n_t = (a.idx_width + kDS - 1) / kDS;
+  gather_tile<VA>(a, g, s.key, kfb, 0, s.k[0], s.v[0], nw, wave, lane);
+
+  // B operands: Q^T and dO^T fragments of head h
+  bf16x8 qf[kTQ / 16], gf[kTV / 16];
+  {
+    const __bf16* qp = elem_ptr<__bf16>(a.q, i, h);
+    const __bf16* gp = elem_ptr<__bf16>(a.g16, i, h);
+#pragma unroll
+    for (int ks = 0; ks < kTQ / 16; ++ks)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * half);
+#pragma unroll
+    for (int ks = 0; ks < kTV / 16; ++ks)
+      gf[ks] = *reinterpret_cast<const bf16x8*>(gp + 16 * ks + 8 * half);
+  }
+  const int64_t pair = (int64_t)i * hq + h;
+  const float lse2 = a.lse[pair] * kL2e;
+  const float dl = a.delta[pair];
+  __bf16* dsrow = a.ds + pair * a.w32;
+  bf16x8 prev[2];  // the previous tile's dS', stored once the next tile is under way
+  // lane holds slots 32 t + 8 jj + 4 half + 0 .. 3 in prev[jj / 2][4 (jj % 2) ..]
+  auto store_prev = [&](int t) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      bf16x4 v;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = prev[jj >> 1][4 * (jj & 1) + u];
+      *reinterpret_cast<bf16x4*>(dsrow + kDS * t + 8 * jj + 4 * half) = v;
+    }
+  };
+  for (int t = 0; t < n_t; ++t) {
+    wait_gathers();
+    __syncthreads();
+    if (t + 1 < n_t)
+      gather_tile<VA>(a, g, s.key, kfb, t + 1, s.k[(t + 1) & 1], s.v[VA ? 0 : (t + 1) & 1], nw,
+                      wave, lane);
+    if (t > 0) store_prev(t - 1);
+    const __bf16* kt = s.k[t & 1];
+    const __bf16* vt = s.v[VA ? 0 : t & 1];
+    // S^T and dP^T: rows = the tile's slots, columns = the wave's heads
+    const int r = lane & 31;
+    f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < kTQ / 16; ks += 2) {
+      s0 = mfma(*reinterpret_cast<const bf16x8*>(kt + offq(r, 16 * ks + 8 * half)), qf[ks], s0);
+      s1 = mfma(*reinterpret_cast<const bf16x8*>(kt + offq(r, 16 * ks + 16 + 8 * half)), qf[ks + 1], s1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int ks = 0; ks < kTV / 16; ks += 2) {
+      const int e0 = 16 * ks + 8 * half, e1 = e0 + 16;
+      const bf16x8& v0 = *reinterpret_cast<const bf16x8*>(VA ? kt + offq(r, e0) : vt + offg(r, e0));
+      const bf16x8& v1 = *reinterpret_cast<const bf16x8*>(VA ? kt + offq(r, e1) : vt + offg(r, e1));
+      p0 = mfma(v0, gf[ks], p0);
+      p1 = mfma(v1, gf[ks + 1], p1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // lane holds head h, slots 32 t + 8 (j / 4) + 4 half + (j % 4)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int slot = kDS * t + 8 * (j >> 2) + 4 * half + (j & 3);
+      const bool ok = slot < a.idx_width && s.key[min(slot, a.idx_width - 1)] >= 0;
+      const float pv = exp2_raw(fmaf(s0[j] + s1[j], a.scale_log2, ok ? -lse2 : -INFINITY));
+      prev[j >> 3][j & 7] = (__bf16)(pv * (p0[j] + p1[j] - dl));
+    }
+  }
+  store_prev(n_t - 1);
+}
+
+// B operand [16 slots x 32 columns] of a gathered key tile, slots in natural order
+// (16 qs + 8 half + 0 .. 7), columns c0 .. c0 + 31
+__device__ __forceinline__ bf16x8 trnat(const __bf16* t, int qs, int c0, int lane) {
+  const int half = lane >> 5, c16 = lane & 15, grp = lane >> 4;
+  const int r = 16 * qs + 8 * half + (c16 >> 2);
+  const int c = c0 + 16 * (grp & 1) + 4 * (c16 & 3);
+  const bf16x4 lo = read_tr(t, offq(r, c));
+  const bf16x4 hi = read_tr(t, offq(r + 4, c));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__global__ __launch_bounds__(256, 1) void k_bwtm_dq(BwTokArgs a) {
+  __shared__ DqLds s;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int nw = blockDim.x / kWave;
+  const int half = lane >> 5;
+  const int i = blockIdx.x / a.k.h, g = blockIdx.x % a.k.h;
+  const int hq = a.q.h, G = hq / a.k.h;
+  const int h0 = g * G + 32 * wave;  // this wave's first head
+  const int kfb = stage_slots(a, i, s.key);
+  __syncthreads();
+  const int n_t = (a.idx_width + kDS - 1) / kDS;
+  // this wave's dS' tile t (32 heads x 32 slots, 2 KiB) into stage st
+  auto copy_ds = [&](int t, int st) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int byte = 1024 * u + 16 * lane;
+      const int hl = byte / (2 * kDS), sl = (byte % (2 * kDS)) / 2;
+      const __bf16* src = a.ds + ((int64_t)i * hq + h0 + hl) * a.w32 + kDS * t + sl;
+      gather16_addr(src, __builtin_amdgcn_readfirstlane(lds_addr(&s.ds[st][wave][0]) + 1024 * u));
+    }
+  };
+  gather_tile<true>(a, g, s.key, kfb, 0, s.k[0], nullptr, nw, wave, lane);
+  copy_ds(0, 0);
+  constexpr int NB = kTQ / 32;  // 18 column blocks of dQ
+  f32x16 acc[NB];
+#pragma unroll
+  for (int x = 0; x < NB; ++x) acc[x] = f32x16{};
+  for (int t = 0; t < n_t; ++t) {
+    wait_gathers();
+    __syncthreads();
+    if (t + 1 < n_t) {
+      gather_tile<true>(a, g, s.key, kfb, t + 1, s.k[(t + 1) & 1], nullptr, nw, wave, lane);
+      copy_ds(t + 1, (t + 1) & 1);
+    }
+    const __bf16* kt = s.k[t & 1];
+    const __bf16* dt = s.ds[t & 1][wave];
+    // A operands: dS' rows of the wave's heads (m = head lane % 32), slots 16 qs + 8 half ..
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(dt + (lane & 31) * kDS + 8 * half);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(dt + (lane & 31) * kDS + 16 + 8 * half);
+    bf16x8 f0 = trnat(kt, 0, 0, lane), f1 = trnat(kt, 0, 32, lane);
+#pragma unroll
+    for (int u = 0; u < 2 * NB; ++u) {  // u = NB qs + x
+      bf16x8 nf;
+      if (u + 2 < 2 * NB) nf = trnat(kt, (u + 2) / NB, 32 * ((u + 2) % NB), lane);
+      acc[u % NB] = mfma(u < NB ? a0 : a1, f0, acc[u % NB]);
+      f0 = f1;
+      f1 = nf;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // lane holds column 32 x + lane % 32, heads h0 + 8 (j / 4) + 4 half + (j % 4)
+  const float scl = a.scale;  // dQ sums dS' = dS / scale
+#pragma unroll
+  for (int x = 0; x < NB; ++x)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int hh = h0 + 8 * (j >> 2) + 4 * half + (j & 3);
+      a.dq[((int64_t)i * hq + hh) * kTQ + 32 * x + (lane & 31)] = scl * acc[x][j];
+    }
+}
+
 unsigned grid_of(int64_t items, int per) { return (unsigned)((items + per - 1) / per); }
 
 }  // namespace
 
 bool attn_bwd_token_mfma_supported(int mode, int dtype, int dqk, int dv, int hq, int hkv,
                                    int idx_heads, int idx_width) {
-  return mode == CSA_SEL_TOKEN && dtype == CSA_BF16 && dqk == kTQ && dv == kTV &&
-         idx_heads == 1 && idx_width < 65536 && hq % hkv == 0 && (hq / hkv) % kTI == 0;
+  if (mode != CSA_SEL_TOKEN || dtype != CSA_BF16 || dqk != kTQ || dv != kTV ||
+      idx_heads != 1 || idx_width > kMaxW || hq % hkv)
+    return false;
+  const int G = hq / hkv;
+  return G == 32 || G == 64 || G == 128;
 }
 
 int attn_bwd_token_chunks(int n_q) { return (n_q + kTRows - 1) / kTRows; }
 int attn_bwd_token_kvp(int n_kv) { return (n_kv + kTK - 1) / kTK * kTK; }
+int attn_bwd_token_w32(int idx_width) { return (idx_width + kDS - 1) / kDS * kDS; }
 
-hipError_t launch_attn_bwd_token_dkdv(const BwTokArgs& a0, hipStream_t stream) {
+hipError_t launch_attn_bwd_token(const BwTokArgs& a0, hipStream_t stream) {
   hipError_t e;
   BwTokArgs a = a0;
   const int64_t pairs = (int64_t)a.L.n_q * a.q.h;
@@ -452,7 +676,15 @@ hipError_t launch_attn_bwd_token_dkdv(const BwTokArgs& a0, hipStream_t stream) {
     hipLaunchKernelGGL(k_bwtm_rec, dim3(grid_of(pairs, 256)), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (a.L.n_kv == 0) return hipSuccess;
+  if (a.L.n_kv == 0) {  // no keys: dQ is zero (dK, dV have no rows)
+    const int64_t words = pairs * kTQ;
+    if (words > 0) {
+      hipLaunchKernelGGL(k_bwtm_fill, dim3((unsigned)std::min<int64_t>(4096, grid_of(words, 256))),
+                         dim3(256), 0, stream, reinterpret_cast<uint32_t*>(a.dq), words);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   const int64_t wgs = (int64_t)a.k.h * (a.n_kvp / kTK) * a.n_chunks;
   int slot;
   trace_begin(stream, "k_bwtm_dkdv", &slot);
@@ -462,6 +694,20 @@ hipError_t launch_attn_bwd_token_dkdv(const BwTokArgs& a0, hipStream_t stream) {
   hipLaunchKernelGGL(k_bwtm_reduce,
                      dim3(grid_of((int64_t)a.L.n_kv * a.k.h * (kTPart / 4), 256)), dim3(256), 0,
                      stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.L.n_q == 0) return hipSuccess;
+  const int G = a.q.h / a.k.h;
+  const dim3 grid((unsigned)((int64_t)a.L.n_q * a.k.h)), block((unsigned)(G / 32 * kWave));
+  const bool va = a.v.data == a.k.data && a.v.stride_n == a.k.stride_n &&
+                  a.v.stride_h == a.k.stride_h;
+  trace_begin(stream, "k_bwtm_ds", &slot);
+  if (va) hipLaunchKernelGGL(k_bwtm_ds<true>, grid, block, 0, stream, a);
+  else hipLaunchKernelGGL(k_bwtm_ds<false>, grid, block, 0, stream, a);
+  trace_end(stream, slot);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  trace_begin(stream, "k_bwtm_dq", &slot);
+  hipLaunchKernelGGL(k_bwtm_dq, grid, block, 0, stream, a);
+  trace_end(stream, slot);
   return hipGetLastError();
 }
 
