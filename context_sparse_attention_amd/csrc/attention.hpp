@@ -82,22 +82,17 @@ struct BwTokArgs {
   const float* lse;         // [n_q, Hq]
   const float* delta;       // [n_q, Hq]
   float scale, scale_log2;
-  float *dk, *dv;
-  uint16_t* cmap;           // [n_q, n_kvp] selection counts
-  int n_kvp;                // n_kv rounded up to 64
-  float* rec;               // [n_q, Hq / 32, 64]
-  float* part;              // [n_chunks, n_kvp, Hkv, 1088]
-  int n_chunks;
+  float *dq, *dk, *dv;
   __bf16* dout16;           // [n_q, Hq, 512]: room for the rounded dO
-  __bf16* ds;               // [n_q, Hq, w32]: dS' per slot
-  int w32;                  // idx_width rounded up to 32
-  float* dq;
+  __bf16 *ds, *pb;          // [n_q, Hq, wpad]: dS' and P per slot
+  int wpad;                 // idx_width rounded up to 128
+  __bf16 *ck, *cv;          // [n_q * idx_width, Hkv, 576 / 512]: per-slot contributions
+  const int32_t* list_off;  // [n_kv + 1]: each key's slots (flat slot ids, ascending)
+  const int32_t* entries;
 };
 bool attn_bwd_token_mfma_supported(int mode, int dtype, int dqk, int dv, int hq, int hkv,
                                    int idx_heads, int idx_width);
-int attn_bwd_token_chunks(int n_q);
-int attn_bwd_token_kvp(int n_kv);
-int attn_bwd_token_w32(int idx_width);
+int attn_bwd_token_wpad(int idx_width);
 // dK, dV and dQ
 hipError_t launch_attn_bwd_token(const BwTokArgs& a, hipStream_t stream);
 

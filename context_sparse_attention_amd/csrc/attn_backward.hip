@@ -449,13 +449,10 @@ struct BwLayout {
   int64_t n_part;      // its dQ partials (floats)
   int64_t n_info;      // its entry records
   int64_t n_dout16;    // its bf16 dO copy (elements)
-  bool tok;            // token-mode dK / dV on the matrix cores (no lists)
-  int n_kvp, n_chunks;
-  int64_t n_cmap;      // its count map (uint16)
-  int64_t n_rec;       // its per-(row, head block) records (floats)
-  int64_t n_tpart;     // its per-row-chunk partial sums (floats)
-  int64_t n_ds;        // its dS' per slot (bf16)
-  int w32;
+  bool tok;            // token mode on the matrix cores
+  int wpad;
+  int64_t n_ds;        // its dS' and P per slot (bf16, each)
+  int64_t n_ck, n_cv;  // its per-slot contributions (bf16)
 };
 
 BwLayout bw_layout(int n_q, int n_kv, int n_blocks, int mode, int dtype, int hq, int hkv,
@@ -480,22 +477,11 @@ BwLayout bw_layout(int n_q, int n_kv, int n_blocks, int mode, int dtype, int hq,
   b.n_info = b.mfma ? b.n_entries + 128 : 0;
   b.n_dout16 = b.mfma ? (int64_t)n_q * hq * dqk : 0;
   b.tok = attn_bwd_token_mfma_supported(mode, dtype, dqk, dv, hq, hkv, idx_heads, idx_width);
-  b.n_kvp = b.tok ? attn_bwd_token_kvp(n_kv) : 0;
-  b.n_chunks = b.tok ? attn_bwd_token_chunks(n_q) : 0;
-  b.n_cmap = b.tok ? (int64_t)n_q * b.n_kvp : 0;
-  b.n_rec = b.tok ? (int64_t)n_q * hq * 2 : 0;
-  b.n_tpart = b.tok ? (int64_t)b.n_chunks * b.n_kvp * hkv * (dqk + dv) : 0;
-  b.w32 = b.tok ? attn_bwd_token_w32(idx_width) : 0;
-  b.n_ds = b.tok ? (int64_t)n_q * hq * b.w32 : 0;
-  if (b.tok) {
-    b.n_dout16 = (int64_t)n_q * hq * dv;
-    // no key lists: the count map takes their place
-    b.n_lists = 0;
-    b.R = 1;
-    b.n_hist = 0;
-    b.n_tiles = 0;
-    b.n_entries = 0;
-  }
+  b.wpad = b.tok ? attn_bwd_token_wpad(idx_width) : 0;
+  b.n_ds = b.tok ? (int64_t)n_q * hq * b.wpad : 0;
+  b.n_ck = b.tok ? (int64_t)n_q * idx_width * hkv * dqk : 0;
+  b.n_cv = b.tok ? (int64_t)n_q * idx_width * hkv * dv : 0;
+  if (b.tok) b.n_dout16 = (int64_t)n_q * hq * dv;
   return b;
 }
 
@@ -508,9 +494,7 @@ struct BwWs {
   int32_t* n_tiles;
   BwEntryInfo* info;
   __bf16* dout16;
-  uint16_t* cmap;
-  float *rec, *tpart;
-  __bf16* ds;
+  __bf16 *ds, *pb, *ck, *cv;
 };
 
 BwWs carve_bw(void* base, const BwLayout& b, int n_q, int hq, int n_seq, int n_blocks,
@@ -530,10 +514,10 @@ BwWs carve_bw(void* base, const BwLayout& b, int n_q, int hq, int n_seq, int n_b
   w.n_tiles = c.take<int32_t>(b.mfma ? 1 : 0);
   w.info = c.take<BwEntryInfo>(b.n_info);
   w.dout16 = c.take<__bf16>(b.n_dout16);
-  w.cmap = c.take<uint16_t>(b.n_cmap);
-  w.rec = c.take<float>(b.n_rec);
-  w.tpart = c.take<float>(b.n_tpart);
   w.ds = c.take<__bf16>(b.n_ds);
+  w.pb = c.take<__bf16>(b.n_ds);
+  w.ck = c.take<__bf16>(b.n_ck);
+  w.cv = c.take<__bf16>(b.n_cv);
   if (used) *used = c.used;
   return w;
 }
@@ -611,34 +595,6 @@ hipError_t launch_attn_backward(const AttnBwdArgs& x, hipStream_t stream) {
                        stream, a, x.o_dtype, x.dout_dtype);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (b.tok) {
-    BwTokArgs t;
-    t.q = x.q;
-    t.k = x.k;
-    t.v = x.v;
-    t.dout = x.dout;
-    t.dout_dtype = x.dout_dtype;
-    t.g16 = x.dout;
-    t.L = x.L;
-    t.idx = x.idx;
-    t.idx_width = x.idx_width;
-    t.lse = x.lse;
-    t.delta = w.delta;
-    t.scale = x.scale;
-    t.scale_log2 = x.scale * kLog2e;
-    t.dk = x.dk;
-    t.dv = x.dv;
-    t.cmap = w.cmap;
-    t.n_kvp = b.n_kvp;
-    t.rec = w.rec;
-    t.part = w.tpart;
-    t.n_chunks = b.n_chunks;
-    t.dout16 = w.dout16;
-    t.ds = w.ds;
-    t.w32 = b.w32;
-    t.dq = x.dq;
-    return launch_attn_bwd_token(t, stream);
-  }
   if (pairs > 0) {
     hipLaunchKernelGGL(k_bwd_hist, dim3(grid_for(b.R, kBwWaves)), dim3(kBwThreads), 0, stream,
                        a);
@@ -658,6 +614,34 @@ hipError_t launch_attn_backward(const AttnBwdArgs& x, hipStream_t stream) {
     hipLaunchKernelGGL(k_bwd_fill, dim3(grid_for(b.R, kBwWaves)), dim3(kBwThreads), 0, stream,
                        a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (b.tok) {
+    BwTokArgs t;
+    t.q = x.q;
+    t.k = x.k;
+    t.v = x.v;
+    t.dout = x.dout;
+    t.dout_dtype = x.dout_dtype;
+    t.g16 = x.dout;
+    t.L = x.L;
+    t.idx = x.idx;
+    t.idx_width = x.idx_width;
+    t.lse = x.lse;
+    t.delta = w.delta;
+    t.scale = x.scale;
+    t.scale_log2 = x.scale * kLog2e;
+    t.dq = x.dq;
+    t.dk = x.dk;
+    t.dv = x.dv;
+    t.dout16 = w.dout16;
+    t.ds = w.ds;
+    t.pb = w.pb;
+    t.wpad = b.wpad;
+    t.ck = w.ck;
+    t.cv = w.cv;
+    t.list_off = w.list_off;
+    t.entries = w.entries;
+    return launch_attn_bwd_token(t, stream);
   }
   if (b.mfma) {
     BwMfmaArgs m;

@@ -1,34 +1,24 @@
-// Token-mode backward of dK and dV on the matrix cores: one selection per
-// token (shared by every query head), bf16, Dqk = 576 and Dv = 512 (absorbed
-// MLA: the value may be the key's first 512 columns).
+// Token-mode backward on the matrix cores: one selection per token (shared by
+// every query head), bf16, Dqk = 576 and Dv = 512 (absorbed MLA: the value may be
+// the key's first 512 columns), 32, 64 or 128 query heads per key head.
 //
 // "Context parallel attention: exchange keys and merge softmax globally", masks
 // paragraph (key and value gradients go back to their owners); Megatron-LM issue
 // #4878, "Strategy: allgather CP mode", backward step.  With the forward's lse,
-// c(i, j) the number of times row i's index row holds key j (only permitted
-// keys count) and dS' = P (dP - D):
+// P = exp(scale q.k - lse) and dS' = P (dP - D), dP = dO.v, D = dO.O:
 //
-//   dv_j = sum_(i, h) c(i, j) P dO[i, h]      dk_j = scale sum_(i, h) c(i, j) dS' q[i, h]
+//   dq   = scale sum_slots dS' k          dv_j = sum_(slots holding j) sum_h P dO
+//   dk_j = scale sum_(slots holding j) sum_h dS' q
 //
-// The keys a token selects share no structure with its neighbours', so a key
-// tile has no common set of rows.  The kernel therefore runs key tiles against
-// every row whose permitted range meets the tile, masked by c: more products
-// than the selection needs (about 1 / density), but each one a dense MFMA tile
-// with its operands in LDS, instead of scattered per-key work.
-//
-//   k_bwtm_count  c(i, j) as a uint16 map [n_q, n_kv rounded up to 64]
-//   k_bwtm_rec    per (row, 32-head block): lse * log2(e) and D, 256 bytes
-//   k_bwtm_dout16 dO rounded to bf16 when it arrives in fp32
-//   k_bwtm_dkdv   one workgroup per (key head, 32 keys, 512 rows), four waves.
-//                 Per block of 32 items (32 heads of one row), waves 0 and 1 each
-//                 take half of S = Q K^T's contraction (half K rows in registers)
-//                 and waves 2 and 3 half of dP = dO V^T's; the partial sums meet
-//                 in LDS; waves 0 and 1 form P and each accumulates half of
-//                 dV^T += dO^T P, waves 2 and 3 form dS' and each half of
-//                 dK^T += Q^T dS'.  The next
-//                 block's rows, record and counts are copied global -> LDS while
-//                 the current one is computed.  Partial sums per row chunk.
-//   k_bwtm_reduce the row chunks' partial sums in chunk order
+//   k_bwtm_ds   per (row, key head): the row's selected keys gathered 32 slots at
+//               a time, S^T and dP^T against the heads' q and dO (in registers);
+//               dS' and P stored per slot in bf16
+//   k_bwtm_dq   the same gathered tiles: dq = scale dS' K
+//   k_bwtm_ckv  per (row, key head, 128 slots): each slot's contributions summed
+//               over the heads, C_K = dS'^T q and C_V = P^T dO, in bf16
+//   k_bwtm_kred per (key, key head): dk, dv = the sums of C_K, C_V over the key's
+//               slots, in list order (the lists of attn_backward.hip)
+// No floating-point atomics; results are bitwise reproducible.
 #include <algorithm>
 
 #include "attention.hpp"
@@ -45,15 +35,8 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTQ = 576;              // key / query width
 constexpr int kTV = 512;              // value width
-constexpr int kTI = 32;               // items (heads of one row) per block
-constexpr int kTK = 32;               // keys per workgroup
-constexpr int kTRows = 512;           // rows per workgroup
-constexpr int kTW = 4;                // waves
-constexpr int kTT = kTW * kWave;      // threads
-constexpr int kTQC = kTI * kTQ * 2 / 1024;  // 1 KiB copies of a block's query rows (36)
-constexpr int kTGC = kTI * kTV * 2 / 1024;  // ... of its dO rows (32)
-constexpr int kTC = kTQC + kTGC + 1;        // with the record / counts copy
-constexpr int kTPart = kTQ + kTV;     // floats per (chunk, key, key head) partial
+constexpr int kTQC = 32 * kTQ * 2 / 1024;  // 1 KiB copies of a 32-row key tile (36)
+constexpr int kTGC = 32 * kTV * 2 / 1024;  // ... of a value tile (32)
 constexpr float kL2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -87,76 +70,11 @@ __device__ __forceinline__ bf16x4 read_tr(const __bf16* base, int elem) {
   return __builtin_bit_cast(bf16x4, x);
 }
 
-// A operand [32 columns x 16 items] of a transposed item tile: items (16 st +
-// the permutation of the first product's accumulator rows), columns c0 .. c0 + 31.
-template <bool Q>
-__device__ __forceinline__ bf16x8 trfrag(const __bf16* t, int st, int c0, int lane) {
-  const int half = lane >> 5, c16 = lane & 15, grp = lane >> 4;
-  const int r = 16 * st + 4 * half + (c16 >> 2);
-  const int c = c0 + 16 * (grp & 1) + 4 * (c16 & 3);
-  const bf16x4 lo = read_tr(t, Q ? offq(r, c) : offg(r, c));
-  const bf16x4 hi = read_tr(t, Q ? offq(r + 8, c) : offg(r + 8, c));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// acc0 + acc1 = sum over k-steps of A rows (item tile t, row `it`, columns from e0)
-// times B[ks]: two
-// accumulator chains, each step's A fragments read two steps ahead, with a
-// scheduling fence per step so that the reads are not hoisted further (the
-// registers are spoken for).
-template <bool Q, int NKS>
-__device__ __forceinline__ void row_chains(const __bf16* t, int it, int half, int e0,
-                                           const bf16x8 (&bf)[kTQ / 32], f32x16& acc0,
-                                           f32x16& acc1) {
-  auto ld = [&](int ks) {
-    const int e = e0 + 16 * ks + 8 * half;
-    return *reinterpret_cast<const bf16x8*>(t + (Q ? offq(it, e) : offg(it, e)));
-  };
-  bf16x8 a0 = ld(0), a1 = ld(1);
-#pragma unroll
-  for (int ks = 0; ks < NKS; ks += 2) {
-    bf16x8 n0, n1;
-    if (ks + 2 < NKS) {
-      n0 = ld(ks + 2);
-      n1 = ld(ks + 3);
-    }
-    acc0 = mfma(a0, bf[ks], acc0);
-    acc1 = mfma(a1, bf[ks + 1], acc1);
-    a0 = n0;
-    a1 = n1;
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
 // ---- preparation --------------------------------------------------------------------------
 __global__ void k_bwtm_fill(uint32_t* p, int64_t n) {
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n;
        t += (int64_t)gridDim.x * blockDim.x)
     p[t] = 0u;
-}
-
-// c(i, j): one thread per index slot; repeated slots add again
-__global__ __launch_bounds__(256) void k_bwtm_count(BwTokArgs a) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= (int64_t)a.L.n_q * a.idx_width) return;
-  const int i = (int)(t / a.idx_width);
-  const RowKeys r = row_keys(a.L, i);
-  const int s = a.idx[t];
-  if (!r.valid || s < r.lo || s > r.hi) return;
-  const int64_t e = (int64_t)i * a.n_kvp + s;
-  uint32_t* w = reinterpret_cast<uint32_t*>(a.cmap) + (e >> 1);
-  atomicAdd(w, (e & 1) ? 0x10000u : 1u);
-}
-
-// per (row, 32-head block): lse * log2(e) for the 32 heads, then their D
-__global__ __launch_bounds__(256) void k_bwtm_rec(BwTokArgs a) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= (int64_t)a.L.n_q * a.q.h) return;
-  const int64_t i = t / a.q.h;
-  const int h = (int)(t % a.q.h);
-  float* rec = a.rec + (i * (a.q.h / kTI) + h / kTI) * 64;
-  rec[h % kTI] = a.lse[t] * kL2e;
-  rec[kTI + h % kTI] = a.delta[t];
 }
 
 __global__ __launch_bounds__(256) void k_bwtm_dout16(BwTokArgs a, __bf16* g16) {
@@ -170,246 +88,6 @@ __global__ __launch_bounds__(256) void k_bwtm_dout16(BwTokArgs a, __bf16* g16) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) r[k] = (__bf16)x[k];
   *reinterpret_cast<bf16x8*>(g16 + pair * kTV + e) = r;
-}
-
-// ---- dK, dV -------------------------------------------------------------------------------
-struct TkLds {
-  __bf16 q[2][kTI * kTQ];
-  __bf16 g[2][kTI * kTV];
-  float xs[kTW][kWave * 16];   // [wave][lane * 16 + j]: partial S or dP
-  float meta[2][256];          // [stage]: lse2[32], D[32], counts (32 x uint16), unused
-  int rows[kTRows];            // the chunk's rows that meet the key tile
-};
-
-__global__ __launch_bounds__(kTT, 1) void k_bwtm_dkdv(BwTokArgs a) {
-  __shared__ TkLds s;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int half = lane >> 5;
-  // waves 0, 1: halves of S's contraction (K rows in registers), then P and half
-  // of dV^T each; waves 2, 3: halves of dP's (V rows), then P, dS' and half of dK^T
-  const int role = wave >> 1;  // 0: S / dV^T, 1: dP / dK^T
-  const int hf = wave & 1;     // which half
-  const int n_tiles = a.n_kvp / kTK;
-  const int g = blockIdx.x / (n_tiles * a.n_chunks);
-  const int rem = blockIdx.x % (n_tiles * a.n_chunks);
-  const int kt = rem / a.n_chunks;
-  const int chunk = rem % a.n_chunks;
-  const int tk0 = kt * kTK;
-  const int hq = a.q.h;
-  const int G = hq / a.k.h;
-  const int nhb = G / kTI;
-  float* part = a.part + (((int64_t)chunk * a.n_kvp + tk0) * a.k.h + g) * kTPart;
-
-  // the chunk's rows whose permitted keys meet [tk0, tk0 + 64)
-  const int c0 = chunk * kTRows;
-  int nvis;
-  {
-    __shared__ int s_wave[kTW];
-    const int t0 = 2 * threadIdx.x;
-    int f[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = c0 + t0 + u;
-      f[u] = 0;
-      if (i < a.L.n_q) {
-        const RowKeys r = row_keys(a.L, i);
-        f[u] = r.valid && r.lo < tk0 + kTK && r.hi >= tk0;
-      }
-    }
-    const int cnt = f[0] + f[1];
-    int incl = cnt;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int y = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += y;
-    }
-    if (lane == kWave - 1) s_wave[wave] = incl;
-    __syncthreads();
-    int before = 0;
-    nvis = 0;
-    for (int w = 0; w < kTW; ++w) {
-      if (w < wave) before += s_wave[w];
-      nvis += s_wave[w];
-    }
-    int at = before + incl - cnt;
-    if (f[0]) s.rows[at++] = c0 + t0;
-    if (f[1]) s.rows[at] = c0 + t0 + 1;
-  }
-  const int n_blk = nvis * nhb;
-  if (n_blk == 0) {  // no row meets the tile: the partial sums are zero
-    for (int t = threadIdx.x; t < kTK * kTPart / 4; t += kTT) {
-      const int key = t / (kTPart / 4), d4 = t % (kTPart / 4);
-      *reinterpret_cast<float4*>(part + (int64_t)key * a.k.h * kTPart + 4 * d4) =
-          make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    return;
-  }
-  __syncthreads();  // s.rows complete
-
-  const __bf16* qb = static_cast<const __bf16*>(a.q.data);
-  const __bf16* gb = static_cast<const __bf16*>(a.g16.data);
-  // block b: row rows[b / nhb], heads g G + 32 (b % nhb) ..
-  auto copy_block = [&](int b) {
-    const int i = s.rows[b / nhb];
-    const int h0 = g * G + kTI * (b % nhb);
-    const int stg = b & 1;
-    for (int c = wave; c < kTC; c += kTW) {
-      if (c < kTQC) {
-        const int byte = 1024 * c + 16 * lane;
-        const int r = byte / (kTQ * 2);
-        const int pp = (byte % (kTQ * 2)) / 16;
-        const int e = (pp ^ swq(r)) * 8;
-        const __bf16* src = qb + (int64_t)i * a.q.stride_n + (int64_t)(h0 + r) * a.q.stride_h + e;
-        gather16_addr(src, __builtin_amdgcn_readfirstlane(lds_addr(&s.q[stg][0]) + 1024 * c));
-      } else if (c < kTQC + kTGC) {
-        const int r = c - kTQC;
-        const int e = (lane ^ swg(r)) * 8;
-        const __bf16* src =
-            gb + (int64_t)i * a.g16.stride_n + (int64_t)(h0 + r) * a.g16.stride_h + e;
-        gather16_addr(src, __builtin_amdgcn_readfirstlane(lds_addr(&s.g[stg][0]) + 1024 * r));
-      } else {
-        const float* rec = a.rec + ((int64_t)i * (hq / kTI) + h0 / kTI) * 64;
-        const void* src;
-        if (lane < 16) src = rec + 4 * lane;
-        else if (lane < 20) src = a.cmap + (int64_t)i * a.n_kvp + tk0 + 8 * (lane - 16);
-        else src = rec;
-        gather16_addr(src, __builtin_amdgcn_readfirstlane(lds_addr(&s.meta[stg][0])));
-      }
-    }
-  };
-  copy_block(0);
-
-  // B operands: half of the K row (role 0: 18 k-steps) or of the V row (role 1:
-  // 16) of key tk0 + lane % 32 (past the last key: the last one, counts are 0)
-  constexpr int NKS = kTQ / 32;  // 18
-  bf16x8 bf[NKS];
-  {
-    const int key = min(tk0 + (lane & 31), a.L.n_kv - 1);
-    const __bf16* src = role == 0 ? elem_ptr<__bf16>(a.k, key, g) + hf * (kTQ / 2)
-                                  : elem_ptr<__bf16>(a.v, key, g) + hf * (kTV / 2);
-    const int nks = role == 0 ? kTQ / 32 : kTV / 32;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      if (ks < nks) bf[ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks + 8 * half);
-  }
-  // role 0: dV^T rows 256 hf .. (8 blocks); role 1: dK^T rows 288 hf .. (9 blocks)
-  constexpr int NB = kTQ / 64;  // 9
-  f32x16 acc[NB];
-#pragma unroll
-  for (int x = 0; x < NB; ++x) acc[x] = f32x16{};
-  const int kl = lane & 31;
-
-  for (int b = 0; b < n_blk; ++b) {
-    // block b's copies have landed and every wave is past block b - 1
-    wait_gathers();
-    __syncthreads();
-    if (b + 1 < n_blk) copy_block(b + 1);
-    const int stg = b & 1;
-    const __bf16* sq = s.q[stg];
-    const __bf16* sg = s.g[stg];
-    const float* meta = s.meta[stg];
-    // partial S (role 0) or dP (role 1) over this wave's half of the contraction:
-    // rows = the block's 32 items, columns = the keys; lane holds key kl, items
-    // 8 (j / 4) + 4 half + (j % 4)
-    f32x16 acc0 = f32x16{}, acc1 = f32x16{};
-    const int it = lane & 31;
-    if (role == 0) row_chains<true, kTQ / 32>(sq, it, half, hf * (kTQ / 2), bf, acc0, acc1);
-    else row_chains<false, kTV / 32>(sg, it, half, hf * (kTV / 2), bf, acc0, acc1);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) acc0[j] += acc1[j];
-    float* xw = &s.xs[wave][lane * 16];
-#pragma unroll
-    for (int j = 0; j < 16; j += 4)
-      *reinterpret_cast<float4*>(xw + j) = make_float4(acc0[j], acc0[j + 1], acc0[j + 2], acc0[j + 3]);
-    __syncthreads();
-    // P = c exp(S scale - lse) (a key the row does not select: exponent -inf);
-    // role 1 also dS' = P (dP - D); both in the B layout
-    const float cnt = (float)reinterpret_cast<const uint16_t*>(meta + 64)[kl];
-    const float bias_off = cnt > 0.f ? 0.f : -INFINITY;
-    bf16x8 ob[2];
-    const float* s0 = &s.xs[0][lane * 16];
-    const float* s1 = &s.xs[1][lane * 16];
-    const float* po = &s.xs[role == 1 ? (wave ^ 1) : 0][lane * 16];  // role 1: the other dP half
-#pragma unroll
-    for (int j = 0; j < 16; j += 4) {
-      float sv[4], dv4[4];
-      if (role == 0) {
-        const float4 o = *reinterpret_cast<const float4*>((hf ? s0 : s1) + j);
-        sv[0] = acc0[j] + o.x; sv[1] = acc0[j + 1] + o.y;
-        sv[2] = acc0[j + 2] + o.z; sv[3] = acc0[j + 3] + o.w;
-      } else {
-        const float4 x0 = *reinterpret_cast<const float4*>(s0 + j);
-        const float4 x1 = *reinterpret_cast<const float4*>(s1 + j);
-        const float4 o = *reinterpret_cast<const float4*>(po + j);
-        sv[0] = x0.x + x1.x; sv[1] = x0.y + x1.y; sv[2] = x0.z + x1.z; sv[3] = x0.w + x1.w;
-        dv4[0] = acc0[j] + o.x; dv4[1] = acc0[j + 1] + o.y;
-        dv4[2] = acc0[j + 2] + o.z; dv4[3] = acc0[j + 3] + o.w;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int jj = j + u;
-        const int q = 8 * (jj >> 2) + 4 * half + (jj & 3);
-        const float pv = cnt * exp2_raw(fmaf(sv[u], a.scale_log2, bias_off - meta[q]));
-        ob[jj >> 3][jj & 7] =
-            role == 0 ? (__bf16)pv : (__bf16)(pv * (dv4[u] - meta[kTI + q]));
-      }
-    }
-    // role 0: dV^T += dO^T P on rows 256 hf + 32 x (8 blocks); role 1: dK^T += Q^T dS'
-    // on rows 288 hf + 32 x (9 blocks); each A fragment read two steps ahead
-    const int nb = role == 0 ? kTV / 64 : kTQ / 64;
-    auto frag = [&](int u) {  // u = NB qs + x; role 0's step x = 8 reads block 7 (unused)
-      const int qs = u / NB, x = min(u % NB, nb - 1);
-      return role == 0 ? trfrag<false>(sg, qs, 256 * hf + 32 * x, lane)
-                       : trfrag<true>(sq, qs, 288 * hf + 32 * x, lane);
-    };
-    bf16x8 f0 = frag(0), f1 = frag(1);
-#pragma unroll
-    for (int u = 0; u < 2 * NB; ++u) {
-      bf16x8 nf;
-      if (u + 2 < 2 * NB) nf = frag(u + 2);
-      const int qs = u / NB, x = u % NB;
-      if (x < nb) acc[x] = mfma(f0, ob[qs], acc[x]);
-      f0 = f1;
-      f1 = nf;
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  // lane holds key tk0 + kl, rows 32 x + 8 (j / 4) + 4 half + (j % 4) of its part
-  float* out = part + (int64_t)kl * a.k.h * kTPart +
-               (role == 0 ? kTQ + 256 * hf : 288 * hf);
-  const float scl = role == 0 ? 1.f : a.scale;  // dK sums dS' = dS / scale
-  const int nb = role == 0 ? kTV / 64 : kTQ / 64;
-#pragma unroll
-  for (int x = 0; x < NB; ++x)
-    if (x < nb) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        *reinterpret_cast<float4*>(out + 32 * x + 8 * jj + 4 * half) =
-            make_float4(scl * acc[x][4 * jj], scl * acc[x][4 * jj + 1], scl * acc[x][4 * jj + 2],
-                        scl * acc[x][4 * jj + 3]);
-    }
-}
-
-// dk, dv = the row chunks' partial sums, added in chunk order
-__global__ __launch_bounds__(256) void k_bwtm_reduce(BwTokArgs a) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t per = kTPart / 4;
-  const int64_t kh = t / per;  // key * Hkv + g
-  if (kh >= (int64_t)a.L.n_kv * a.k.h) return;
-  const int d4 = (int)(t % per) * 4;
-  const int64_t stride = (int64_t)a.n_kvp * a.k.h * kTPart;
-  const float* p = a.part + kh * kTPart + d4;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c = 0; c < a.n_chunks; ++c) {
-    const float4 x = *reinterpret_cast<const float4*>(p + c * stride);
-    acc.x += x.x;
-    acc.y += x.y;
-    acc.z += x.z;
-    acc.w += x.w;
-  }
-  if (d4 < kTQ) *reinterpret_cast<float4*>(a.dk + kh * kTQ + d4) = acc;
-  else *reinterpret_cast<float4*>(a.dv + kh * kTV + (d4 - kTQ)) = acc;
 }
 
 // ---- dQ -----------------------------------------------------------------------------------
@@ -508,16 +186,22 @@ __global__ __launch_bounds__(256, 1) void k_bwtm_ds(BwTokArgs a) {
   const int64_t pair = (int64_t)i * hq + h;
   const float lse2 = a.lse[pair] * kL2e;
   const float dl = a.delta[pair];
-  __bf16* dsrow = a.ds + pair * a.w32;
-  bf16x8 prev[2];  // the previous tile's dS', stored once the next tile is under way
-  // lane holds slots 32 t + 8 jj + 4 half + 0 .. 3 in prev[jj / 2][4 (jj % 2) ..]
+  __bf16* dsrow = a.ds + pair * a.wpad;
+  __bf16* prow = a.pb + pair * a.wpad;
+  // the previous tile's dS' and P, stored once the next tile is under way; lane
+  // holds slots 32 t + 8 jj + 4 half + 0 .. 3 in [jj / 2][4 (jj % 2) ..]
+  bf16x8 prev[2], prevp[2];
   auto store_prev = [&](int t) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      bf16x4 v;
+      bf16x4 v, w;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = prev[jj >> 1][4 * (jj & 1) + u];
+      for (int u = 0; u < 4; ++u) {
+        v[u] = prev[jj >> 1][4 * (jj & 1) + u];
+        w[u] = prevp[jj >> 1][4 * (jj & 1) + u];
+      }
       *reinterpret_cast<bf16x4*>(dsrow + kDS * t + 8 * jj + 4 * half) = v;
+      *reinterpret_cast<bf16x4*>(prow + kDS * t + 8 * jj + 4 * half) = w;
     }
   };
   for (int t = 0; t < n_t; ++t) {
@@ -554,6 +238,7 @@ __global__ __launch_bounds__(256, 1) void k_bwtm_ds(BwTokArgs a) {
       const bool ok = slot < a.idx_width && s.key[min(slot, a.idx_width - 1)] >= 0;
       const float pv = exp2_raw(fmaf(s0[j] + s1[j], a.scale_log2, ok ? -lse2 : -INFINITY));
       prev[j >> 3][j & 7] = (__bf16)(pv * (p0[j] + p1[j] - dl));
+      prevp[j >> 3][j & 7] = (__bf16)pv;
     }
   }
   store_prev(n_t - 1);
@@ -588,7 +273,7 @@ __global__ __launch_bounds__(256, 1) void k_bwtm_dq(BwTokArgs a) {
     for (int u = 0; u < 2; ++u) {
       const int byte = 1024 * u + 16 * lane;
       const int hl = byte / (2 * kDS), sl = (byte % (2 * kDS)) / 2;
-      const __bf16* src = a.ds + ((int64_t)i * hq + h0 + hl) * a.w32 + kDS * t + sl;
+      const __bf16* src = a.ds + ((int64_t)i * hq + h0 + hl) * a.wpad + kDS * t + sl;
       gather16_addr(src, __builtin_amdgcn_readfirstlane(lds_addr(&s.ds[st][wave][0]) + 1024 * u));
     }
   };
@@ -632,6 +317,155 @@ __global__ __launch_bounds__(256, 1) void k_bwtm_dq(BwTokArgs a) {
     }
 }
 
+// ---- dK, dV -------------------------------------------------------------------------------
+// Row-centric: each selected slot's contributions, summed over the heads of its
+// key head, then added per key over the key's list of slots:
+//   k_bwtm_ckv  per (row, key head, 128 slots): C_K[slot] = sum_h dS'[h, slot] q[h]
+//               (576) and C_V[slot] = sum_h P[h, slot] dO[h] (512), bf16, as MFMA
+//               products over the heads with the slots' dS' and P and 64-column
+//               chunks of the heads' q and dO rows in LDS
+//   k_bwtm_kred per (key, key head): dk = scale sum C_K, dv = sum C_V over the
+//               key's slots in list order (no floating-point atomics)
+constexpr int kCS = 128;  // slots per k_bwtm_ckv workgroup
+constexpr int kCC = 64;   // columns per chunk
+
+__device__ __forceinline__ int sw128(int r) { return ((r >> 1) & 1) << 2; }
+__device__ __forceinline__ int sw256(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int offx(int r, int e) {  // [head][64 columns], 128-byte rows
+  return r * kCC + ((((e >> 3) ^ sw128(r))) << 3) + (e & 7);
+}
+__device__ __forceinline__ int offs(int r, int e) {  // [head][128 slots], 256-byte rows
+  return r * kCS + ((((e >> 3) ^ sw256(r))) << 3) + (e & 7);
+}
+
+struct CkLds {
+  __bf16 ds[128 * kCS];     // dS' of the group's heads
+  __bf16 p[128 * kCS];      // P
+  __bf16 x[2][128 * kCC];   // a 64-column chunk of the heads' q (chunks 0 .. 8) or dO (9 .. 16)
+};
+
+// operand [16 heads (natural order) x 32 columns] read transposed from a [head][...] tile
+template <bool S>
+__device__ __forceinline__ bf16x8 trh(const __bf16* t, int ks, int c0, int lane) {
+  const int half = lane >> 5, c16 = lane & 15, grp = lane >> 4;
+  const int r = 16 * ks + 8 * half + (c16 >> 2);
+  const int c = c0 + 16 * (grp & 1) + 4 * (c16 & 3);
+  const bf16x4 lo = read_tr(t, S ? offs(r, c) : offx(r, c));
+  const bf16x4 hi = read_tr(t, S ? offs(r + 4, c) : offx(r + 4, c));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__global__ __launch_bounds__(256, 1) void k_bwtm_ckv(BwTokArgs a) {
+  __shared__ CkLds s;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int half = lane >> 5;
+  const int hkv = a.k.h, hq = a.q.h, G = hq / hkv;
+  const int n_st = a.wpad / kCS;
+  const int i = blockIdx.x / (hkv * n_st);
+  const int g = (blockIdx.x / n_st) % hkv;
+  const int st = blockIdx.x % n_st;
+  const int W = a.idx_width;
+  if (kCS * st >= W) return;
+  const int h0 = g * G;
+  const __bf16* qb = static_cast<const __bf16*>(a.q.data);
+  const __bf16* gb = static_cast<const __bf16*>(a.g16.data);
+
+  // dS' and P of the G heads for the 128 slots: 4 heads per 1 KiB copy
+  for (int c = wave; c < 2 * (G / 4); c += 4) {
+    const int tn = c / (G / 4), m = c % (G / 4);
+    const int hh = 4 * m + lane / 16, pp = lane % 16;
+    const __bf16* src = (tn == 0 ? a.ds : a.pb) + ((int64_t)i * hq + h0 + hh) * a.wpad + kCS * st +
+                        8 * (pp ^ sw256(hh));
+    gather16_addr(src, __builtin_amdgcn_readfirstlane(lds_addr(tn == 0 ? s.ds : s.p) + 1024 * m));
+  }
+  // chunk c of the heads' q (c < 9) or dO rows: 8 heads per 1 KiB copy
+  auto copy_chunk = [&](int c) {
+    const bool qq = c < kTQ / kCC;
+    const int col = kCC * (qq ? c : c - kTQ / kCC);
+    for (int m = wave; m < G / 8; m += 4) {
+      const int hh = 8 * m + lane / 8, pp = lane % 8;
+      const __bf16* src =
+          qq ? qb + (int64_t)i * a.q.stride_n + (int64_t)(h0 + hh) * a.q.stride_h
+             : gb + (int64_t)i * a.g16.stride_n + (int64_t)(h0 + hh) * a.g16.stride_h;
+      gather16_addr(src + col + 8 * (pp ^ sw128(hh)),
+                    __builtin_amdgcn_readfirstlane(lds_addr(s.x[c & 1]) + 1024 * m));
+    }
+  };
+  copy_chunk(0);
+  constexpr int NCH = kTQ / kCC + kTV / kCC;  // 17
+  const int db = wave & 1;          // 32-column block of the chunk
+  const int sb = 2 * (wave >> 1);   // first of this wave's two 32-slot blocks
+  for (int c = 0; c < NCH; ++c) {
+    wait_gathers();
+    __syncthreads();
+    if (c + 1 < NCH) copy_chunk(c + 1);
+    const bool qq = c < kTQ / kCC;
+    const __bf16* xt = s.x[c & 1];
+    const __bf16* bt = qq ? s.ds : s.p;
+    // C^T [32 columns x 32 slots] = X^T [columns x heads] . B [heads x slots], twice
+    f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+    for (int ks = 0; ks < G / 16; ++ks) {
+      const bf16x8 af = trh<false>(xt, ks, 32 * db, lane);
+      acc0 = mfma(af, trh<true>(bt, ks, 32 * sb, lane), acc0);
+      acc1 = mfma(af, trh<true>(bt, ks, 32 * sb + 32, lane), acc1);
+    }
+    // lane holds slot 128 st + 32 (sb + u) + lane % 32, columns 32 db + 8 (j / 4) + 4 half + (j % 4)
+    const int dbase = kCC * (qq ? c : c - kTQ / kCC) + 32 * db + 4 * half;
+    __bf16* outb = qq ? a.ck : a.cv;
+    const int D = qq ? kTQ : kTV;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int slot = kCS * st + 32 * (sb + u) + (lane & 31);
+      if (slot >= W) continue;
+      const f32x16& acc = u == 0 ? acc0 : acc1;
+      __bf16* o = outb + (((int64_t)i * W + slot) * hkv + g) * D + dbase;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        bf16x4 v;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = (__bf16)acc[4 * jj + t];
+        *reinterpret_cast<bf16x4*>(o + 8 * jj) = v;
+      }
+    }
+  }
+}
+
+// one wave per (key, key head): its slots' contributions in list order
+__global__ __launch_bounds__(256) void k_bwtm_kred(BwTokArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t kp = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  const int hkv = a.k.h;
+  if (kp >= (int64_t)a.L.n_kv * hkv) return;
+  const int j = (int)(kp / hkv), g = (int)(kp % hkv);
+  const int e0 = a.list_off[j], e1 = a.list_off[j + 1];
+  float ak[8] = {}, ak2[8] = {}, av[8] = {};
+  auto add8 = [](float* acc, const bf16x8& v) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] += (float)v[t];
+  };
+  for (int e = e0; e < e1; ++e) {
+    const int64_t p = a.entries[e];  // row * W + slot
+    const __bf16* ckr = a.ck + (p * hkv + g) * kTQ;
+    const __bf16* cvr = a.cv + (p * hkv + g) * kTV;
+    add8(ak, *reinterpret_cast<const bf16x8*>(ckr + 8 * lane));
+    if (lane < kTQ / 8 - kWave) add8(ak2, *reinterpret_cast<const bf16x8*>(ckr + 8 * (kWave + lane)));
+    add8(av, *reinterpret_cast<const bf16x8*>(cvr + 8 * lane));
+  }
+  float* dk = a.dk + kp * kTQ;
+  float* dv = a.dv + kp * kTV;
+  const float scl = a.scale;  // dK sums dS' = dS / scale
+#pragma unroll
+  for (int t = 0; t < 8; t += 4) {
+    *reinterpret_cast<float4*>(dk + 8 * lane + t) =
+        make_float4(scl * ak[t], scl * ak[t + 1], scl * ak[t + 2], scl * ak[t + 3]);
+    if (lane < kTQ / 8 - kWave)
+      *reinterpret_cast<float4*>(dk + 8 * (kWave + lane) + t) =
+          make_float4(scl * ak2[t], scl * ak2[t + 1], scl * ak2[t + 2], scl * ak2[t + 3]);
+    *reinterpret_cast<float4*>(dv + 8 * lane + t) = make_float4(av[t], av[t + 1], av[t + 2], av[t + 3]);
+  }
+}
+
 unsigned grid_of(int64_t items, int per) { return (unsigned)((items + per - 1) / per); }
 
 }  // namespace
@@ -645,9 +479,7 @@ bool attn_bwd_token_mfma_supported(int mode, int dtype, int dqk, int dv, int hq,
   return G == 32 || G == 64 || G == 128;
 }
 
-int attn_bwd_token_chunks(int n_q) { return (n_q + kTRows - 1) / kTRows; }
-int attn_bwd_token_kvp(int n_kv) { return (n_kv + kTK - 1) / kTK * kTK; }
-int attn_bwd_token_w32(int idx_width) { return (idx_width + kDS - 1) / kDS * kDS; }
+int attn_bwd_token_wpad(int idx_width) { return (idx_width + kCS - 1) / kCS * kCS; }
 
 hipError_t launch_attn_bwd_token(const BwTokArgs& a0, hipStream_t stream) {
   hipError_t e;
@@ -663,19 +495,6 @@ hipError_t launch_attn_bwd_token(const BwTokArgs& a0, hipStream_t stream) {
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
-  const int64_t words = (int64_t)a.L.n_q * a.n_kvp / 2;
-  if (words > 0) {
-    hipLaunchKernelGGL(k_bwtm_fill, dim3((unsigned)std::min<int64_t>(4096, grid_of(words, 256))),
-                       dim3(256), 0, stream, reinterpret_cast<uint32_t*>(a.cmap), words);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  if (pairs > 0) {
-    hipLaunchKernelGGL(k_bwtm_count, dim3(grid_of((int64_t)a.L.n_q * a.idx_width, 256)),
-                       dim3(256), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_bwtm_rec, dim3(grid_of(pairs, 256)), dim3(256), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
   if (a.L.n_kv == 0) {  // no keys: dQ is zero (dK, dV have no rows)
     const int64_t words = pairs * kTQ;
     if (words > 0) {
@@ -685,28 +504,30 @@ hipError_t launch_attn_bwd_token(const BwTokArgs& a0, hipStream_t stream) {
     }
     return hipSuccess;
   }
-  const int64_t wgs = (int64_t)a.k.h * (a.n_kvp / kTK) * a.n_chunks;
   int slot;
-  trace_begin(stream, "k_bwtm_dkdv", &slot);
-  hipLaunchKernelGGL(k_bwtm_dkdv, dim3((unsigned)wgs), dim3(kTT), 0, stream, a);
-  trace_end(stream, slot);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_bwtm_reduce,
-                     dim3(grid_of((int64_t)a.L.n_kv * a.k.h * (kTPart / 4), 256)), dim3(256), 0,
-                     stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (a.L.n_q == 0) return hipSuccess;
   const int G = a.q.h / a.k.h;
-  const dim3 grid((unsigned)((int64_t)a.L.n_q * a.k.h)), block((unsigned)(G / 32 * kWave));
-  const bool va = a.v.data == a.k.data && a.v.stride_n == a.k.stride_n &&
-                  a.v.stride_h == a.k.stride_h;
-  trace_begin(stream, "k_bwtm_ds", &slot);
-  if (va) hipLaunchKernelGGL(k_bwtm_ds<true>, grid, block, 0, stream, a);
-  else hipLaunchKernelGGL(k_bwtm_ds<false>, grid, block, 0, stream, a);
-  trace_end(stream, slot);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  trace_begin(stream, "k_bwtm_dq", &slot);
-  hipLaunchKernelGGL(k_bwtm_dq, grid, block, 0, stream, a);
+  if (a.L.n_q > 0) {
+    const dim3 grid((unsigned)((int64_t)a.L.n_q * a.k.h)), block((unsigned)(G / 32 * kWave));
+    const bool va = a.v.data == a.k.data && a.v.stride_n == a.k.stride_n &&
+                    a.v.stride_h == a.k.stride_h;
+    trace_begin(stream, "k_bwtm_ds", &slot);
+    if (va) hipLaunchKernelGGL(k_bwtm_ds<true>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(k_bwtm_ds<false>, grid, block, 0, stream, a);
+    trace_end(stream, slot);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    trace_begin(stream, "k_bwtm_dq", &slot);
+    hipLaunchKernelGGL(k_bwtm_dq, grid, block, 0, stream, a);
+    trace_end(stream, slot);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    trace_begin(stream, "k_bwtm_ckv", &slot);
+    hipLaunchKernelGGL(k_bwtm_ckv, dim3((unsigned)((int64_t)a.L.n_q * a.k.h * (a.wpad / kCS))),
+                       dim3(256), 0, stream, a);
+    trace_end(stream, slot);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  trace_begin(stream, "k_bwtm_kred", &slot);
+  hipLaunchKernelGGL(k_bwtm_kred, dim3(grid_of((int64_t)a.L.n_kv * a.k.h, 4)), dim3(256), 0,
+                     stream, a);
   trace_end(stream, slot);
   return hipGetLastError();
 }
