@@ -342,7 +342,13 @@ struct CkLds {
   __bf16 ds[128 * kCS];     // dS' of the group's heads
   __bf16 p[128 * kCS];      // P
   __bf16 x[2][128 * kCC];   // a 64-column chunk of the heads' q (chunks 0 .. 8) or dO (9 .. 16)
+  __bf16 out[kCS * kCC];    // the chunk's results, slot-major, on their way out
 };
+
+// the output tile: 128-byte slot rows, piece p of row s at p ^ ((s / 2) % 8)
+__device__ __forceinline__ int offo(int s, int e) {
+  return s * kCC + ((((e >> 3) ^ ((s >> 1) & 7))) << 3) + (e & 7);
+}
 
 // operand [16 heads (natural order) x 32 columns] read transposed from a [head][...] tile
 template <bool S>
@@ -410,23 +416,30 @@ __global__ __launch_bounds__(256, 1) void k_bwtm_ckv(BwTokArgs a) {
       acc0 = mfma(af, trh<true>(bt, ks, 32 * sb, lane), acc0);
       acc1 = mfma(af, trh<true>(bt, ks, 32 * sb + 32, lane), acc1);
     }
-    // lane holds slot 128 st + 32 (sb + u) + lane % 32, columns 32 db + 8 (j / 4) + 4 half + (j % 4)
-    const int dbase = kCC * (qq ? c : c - kTQ / kCC) + 32 * db + 4 * half;
-    __bf16* outb = qq ? a.ck : a.cv;
-    const int D = qq ? kTQ : kTV;
+    // lane holds slot 32 (sb + u) + lane % 32 of the tile, columns 32 db + 8 (j / 4) +
+    // 4 half + (j % 4) of the chunk: through LDS, then out as whole 128-byte rows
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int slot = kCS * st + 32 * (sb + u) + (lane & 31);
-      if (slot >= W) continue;
       const f32x16& acc = u == 0 ? acc0 : acc1;
-      __bf16* o = outb + (((int64_t)i * W + slot) * hkv + g) * D + dbase;
+      const int sl = 32 * (sb + u) + (lane & 31);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         bf16x4 v;
 #pragma unroll
         for (int t = 0; t < 4; ++t) v[t] = (__bf16)acc[4 * jj + t];
-        *reinterpret_cast<bf16x4*>(o + 8 * jj) = v;
+        *reinterpret_cast<bf16x4*>(&s.out[offo(sl, 32 * db + 8 * jj + 4 * half)]) = v;
       }
+    }
+    __syncthreads();
+    __bf16* outb = qq ? a.ck : a.cv;
+    const int D = qq ? kTQ : kTV;
+    const int col = kCC * (qq ? c : c - kTQ / kCC);
+    for (int t = threadIdx.x; t < kCS * (kCC / 8); t += 256) {
+      const int sl = t / (kCC / 8), pc = t % (kCC / 8);
+      const int slot = kCS * st + sl;
+      if (slot < W)
+        *reinterpret_cast<bf16x8*>(outb + (((int64_t)i * W + slot) * hkv + g) * D + col + 8 * pc) =
+            *reinterpret_cast<const bf16x8*>(&s.out[offo(sl, 8 * pc)]);
     }
   }
 }
