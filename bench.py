@@ -336,11 +336,12 @@ def backward_stage(torch, csa, w, q, k, v, lay, idx, mode, out_dtype, reps=1):
                                               idx.shape[-1], w.block_size)
     # the matrix-core kernels price against the bf16 dense peak, the vector-ALU
     # ones against the fp32 vector peak
-    peak = PEAK_BF16_TFLOPS if family == "block_mfma" else PEAK_FP32_TFLOPS
+    on_mfma = family in ("block_mfma", "token_mfma")
+    peak = PEAK_BF16_TFLOPS if on_mfma else PEAK_FP32_TFLOPS
     return {"call": "sparse_attn_bwd_shard", "kernel_family": family, "ms": mean,
             "ms_min": float(np.min(ms)), "alg_gflop": flops / 1e9,
             "TFLOPs": flops / (mean * 1e-3) / 1e12,
-            "bound": "mfma" if family == "block_mfma" else "alu", "peak": peak,
+            "bound": "mfma" if on_mfma else "alu", "peak": peak,
             "frac": flops / (mean * 1e-3) / 1e12 / peak,
             "kernels_ms": {k_: float(np.mean(v_)) for k_, v_ in kern.items()},
             "reps": reps}

@@ -273,7 +273,8 @@ def sparse_attn_bwd_shard_workspace_size(q, k, v, layout, mode, idx_heads, idx_w
 
 
 def sparse_attn_bwd_shard_kernel(q, k, v, layout, mode, idx_heads, idx_width, block_size=0):
-    """The kernel family sparse_attn_bwd_shard runs: "block_mfma" or "generic"."""
+    """The kernel family sparse_attn_bwd_shard runs: "block_mfma", "token_mfma" or
+    "generic"."""
     name = lib.sparse_attn_bwd_shard_kernel(
         layout.c, mode, _dtype_code(q), q.shape[1], k.shape[1], q.shape[2], v.shape[2],
         idx_heads, idx_width, block_size)

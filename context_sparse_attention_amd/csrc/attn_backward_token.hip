@@ -155,9 +155,11 @@ __device__ __forceinline__ void gather_tile(const BwTokArgs& a, int g, const int
   }
 }
 
-// one workgroup per (row, key head); wave w takes query heads g G + 32 w ..
-template <bool VA>
-__global__ __launch_bounds__(256, 1) void k_bwtm_ds(BwTokArgs a) {
+// Separate value rows: one workgroup per (row, key head); wave w takes query heads
+// g G + 32 w .. and forms both S^T and dP^T (the K and V tiles leave no LDS for
+// handing P between waves)
+__global__ __launch_bounds__(256, 1) void k_bwtm_ds_v(BwTokArgs a) {
+  constexpr bool VA = false;
   __shared__ DsLds<VA> s;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -242,6 +244,121 @@ __global__ __launch_bounds__(256, 1) void k_bwtm_ds(BwTokArgs a) {
     }
   }
   store_prev(n_t - 1);
+}
+
+// The value is the key's first 512 columns: one gathered tile serves both products,
+// and each block of 32 heads gets two waves, one forming S^T (the heads' Q^T
+// fragments in registers, 144 of them) and one forming dP^T (dO^T, 128), so neither
+// runs out of registers at two waves per SIMD.  The S wave hands P (fp32) to the dP
+// wave through LDS; the dP wave forms dS' = P (dP - D) one tile later, which keeps
+// one barrier per tile: P of tile t is written after barrier t into stage t % 2 and
+// read after barrier t + 1, before stage t % 2 is written again after barrier t + 2.
+struct SdpLds {
+  __bf16 k[2][kDS * kTQ];
+  float4 xp[2][4][4][kWave];  // [stage][head block][j / 4][lane]: P in accumulator order
+  int key[kMaxW];
+};
+
+template <bool SW>
+__device__ __forceinline__ void sdp_role(const BwTokArgs& a, SdpLds& s, int i, int g, int hb,
+                                         int kfb, int nw, int wave, int lane) {
+  const int half = lane >> 5;
+  const int hq = a.q.h, G = hq / a.k.h;
+  const int h = g * G + 32 * hb + (lane & 31);  // this lane's head (B-operand column)
+  constexpr int NF = (SW ? kTQ : kTV) / 16;
+  bf16x8 f[NF];
+  {
+    const __bf16* fp = SW ? elem_ptr<__bf16>(a.q, i, h) : elem_ptr<__bf16>(a.g16, i, h);
+#pragma unroll
+    for (int ks = 0; ks < NF; ++ks)
+      f[ks] = *reinterpret_cast<const bf16x8*>(fp + 16 * ks + 8 * half);
+  }
+  const int64_t pair = (int64_t)i * hq + h;
+  const float lse2 = SW ? a.lse[pair] * kL2e : 0.f;
+  const float dl = SW ? 0.f : a.delta[pair];
+  __bf16* orow = (SW ? a.pb : a.ds) + pair * a.wpad;
+  const int n_t = (a.idx_width + kDS - 1) / kDS;
+  const int r = lane & 31;
+  // lane holds head h, slots 32 t + 8 (j / 4) + 4 half + (j % 4); the previous tile's
+  // results (P, or dP - D) wait here for the next iteration
+  float prev[16];
+  auto store = [&](int t, const float* x) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      bf16x4 v;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = (__bf16)x[4 * jj + u];
+      *reinterpret_cast<bf16x4*>(orow + kDS * t + 8 * jj + 4 * half) = v;
+    }
+  };
+  for (int t = 0; t <= n_t; ++t) {
+    wait_gathers();
+    __syncthreads();
+    if (t + 1 < n_t)
+      gather_tile<true>(a, g, s.key, kfb, t + 1, s.k[(t + 1) & 1], nullptr, nw, wave, lane);
+    if (t > 0) {
+      if (SW) {
+        store(t - 1, prev);
+      } else {
+        float ds[16];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float4 pv = s.xp[(t - 1) & 1][hb][jj][lane];
+          ds[4 * jj + 0] = pv.x * prev[4 * jj + 0];
+          ds[4 * jj + 1] = pv.y * prev[4 * jj + 1];
+          ds[4 * jj + 2] = pv.z * prev[4 * jj + 2];
+          ds[4 * jj + 3] = pv.w * prev[4 * jj + 3];
+        }
+        store(t - 1, ds);
+      }
+    }
+    if (t == n_t) break;
+    // row r's piece 2 ks + half sits at (2 ks + half) ^ swq(r): for ks = 4 q + u that is
+    // base u plus 8 q pieces, so four per-lane bases and immediate offsets suffice
+    const __bf16* kt = s.k[t & 1] + r * kTQ;
+    f32x16 c0 = f32x16{}, c1 = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < NF; ks += 2) {
+      const __bf16* b0 = kt + (((2 * (ks & 3) + half) ^ swq(r)) << 3) + 64 * (ks >> 2);
+      const __bf16* b1 = kt + (((2 * ((ks + 1) & 3) + half) ^ swq(r)) << 3) + 64 * (ks >> 2);
+      c0 = mfma(*reinterpret_cast<const bf16x8*>(b0), f[ks], c0);
+      c1 = mfma(*reinterpret_cast<const bf16x8*>(b1), f[ks + 1], c1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (SW) {
+      // slots past the width or selecting no permitted key get P = 0
+      const int sl = kDS * t + r;
+      const int kk = s.key[min(sl, a.idx_width - 1)];
+      const uint64_t ok = __ballot(sl < a.idx_width && kk >= 0);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const bool on = (ok >> (8 * (j >> 2) + 4 * half + (j & 3))) & 1;
+        prev[j] = exp2_raw(fmaf(c0[j] + c1[j], a.scale_log2, on ? -lse2 : -INFINITY));
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        s.xp[t & 1][hb][jj][lane] = make_float4(prev[4 * jj], prev[4 * jj + 1],
+                                                prev[4 * jj + 2], prev[4 * jj + 3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) prev[j] = c0[j] + c1[j] - dl;
+    }
+  }
+}
+
+// one workgroup per (row, key head): waves 0 .. G/32 - 1 form S^T for head block w,
+// waves G/32 .. G/16 - 1 dP^T for head block w - G/32
+__global__ __launch_bounds__(512, 1) void k_bwtm_ds(BwTokArgs a) {
+  __shared__ SdpLds s;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int nw = blockDim.x / kWave, nb = nw / 2;
+  const int i = blockIdx.x / a.k.h, g = blockIdx.x % a.k.h;
+  const int kfb = stage_slots(a, i, s.key);
+  __syncthreads();
+  gather_tile<true>(a, g, s.key, kfb, 0, s.k[0], nullptr, nw, wave, lane);
+  if (wave < nb) sdp_role<true>(a, s, i, g, wave, kfb, nw, wave, lane);
+  else sdp_role<false>(a, s, i, g, wave - nb, kfb, nw, wave, lane);
 }
 
 // B operand [16 slots x 32 columns] of a gathered key tile, slots in natural order
@@ -524,8 +641,8 @@ hipError_t launch_attn_bwd_token(const BwTokArgs& a0, hipStream_t stream) {
     const bool va = a.v.data == a.k.data && a.v.stride_n == a.k.stride_n &&
                     a.v.stride_h == a.k.stride_h;
     trace_begin(stream, "k_bwtm_ds", &slot);
-    if (va) hipLaunchKernelGGL(k_bwtm_ds<true>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(k_bwtm_ds<false>, grid, block, 0, stream, a);
+    if (va) hipLaunchKernelGGL(k_bwtm_ds, grid, dim3(2 * block.x), 0, stream, a);
+    else hipLaunchKernelGGL(k_bwtm_ds_v, grid, block, 0, stream, a);
     trace_end(stream, slot);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     trace_begin(stream, "k_bwtm_dq", &slot);

@@ -243,7 +243,12 @@ const char* sparse_attn_fwd_shard_kernel(const csa_tensor3* q, const csa_tensor3
  * each dq over its slots in order: bitwise reproducible, no floating-point atomics.
  * bf16 block mode with D = Dqk = Dv in {64, 128} and idx_heads = Hq runs on the
  * matrix cores ("block_mfma": P and dS rounded to bf16 as operands, as P is in
- * the forward; fp32 accumulation); every other case runs fp32 arithmetic on the
+ * the forward; fp32 accumulation).  bf16 token mode with one selection per row
+ * (idx_heads = 1), idx_width <= 4096, Dqk = 576, Dv = 512 (the absorbed-MLA
+ * shape) and Hq / Hkv in {32, 64, 128} runs on the matrix cores too
+ * ("token_mfma": P and dS as bf16 operands; each slot's dK and dV
+ * contributions, summed over the group's heads in fp32, are stored in bf16 and
+ * then summed per key in fp32).  Every other case runs fp32 arithmetic on the
  * vector ALUs ("generic").
  *
  *  q, k, v, idx, idx_heads, idx_width, block_size, softmax_scale, L, mode: as in
@@ -257,7 +262,10 @@ const char* sparse_attn_fwd_shard_kernel(const csa_tensor3* q, const csa_tensor3
  *     every element written (0 where nothing contributes).
  *  ws: at least sparse_attn_bwd_shard_workspace_size() bytes, 256-byte aligned (it
  *     holds D, the block table and the key lists: about 4 bytes per index slot; on
- *     the "block_mfma" path also one fp32 dq partial per slot, 4 * Dqk bytes).
+ *     the "block_mfma" path also one fp32 dq partial per slot, 4 * Dqk bytes; on the
+ *     "token_mfma" path also dS and P per (row, head, slot), 4 bytes, and the
+ *     per-slot contributions, 2 * Hkv * (Dqk + Dv) bytes per (row, slot): about
+ *     22.5 GB for 4096 rows of 2048 slots, 128 heads, one latent head).
  *  n_q * Hq and n_q * idx_heads * idx_width must stay below 2^31.
  * ------------------------------------------------------------------------------- */
 /* The workspace of a call with q [n_q, hq, dqk] and v [n_kv, hkv, dv] of dtype
@@ -267,7 +275,7 @@ size_t sparse_attn_bwd_shard_workspace_size(const csa_layout* L, int32_t mode, i
                                             int32_t hq, int32_t hkv, int32_t dqk, int32_t dv,
                                             int32_t idx_heads, int32_t idx_width,
                                             int32_t block_size);
-/* "block_mfma" or "generic": the kernel family such a call runs; NULL (with
+/* "block_mfma", "token_mfma" or "generic": the kernel family such a call runs; NULL (with
  * csa_last_error set) when the arguments are malformed. */
 const char* sparse_attn_bwd_shard_kernel(const csa_layout* L, int32_t mode, int32_t dtype,
                                          int32_t hq, int32_t hkv, int32_t dqk, int32_t dv,

@@ -152,6 +152,36 @@ def test_token_backward_matches_oracle(case, dtype):
     _compare(w, idx_np, got[3], got[:3], TOL[dtype], f"token {case} {dtype}")
 
 
+def test_token_backward_separate_value_rows_match_aliased():
+    """Absorbed-MLA shape with V passed as its own tensor (a copy of the key's first
+    512 columns): the separate-value kernel must give the aliased kernel's gradients
+    bit for bit, and both the oracle's."""
+    w = tiny_token_workload(seed=66, dtype="bf16", **TOKEN_CASES[1])
+    _say("token backward separate v")
+    d = upload(w)
+    idx = csa.dsa_indexer_topk(d["iq"], d["ik"], d["w"], d["layout"], w.topk)
+    assert _family(w, d, idx) == "token_mfma"
+    mode = csa.CSA_SEL_TOKEN
+    out, lse = csa.sparse_attn_fwd_shard(d["q"], d["k"], d["v"], d["layout"], mode, idx,
+                                         softmax_scale=w.scale)
+    dout_np = np.random.default_rng(5).standard_normal((w.n_q, w.hq, w.dv))
+    dout = torch.from_numpy(dout_np.astype(np.float32)).cuda()
+    got = []
+    for v in (d["v"], d["v"].contiguous()):
+        dq = poisoned((w.n_q, w.hq, w.dqk), torch.float32)
+        dk = poisoned((w.n_kv, w.hkv, w.dqk), torch.float32)
+        dv = poisoned((w.n_kv, w.hkv, w.dv), torch.float32)
+        csa.sparse_attn_bwd_shard(d["q"], d["k"], v, d["layout"], mode, idx, out, dout, lse,
+                                  softmax_scale=w.scale, dq=dq, dk=dk, dv=dv)
+        torch.cuda.synchronize()
+        got.append((dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()))
+    assert d["v"].data_ptr() == d["k"].data_ptr()
+    for name, a, b in zip(("dq", "dk", "dv"), got[0], got[1]):
+        assert np.array_equal(a, b), f"{name}: separate-value kernel differs from aliased"
+    _compare(w, idx.cpu().numpy()[:, None, :], dout_np.astype(np.float32), got[1], TOL["bf16"],
+             "token separate v")
+
+
 def test_token_backward_per_head_index_with_pads_and_repeats():
     w = tiny_token_workload(seed=67, hq=8, dqk=64, dv=64, lengths=(256,), dtype="bf16")
     rng = np.random.default_rng(67)
