@@ -111,7 +111,7 @@ struct DsLds {
 
 struct DqLds {
   __bf16 k[2][kDS * kTQ];
-  __bf16 ds[2][4][32 * kDS];  // [stage][wave][head][slot]
+  __bf16 ds[2][4][32 * kDS];  // [stage][head block][head][slot]
   int key[kMaxW];
 };
 
@@ -372,31 +372,32 @@ __device__ __forceinline__ bf16x8 trnat(const __bf16* t, int qs, int c0, int lan
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-__global__ __launch_bounds__(256, 1) void k_bwtm_dq(BwTokArgs a) {
+// one workgroup per (row, key head); wave w takes head block w % (G/32) and dQ
+// columns 288 (w / (G/32)) .. + 287: 144 accumulators per wave, two waves per SIMD
+__global__ __launch_bounds__(512, 1) void k_bwtm_dq(BwTokArgs a) {
   __shared__ DqLds s;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int nw = blockDim.x / kWave;
+  const int nw = blockDim.x / kWave, nb = nw / 2;
+  const int hb = wave % nb, ch = wave / nb;
   const int half = lane >> 5;
   const int i = blockIdx.x / a.k.h, g = blockIdx.x % a.k.h;
   const int hq = a.q.h, G = hq / a.k.h;
-  const int h0 = g * G + 32 * wave;  // this wave's first head
+  const int h0 = g * G + 32 * hb;  // this wave's first head
   const int kfb = stage_slots(a, i, s.key);
   __syncthreads();
   const int n_t = (a.idx_width + kDS - 1) / kDS;
-  // this wave's dS' tile t (32 heads x 32 slots, 2 KiB) into stage st
+  // half ch of head block hb's dS' tile t (32 heads x 32 slots, 2 KiB) into stage st
   auto copy_ds = [&](int t, int st) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int byte = 1024 * u + 16 * lane;
-      const int hl = byte / (2 * kDS), sl = (byte % (2 * kDS)) / 2;
-      const __bf16* src = a.ds + ((int64_t)i * hq + h0 + hl) * a.wpad + kDS * t + sl;
-      gather16_addr(src, __builtin_amdgcn_readfirstlane(lds_addr(&s.ds[st][wave][0]) + 1024 * u));
-    }
+    const int byte = 1024 * ch + 16 * lane;
+    const int hl = byte / (2 * kDS), sl = (byte % (2 * kDS)) / 2;
+    const __bf16* src = a.ds + ((int64_t)i * hq + h0 + hl) * a.wpad + kDS * t + sl;
+    gather16_addr(src, __builtin_amdgcn_readfirstlane(lds_addr(&s.ds[st][hb][0]) + 1024 * ch));
   };
   gather_tile<true>(a, g, s.key, kfb, 0, s.k[0], nullptr, nw, wave, lane);
   copy_ds(0, 0);
-  constexpr int NB = kTQ / 32;  // 18 column blocks of dQ
+  constexpr int NB = kTQ / 64;  // 9 column blocks of 32 per wave
+  const int cb = 32 * NB * ch;  // the wave's first column
   f32x16 acc[NB];
 #pragma unroll
   for (int x = 0; x < NB; ++x) acc[x] = f32x16{};
@@ -408,29 +409,29 @@ __global__ __launch_bounds__(256, 1) void k_bwtm_dq(BwTokArgs a) {
       copy_ds(t + 1, (t + 1) & 1);
     }
     const __bf16* kt = s.k[t & 1];
-    const __bf16* dt = s.ds[t & 1][wave];
+    const __bf16* dt = s.ds[t & 1][hb];
     // A operands: dS' rows of the wave's heads (m = head lane % 32), slots 16 qs + 8 half ..
     const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(dt + (lane & 31) * kDS + 8 * half);
     const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(dt + (lane & 31) * kDS + 16 + 8 * half);
-    bf16x8 f0 = trnat(kt, 0, 0, lane), f1 = trnat(kt, 0, 32, lane);
+    bf16x8 f0 = trnat(kt, 0, cb, lane), f1 = trnat(kt, 0, cb + 32, lane);
 #pragma unroll
     for (int u = 0; u < 2 * NB; ++u) {  // u = NB qs + x
       bf16x8 nf;
-      if (u + 2 < 2 * NB) nf = trnat(kt, (u + 2) / NB, 32 * ((u + 2) % NB), lane);
+      if (u + 2 < 2 * NB) nf = trnat(kt, (u + 2) / NB, cb + 32 * ((u + 2) % NB), lane);
       acc[u % NB] = mfma(u < NB ? a0 : a1, f0, acc[u % NB]);
       f0 = f1;
       f1 = nf;
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // lane holds column 32 x + lane % 32, heads h0 + 8 (j / 4) + 4 half + (j % 4)
+  // lane holds column cb + 32 x + lane % 32, heads h0 + 8 (j / 4) + 4 half + (j % 4)
   const float scl = a.scale;  // dQ sums dS' = dS / scale
 #pragma unroll
   for (int x = 0; x < NB; ++x)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int hh = h0 + 8 * (j >> 2) + 4 * half + (j & 3);
-      a.dq[((int64_t)i * hq + hh) * kTQ + 32 * x + (lane & 31)] = scl * acc[x][j];
+      a.dq[((int64_t)i * hq + hh) * kTQ + cb + 32 * x + (lane & 31)] = scl * acc[x][j];
     }
 }
 
@@ -646,7 +647,7 @@ hipError_t launch_attn_bwd_token(const BwTokArgs& a0, hipStream_t stream) {
     trace_end(stream, slot);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     trace_begin(stream, "k_bwtm_dq", &slot);
-    hipLaunchKernelGGL(k_bwtm_dq, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(k_bwtm_dq, grid, dim3(2 * block.x), 0, stream, a);
     trace_end(stream, slot);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     trace_begin(stream, "k_bwtm_ckv", &slot);
