@@ -456,11 +456,18 @@ __device__ __forceinline__ int offs(int r, int e) {  // [head][128 slots], 256-b
   return r * kCS + ((((e >> 3) ^ sw256(r))) << 3) + (e & 7);
 }
 
-struct CkLds {
-  __bf16 ds[128 * kCS];     // dS' of the group's heads
-  __bf16 p[128 * kCS];      // P
-  __bf16 x[2][128 * kCC];   // a 64-column chunk of the heads' q (chunks 0 .. 8) or dO (9 .. 16)
-  __bf16 out[kCS * kCC];    // the chunk's results, slot-major, on their way out
+// dS' and P of the G heads for the 128 slots are staged once and read into each
+// wave's registers (the B operands of its 32 slots); their LDS then holds the
+// double-buffered q / dO chunks and the output tile
+union CkLds {
+  struct {
+    __bf16 ds[128 * kCS];  // dS' of the group's heads
+    __bf16 p[128 * kCS];   // P
+  } b;
+  struct {
+    __bf16 x[2][128 * kCC];  // a 64-column chunk of the heads' q (chunks 0 .. 8) or dO (9 .. 16)
+    __bf16 out[kCS * kCC];   // the chunk's results, slot-major, on their way out
+  } c;
 };
 
 // the output tile: 128-byte slot rows, piece p of row s at p ^ ((s / 2) % 8)
@@ -479,12 +486,16 @@ __device__ __forceinline__ bf16x8 trh(const __bf16* t, int ks, int c0, int lane)
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-__global__ __launch_bounds__(256, 1) void k_bwtm_ckv(BwTokArgs a) {
+// one workgroup per (row, key head, 128 slots); wave w takes slots 32 w .. 32 w + 31
+// and both 32-column blocks of every chunk
+template <int G>
+__global__ __launch_bounds__(256, 2) void k_bwtm_ckv(BwTokArgs a) {
   __shared__ CkLds s;
+  constexpr int KS = G / 16;  // k-steps over the heads
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int half = lane >> 5;
-  const int hkv = a.k.h, hq = a.q.h, G = hq / hkv;
+  const int hkv = a.k.h, hq = a.q.h;
   const int n_st = a.wpad / kCS;
   const int i = blockIdx.x / (hkv * n_st);
   const int g = (blockIdx.x / n_st) % hkv;
@@ -501,8 +512,18 @@ __global__ __launch_bounds__(256, 1) void k_bwtm_ckv(BwTokArgs a) {
     const int hh = 4 * m + lane / 16, pp = lane % 16;
     const __bf16* src = (tn == 0 ? a.ds : a.pb) + ((int64_t)i * hq + h0 + hh) * a.wpad + kCS * st +
                         8 * (pp ^ sw256(hh));
-    gather16_addr(src, __builtin_amdgcn_readfirstlane(lds_addr(tn == 0 ? s.ds : s.p) + 1024 * m));
+    gather16_addr(src,
+                  __builtin_amdgcn_readfirstlane(lds_addr(tn == 0 ? s.b.ds : s.b.p) + 1024 * m));
   }
+  wait_gathers();
+  __syncthreads();
+  bf16x8 bd[KS], bp[KS];  // B operands [heads 16 ks .. x the wave's 32 slots]
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    bd[ks] = trh<true>(s.b.ds, ks, 32 * wave, lane);
+    bp[ks] = trh<true>(s.b.p, ks, 32 * wave, lane);
+  }
+  __syncthreads();
   // chunk c of the heads' q (c < 9) or dO rows: 8 heads per 1 KiB copy
   auto copy_chunk = [&](int c) {
     const bool qq = c < kTQ / kCC;
@@ -513,51 +534,51 @@ __global__ __launch_bounds__(256, 1) void k_bwtm_ckv(BwTokArgs a) {
           qq ? qb + (int64_t)i * a.q.stride_n + (int64_t)(h0 + hh) * a.q.stride_h
              : gb + (int64_t)i * a.g16.stride_n + (int64_t)(h0 + hh) * a.g16.stride_h;
       gather16_addr(src + col + 8 * (pp ^ sw128(hh)),
-                    __builtin_amdgcn_readfirstlane(lds_addr(s.x[c & 1]) + 1024 * m));
+                    __builtin_amdgcn_readfirstlane(lds_addr(s.c.x[c & 1]) + 1024 * m));
     }
   };
   copy_chunk(0);
   constexpr int NCH = kTQ / kCC + kTV / kCC;  // 17
-  const int db = wave & 1;          // 32-column block of the chunk
-  const int sb = 2 * (wave >> 1);   // first of this wave's two 32-slot blocks
+  const int sl = 32 * wave + (lane & 31);      // the lane's slot in the tile
   for (int c = 0; c < NCH; ++c) {
     wait_gathers();
     __syncthreads();
     if (c + 1 < NCH) copy_chunk(c + 1);
     const bool qq = c < kTQ / kCC;
-    const __bf16* xt = s.x[c & 1];
-    const __bf16* bt = qq ? s.ds : s.p;
-    // C^T [32 columns x 32 slots] = X^T [columns x heads] . B [heads x slots], twice
+    const __bf16* xt = s.c.x[c & 1];
+    // C^T [32 columns x 32 slots] = X^T [columns x heads] . B [heads x slots], per
+    // 32-column block
     f32x16 acc0 = f32x16{}, acc1 = f32x16{};
-    for (int ks = 0; ks < G / 16; ++ks) {
-      const bf16x8 af = trh<false>(xt, ks, 32 * db, lane);
-      acc0 = mfma(af, trh<true>(bt, ks, 32 * sb, lane), acc0);
-      acc1 = mfma(af, trh<true>(bt, ks, 32 * sb + 32, lane), acc1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8& b = qq ? bd[ks] : bp[ks];
+      acc0 = mfma(trh<false>(xt, ks, 0, lane), b, acc0);
+      acc1 = mfma(trh<false>(xt, ks, 32, lane), b, acc1);
     }
-    // lane holds slot 32 (sb + u) + lane % 32 of the tile, columns 32 db + 8 (j / 4) +
-    // 4 half + (j % 4) of the chunk: through LDS, then out as whole 128-byte rows
+    // lane holds slot sl, columns 32 u + 8 (j / 4) + 4 half + (j % 4) of the chunk:
+    // through LDS, then out as whole 128-byte rows
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const f32x16& acc = u == 0 ? acc0 : acc1;
-      const int sl = 32 * (sb + u) + (lane & 31);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         bf16x4 v;
 #pragma unroll
         for (int t = 0; t < 4; ++t) v[t] = (__bf16)acc[4 * jj + t];
-        *reinterpret_cast<bf16x4*>(&s.out[offo(sl, 32 * db + 8 * jj + 4 * half)]) = v;
+        *reinterpret_cast<bf16x4*>(&s.c.out[offo(sl, 32 * u + 8 * jj + 4 * half)]) = v;
       }
     }
     __syncthreads();
     __bf16* outb = qq ? a.ck : a.cv;
     const int D = qq ? kTQ : kTV;
     const int col = kCC * (qq ? c : c - kTQ / kCC);
+#pragma unroll
     for (int t = threadIdx.x; t < kCS * (kCC / 8); t += 256) {
-      const int sl = t / (kCC / 8), pc = t % (kCC / 8);
-      const int slot = kCS * st + sl;
+      const int ts = t / (kCC / 8), pc = t % (kCC / 8);
+      const int slot = kCS * st + ts;
       if (slot < W)
         *reinterpret_cast<bf16x8*>(outb + (((int64_t)i * W + slot) * hkv + g) * D + col + 8 * pc) =
-            *reinterpret_cast<const bf16x8*>(&s.out[offo(sl, 8 * pc)]);
+            *reinterpret_cast<const bf16x8*>(&s.c.out[offo(ts, 8 * pc)]);
     }
   }
 }
@@ -651,8 +672,10 @@ hipError_t launch_attn_bwd_token(const BwTokArgs& a0, hipStream_t stream) {
     trace_end(stream, slot);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     trace_begin(stream, "k_bwtm_ckv", &slot);
-    hipLaunchKernelGGL(k_bwtm_ckv, dim3((unsigned)((int64_t)a.L.n_q * a.k.h * (a.wpad / kCS))),
-                       dim3(256), 0, stream, a);
+    const dim3 cgrid((unsigned)((int64_t)a.L.n_q * a.k.h * (a.wpad / kCS)));
+    if (G == 32) hipLaunchKernelGGL(k_bwtm_ckv<32>, cgrid, dim3(256), 0, stream, a);
+    else if (G == 64) hipLaunchKernelGGL(k_bwtm_ckv<64>, cgrid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(k_bwtm_ckv<128>, cgrid, dim3(256), 0, stream, a);
     trace_end(stream, slot);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
