@@ -583,38 +583,69 @@ __global__ __launch_bounds__(256, 2) void k_bwtm_ckv(BwTokArgs a) {
   }
 }
 
-// one wave per (key, key head): its slots' contributions in list order
+// one workgroup per (key, key head): wave w adds the key's list entries w, w + 4, ..
+// (four entries' rows in flight at a time, their ids fetched 64 at a time), and the
+// four partial sums are added in wave order: a fixed order, so bitwise reproducible
+constexpr int kKC = kTQ + kTV;  // contribution columns per slot
+
+__device__ __forceinline__ void add8(float* acc, const bf16x8& v) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] += (float)v[t];
+}
+
 __global__ __launch_bounds__(256) void k_bwtm_kred(BwTokArgs a) {
+  __shared__ float part[4][kKC];
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t kp = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  const int wave = threadIdx.x / kWave;
   const int hkv = a.k.h;
-  if (kp >= (int64_t)a.L.n_kv * hkv) return;
+  const int64_t kp = blockIdx.x;
   const int j = (int)(kp / hkv), g = (int)(kp % hkv);
   const int e0 = a.list_off[j], e1 = a.list_off[j + 1];
+  const bool tail = lane < kTQ / 8 - kWave;  // lanes holding C_K columns 512 .. 575
   float ak[8] = {}, ak2[8] = {}, av[8] = {};
-  auto add8 = [](float* acc, const bf16x8& v) {
+  for (int base = e0 + wave; base < e1; base += 4 * kWave) {
+    // this wave's entries base, base + 4, .. (up to 64 of them), lane t holding the t-th
+    const int n = min(kWave, (e1 - base + 3) / 4);
+    const int mine = lane < n ? a.entries[base + 4 * lane] : 0;
+    int u = 0;
+    for (; u + 4 <= n; u += 4) {
+      bf16x8 k0[4], k1[4], v0[4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] += (float)v[t];
-  };
-  for (int e = e0; e < e1; ++e) {
-    const int64_t p = a.entries[e];  // row * W + slot
-    const __bf16* ckr = a.ck + (p * hkv + g) * kTQ;
-    const __bf16* cvr = a.cv + (p * hkv + g) * kTV;
-    add8(ak, *reinterpret_cast<const bf16x8*>(ckr + 8 * lane));
-    if (lane < kTQ / 8 - kWave) add8(ak2, *reinterpret_cast<const bf16x8*>(ckr + 8 * (kWave + lane)));
-    add8(av, *reinterpret_cast<const bf16x8*>(cvr + 8 * lane));
+      for (int x = 0; x < 4; ++x) {
+        const int64_t p = (int64_t)__builtin_amdgcn_readlane(mine, u + x) * hkv + g;
+        k0[x] = *reinterpret_cast<const bf16x8*>(a.ck + p * kTQ + 8 * lane);
+        if (tail) k1[x] = *reinterpret_cast<const bf16x8*>(a.ck + p * kTQ + 8 * (kWave + lane));
+        v0[x] = *reinterpret_cast<const bf16x8*>(a.cv + p * kTV + 8 * lane);
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        add8(ak, k0[x]);
+        if (tail) add8(ak2, k1[x]);
+        add8(av, v0[x]);
+      }
+    }
+    for (; u < n; ++u) {
+      const int64_t p = (int64_t)__builtin_amdgcn_readlane(mine, u) * hkv + g;
+      add8(ak, *reinterpret_cast<const bf16x8*>(a.ck + p * kTQ + 8 * lane));
+      if (tail) add8(ak2, *reinterpret_cast<const bf16x8*>(a.ck + p * kTQ + 8 * (kWave + lane)));
+      add8(av, *reinterpret_cast<const bf16x8*>(a.cv + p * kTV + 8 * lane));
+    }
   }
+  float* pw = part[wave];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    pw[8 * lane + t] = ak[t];
+    if (tail) pw[8 * (kWave + lane) + t] = ak2[t];
+    pw[kTQ + 8 * lane + t] = av[t];
+  }
+  __syncthreads();
   float* dk = a.dk + kp * kTQ;
   float* dv = a.dv + kp * kTV;
   const float scl = a.scale;  // dK sums dS' = dS / scale
-#pragma unroll
-  for (int t = 0; t < 8; t += 4) {
-    *reinterpret_cast<float4*>(dk + 8 * lane + t) =
-        make_float4(scl * ak[t], scl * ak[t + 1], scl * ak[t + 2], scl * ak[t + 3]);
-    if (lane < kTQ / 8 - kWave)
-      *reinterpret_cast<float4*>(dk + 8 * (kWave + lane) + t) =
-          make_float4(scl * ak2[t], scl * ak2[t + 1], scl * ak2[t + 2], scl * ak2[t + 3]);
-    *reinterpret_cast<float4*>(dv + 8 * lane + t) = make_float4(av[t], av[t + 1], av[t + 2], av[t + 3]);
+  for (int c = threadIdx.x; c < kKC; c += 256) {
+    const float x = ((part[0][c] + part[1][c]) + part[2][c]) + part[3][c];
+    if (c < kTQ) dk[c] = scl * x;
+    else dv[c - kTQ] = x;
   }
 }
 
@@ -680,7 +711,7 @@ hipError_t launch_attn_bwd_token(const BwTokArgs& a0, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   trace_begin(stream, "k_bwtm_kred", &slot);
-  hipLaunchKernelGGL(k_bwtm_kred, dim3(grid_of((int64_t)a.L.n_kv * a.k.h, 4)), dim3(256), 0,
+  hipLaunchKernelGGL(k_bwtm_kred, dim3((unsigned)((int64_t)a.L.n_kv * a.k.h)), dim3(256), 0,
                      stream, a);
   trace_end(stream, slot);
   return hipGetLastError();
