@@ -31,7 +31,7 @@
 // inputs widened).
 #include <algorithm>
 
-#include "attention.hpp"
+#include "backward.hpp"
 
 namespace csa {
 

@@ -23,7 +23,7 @@
 //                 added in slot order
 #include <algorithm>
 
-#include "attention.hpp"
+#include "backward.hpp"
 #include "gather.hpp"
 #include "mfma.hpp"
 

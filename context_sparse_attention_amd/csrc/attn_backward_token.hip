@@ -21,7 +21,7 @@
 // No floating-point atomics; results are bitwise reproducible.
 #include <algorithm>
 
-#include "attention.hpp"
+#include "backward.hpp"
 #include "gather.hpp"
 
 namespace csa {
