@@ -342,12 +342,231 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_tok_attn(AttnKernelArgs a) {
     }
 }
 
+// Absorbed-MLA widths (Dqk = 576, Dv = 512, V = the key's first 512 columns): 16 query
+// heads per wave on 16x16x32 MFMAs, so that a wave's Q^T fragments (72 registers) and
+// output accumulators (128) fit in half a SIMD's register file and two waves share
+// each SIMD: one wave's gather issue and softmax then run under the other's MFMAs
+// (a single wave per SIMD, as with 32 heads a wave, leaves the matrix core idle
+// through both).  Per 32-key tile each wave forms S^T = K Q^T over 18 column steps
+// for two 16-key halves, the softmax of its heads, and O^T += V^T P^T with the keys
+// in the order its score accumulators hold them: key k of step position 8 quad + t
+// is 4 quad + t (t < 4) or 16 + 4 quad + t - 4.
+template <int NW, typename TO>
+__global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void k_tok_attn16(AttnKernelArgs a) {
+  constexpr int DQK = 576, DV = 512;
+  constexpr int kPitch = DQK + 16;
+  constexpr int NKS = DQK / 32;  // score steps
+  constexpr int NDB = DV / 16;   // output blocks of 16 columns
+  // With eight waves, waves 4 .. 7 (the second wave on each SIMD) form O^T += V^T P^T
+  // of a tile at the start of the next one, so that one wave's softmax runs under the
+  // other's MFMAs; a tile then stays resident one tile longer (three buffers).
+  constexpr bool kStagger = NW == 8;
+  constexpr int NBUF = kStagger ? 3 : 2;
+  __shared__ __bf16 s_k[NBUF][kTK * kPitch];
+  __shared__ int s_keys[3][kTK];
+  __shared__ int s_valid[3][kTK];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int quad = lane >> 4, c16 = lane & 15;
+  const int hkv = a.k.h;
+  const int i = blockIdx.x / hkv;
+  const int g = blockIdx.x % hkv;
+  const int G = a.q.h / hkv;
+  const int head = g * G + wave * 16 + c16;
+  const RowKeys r = row_keys(a.L, i);
+  const int W = a.idx_width;
+  const int32_t* slots = a.idx + (int64_t)i * W;
+  const float c = a.scale_log2;
+
+  // B operands: Q^T [32 columns x 16 heads], lane: head c16, columns 32 ks + 8 quad ..
+  bf16x8 qf[NKS];
+  {
+    const __bf16* qp = elem_ptr<__bf16>(a.q, i, head);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks + 8 * quad);
+  }
+  typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+  f32x4 o[NDB];  // O^T: lane holds head c16, columns 16 db + 4 quad + 0 .. 3
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+
+  const int n_kt = r.valid ? (W + kTK - 1) / kTK : 0;
+  auto load_key = [&](int kt) {
+    const int j = kt * kTK + threadIdx.x;
+    return (threadIdx.x < kTK && j < W) ? slots[j] : -1;
+  };
+  auto store_key = [&](int kt, int key) {
+    if (threadIdx.x < kTK) {
+      const bool ok = key >= r.lo && key <= r.hi;
+      s_keys[kt % 3][threadIdx.x] = ok ? key : r.lo;  // masked slots read a valid row
+      s_valid[kt % 3][threadIdx.x] = ok;
+    }
+  };
+  auto issue = [&](int kt) { issue_tile<DQK>(a.k, g, s_keys[kt % 3], s_k[kt % NBUF], wave, NW); };
+  if (n_kt > 0) {
+    store_key(0, load_key(0));
+    if (n_kt > 1) store_key(1, load_key(1));
+    __syncthreads();
+    issue(0);
+  }
+  // on every path, so that no wait for the Q fragments stays inside the loop (where
+  // it would also wait for the next tile's gather)
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // per-lane byte offsets: score A operands (rows c16 and 16 + c16, column unit
+  // 4 ks + quad, swapped on row bit 3: the swap stays within the low two unit bits,
+  // so step ks adds 64 ks bytes) and value A operands (the two 4-key groups)
+  const int ka0 = tile_off<kPitch>(c16, 8 * quad);
+  const int ka1 = tile_off<kPitch>(16 + c16, 8 * quad);
+  const int va0 = tile_off<kPitch>(4 * quad + (c16 >> 2), 4 * (c16 & 3));
+  const int va1 = tile_off<kPitch>(16 + 4 * quad + (c16 >> 2), 4 * (c16 & 3));
+  const bool late = kStagger && wave >= NW / 2;  // wave-uniform
+  bf16x8 pb;  // P^T of the tile (a late wave's: of the previous tile, until its PV)
+  // O^T += V^T P^T over tile buffer b.  Value A operand of block db: columns
+  // 16 db + c16 of the lane's two key groups, read transposed (lane c16 of a 16-lane
+  // group addresses key base + c16 / 4 at column 16 db + 4 (c16 % 4) and receives
+  // column 16 db + c16 of the 4 keys); each MFMA has the next kVF in flight.
+  auto pv = [&](int b) {
+    constexpr int kVF = 3;
+    const __bf16* vt = s_k[b];
+    auto vf = [&](int db) {
+      const bf16x4 lo = read_tr(vt, va0 + 32 * db);
+      const bf16x4 hi = read_tr(vt, va1 + 32 * db);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8 vfr[kVF + 1];
+#pragma unroll
+    for (int t = 0; t < kVF; ++t) vfr[t] = vf(t);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      if (db + kVF < NDB) vfr[(db + kVF) % (kVF + 1)] = vf(db + kVF);
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr[db % (kVF + 1)], pb, o[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt % NBUF;
+    const int ks3 = kt % 3;
+    const int key2 = kt + 2 < n_kt ? load_key(kt + 2) : -1;
+    if (late && kt > 0) pv((kt - 1) % NBUF);
+    const char* kb = reinterpret_cast<const char*>(s_k[buf]);
+    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    {
+      // each step's two key fragments are read one step ahead of their MFMAs
+      auto kf = [&](int off) { return *reinterpret_cast<const bf16x8*>(kb + off); };
+      bf16x8 f0[2], f1[2];
+      f0[0] = kf(ka0);
+      f1[0] = kf(ka1);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (ks + 1 < NKS) {
+          f0[(ks + 1) & 1] = kf(ka0 + 64 * (ks + 1));
+          f1[(ks + 1) & 1] = kf(ka1 + 64 * (ks + 1));
+        }
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f0[ks & 1], qf[ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f1[ks & 1], qf[ks], s1, 0, 0, 0);
+        if (ks == 1 && kt + 1 < n_kt) issue(kt + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // lane: head c16, keys 4 quad + t (s0) and 16 + 4 quad + t (s1).  Bit k of the
+    // ballot: slot k of the tile selects a permitted key; shifted so that bit t is
+    // key 4 quad + t
+    const uint32_t ok = (uint32_t)(__ballot(s_valid[ks3][lane & (kTK - 1)] != 0) >> (4 * quad));
+    float x[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      x[t] = (ok >> t) & 1 ? s0[t] : -INFINITY;
+      x[4 + t] = (ok >> (16 + t)) & 1 ? s1[t] : -INFINITY;
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int t = 1; t < 8; ++t) mx = fmaxf(mx, x[t]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * c;
+    const bool need = mx > m + kLazy || (m == -INFINITY && mx > -INFINITY);
+    if (__any(need)) {  // (a late wave's O already holds the previous tile)
+      const float mn = need ? mx : m;
+      const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) o[db][t] *= alpha;
+      m = mn;
+    }
+    const float mu = (m == -INFINITY) ? 0.f : m;
+    float rs = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(x[t], c, -mu));
+      rs += p;
+      pb[t] = (__bf16)p;
+    }
+    rs += __shfl_xor(rs, 16, kWave);
+    rs += __shfl_xor(rs, 32, kWave);
+    l += rs;
+    if (!late) pv(buf);
+    if (kt + 2 < n_kt) store_key(kt + 2, key2);
+    __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct loads have landed
+    __syncthreads();
+  }
+  if (late && n_kt > 0) pv((n_kt - 1) % NBUF);
+  __syncthreads();  // every wave is done with the tiles before the output staging
+
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (a.lse && quad == 0)
+    a.lse[(int64_t)i * a.q.h + head] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  if constexpr (sizeof(TO) == 2) {
+    // the wave's 16 heads are 16 consecutive output rows: through the (now free) key
+    // tiles 256 columns at a time, then out as whole 16-byte row pieces
+    constexpr int kPart = 256;
+    constexpr int kRowB = kPart * 2 + 16;
+    static_assert(NW * 16 * kRowB <= (int)sizeof(s_k), "staging fits the key tiles");
+    char* st = reinterpret_cast<char*>(&s_k[0][0]) + wave * 16 * kRowB;
+    __bf16* wout = reinterpret_cast<__bf16*>(a.out) + ((int64_t)i * a.q.h + g * G + wave * 16) * DV;
+#pragma unroll
+    for (int pc = 0; pc < DV / kPart; ++pc) {
+#pragma unroll
+      for (int db = pc * kPart / 16; db < (pc + 1) * kPart / 16; ++db) {
+        const bf16x4 x4 = {(__bf16)(o[db][0] * inv), (__bf16)(o[db][1] * inv),
+                           (__bf16)(o[db][2] * inv), (__bf16)(o[db][3] * inv)};
+        *reinterpret_cast<bf16x4*>(st + c16 * kRowB + (16 * db + 4 * quad - pc * kPart) * 2) = x4;
+      }
+#pragma unroll
+      for (int e0 = 0; e0 < 16 * (kPart / 8); e0 += kWave) {
+        const int rr = (e0 + lane) / (kPart / 8), un = (e0 + lane) % (kPart / 8);
+        *reinterpret_cast<uint4*>(wout + (int64_t)rr * DV + pc * kPart + un * 8) =
+            *reinterpret_cast<const uint4*>(st + rr * kRowB + un * 16);
+      }
+    }
+  } else {
+    float* out = reinterpret_cast<float*>(a.out) + ((int64_t)i * a.q.h + head) * DV;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<float4*>(out + 16 * db + 4 * quad) =
+          make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
+  }
+}
+
 template <int DQK, int DV, bool ALIAS, typename TO>
 hipError_t launch_shape(const AttnKernelArgs& a, hipStream_t stream) {
   const int G = a.q.h / a.k.h;
   const dim3 grid((unsigned)a.L.n_q * a.k.h);
   int slot;
   trace_begin(stream, "k_tok_attn", &slot);
+  if constexpr (DQK == 576 && DV == 512 && ALIAS) {
+    if (G == 32)
+      hipLaunchKernelGGL((k_tok_attn16<2, TO>), grid, dim3(128), 0, stream, a);
+    else if (G == 64)
+      hipLaunchKernelGGL((k_tok_attn16<4, TO>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_tok_attn16<8, TO>), grid, dim3(512), 0, stream, a);
+    trace_end(stream, slot);
+    return hipGetLastError();
+  }
   if (G == 32)
     hipLaunchKernelGGL((k_tok_attn<DQK, DV, ALIAS, 1, TO>), grid, dim3(64), 0, stream, a);
   else if (G == 64)

@@ -142,9 +142,11 @@ TINY_TOKEN = [
     dict(hq=16, dqk=64, dv=64, hi=4, di=32, topk=37, lengths=(300, 212)),
     # MFMA kernel, one wave per workgroup (32 heads)
     dict(hq=32, dqk=128, dv=128, hi=4, di=64, topk=50, lengths=(400,)),
-    # MFMA kernel, two waves (64 heads), absorbed-MLA widths
+    # absorbed-MLA widths, 16 heads a wave: two waves (32 heads)
+    dict(hq=32, dqk=576, dv=512, hi=8, di=128, topk=60, lengths=(300,)),
+    # absorbed-MLA widths, four waves (64 heads)
     dict(hq=64, dqk=576, dv=512, hi=8, di=128, topk=100, lengths=(700,)),
-    # MFMA kernel, four waves (128 heads), absorbed-MLA widths
+    # absorbed-MLA widths, eight waves (128 heads)
     dict(hq=128, dqk=576, dv=512, hi=8, di=128, topk=70, lengths=(200, 150)),
 ]
 
