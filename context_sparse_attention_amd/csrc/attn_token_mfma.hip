@@ -62,9 +62,13 @@ struct TokLds {
 // phase of a ds_read_b128 touches then fall on distinct banks (measured on
 // gfx950: 152 B/clk per CU against 113 with the swap on rows 4..7 of every 8),
 // and the transposing value reads stay conflict-free.
-template <int PITCH>
+// The 16-heads-a-wave kernel's read patterns (16 rows x 4 units per ds_read_b128, 4
+// rows x 32 bytes per 16-lane group of the transposing read) are conflict-free with
+// the swap on row bit 2 instead (SQ_LDS_BANK_CONFLICT 0 for both; bit 3 costs ~4
+// conflict cycles per ds_read_b128).
+template <int PITCH, int SB = 3>
 __device__ __forceinline__ int tile_off(int r, int e) {
-  const int unit = (e >> 3) ^ ((r >> 3) & 1);
+  const int unit = (e >> 3) ^ ((r >> SB) & 1);
   return r * PITCH * 2 + unit * 16 + (e & 7) * 2;
 }
 
@@ -96,7 +100,7 @@ __device__ __forceinline__ float acc_scale(float x, float s) {
 // whole KiBs (32 rows of 2 (D + 16) bytes).  No registers hold the data.
 // (gather16_addr of gather.hpp: one instruction per KiB, the source as a
 // 64-bit address per lane, since a chunk spans rows of different tokens).
-template <int D>
+template <int D, int SB = 3>
 __device__ __forceinline__ void issue_tile(const View& T, int g, const int* keys, __bf16* tile,
                                            int wave, int nwaves) {
   constexpr int kPitchB = 2 * (D + 16);
@@ -108,7 +112,7 @@ __device__ __forceinline__ void issue_tile(const View& T, int g, const int* keys
     const int byte = ch * 1024 + lane * 16;
     const int row = byte / kPitchB;
     const int pu = (byte - row * kPitchB) >> 4;
-    const int u = pu < D / 8 ? (pu ^ ((row >> 3) & 1)) : 0;
+    const int u = pu < D / 8 ? (pu ^ ((row >> SB) & 1)) : 0;
     const __bf16* src = elem_ptr<__bf16>(T, keys[row], g) + u * 8;
     const uint32_t dst = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((lds_bytes)(void*)tile + ch * 1024));
@@ -404,7 +408,7 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void k_tok_attn16(Attn
       s_valid[kt % 3][threadIdx.x] = ok;
     }
   };
-  auto issue = [&](int kt) { issue_tile<DQK>(a.k, g, s_keys[kt % 3], s_k[kt % NBUF], wave, NW); };
+  auto issue = [&](int kt) { issue_tile<DQK, 2>(a.k, g, s_keys[kt % 3], s_k[kt % NBUF], wave, NW); };
   if (n_kt > 0) {
     store_key(0, load_key(0));
     if (n_kt > 1) store_key(1, load_key(1));
@@ -416,12 +420,12 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void k_tok_attn16(Attn
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   // per-lane byte offsets: score A operands (rows c16 and 16 + c16, column unit
-  // 4 ks + quad, swapped on row bit 3: the swap stays within the low two unit bits,
+  // 4 ks + quad, swapped on row bit 2: the swap stays within the low two unit bits,
   // so step ks adds 64 ks bytes) and value A operands (the two 4-key groups)
-  const int ka0 = tile_off<kPitch>(c16, 8 * quad);
-  const int ka1 = tile_off<kPitch>(16 + c16, 8 * quad);
-  const int va0 = tile_off<kPitch>(4 * quad + (c16 >> 2), 4 * (c16 & 3));
-  const int va1 = tile_off<kPitch>(16 + 4 * quad + (c16 >> 2), 4 * (c16 & 3));
+  const int ka0 = tile_off<kPitch, 2>(c16, 8 * quad);
+  const int ka1 = tile_off<kPitch, 2>(16 + c16, 8 * quad);
+  const int va0 = tile_off<kPitch, 2>(4 * quad + (c16 >> 2), 4 * (c16 & 3));
+  const int va1 = tile_off<kPitch, 2>(16 + 4 * quad + (c16 >> 2), 4 * (c16 & 3));
   const bool late = kStagger && wave >= NW / 2;  // wave-uniform
   bf16x8 pb;  // P^T of the tile (a late wave's: of the previous tile, until its PV)
   // O^T += V^T P^T over tile buffer b.  Value A operand of block db: columns
