@@ -560,8 +560,9 @@ hipError_t launch_shape(const AttnKernelArgs& a, hipStream_t stream) {
   const int G = a.q.h / a.k.h;
   const dim3 grid((unsigned)a.L.n_q * a.k.h);
   int slot;
-  trace_begin(stream, "k_tok_attn", &slot);
-  if constexpr (DQK == 576 && DV == 512 && ALIAS) {
+  constexpr bool k16 = DQK == 576 && DV == 512 && ALIAS;
+  trace_begin(stream, k16 ? "k_tok_attn16" : "k_tok_attn", &slot);
+  if constexpr (k16) {
     if (G == 32)
       hipLaunchKernelGGL((k_tok_attn16<2, TO>), grid, dim3(128), 0, stream, a);
     else if (G == 64)
