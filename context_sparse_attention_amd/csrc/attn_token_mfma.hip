@@ -346,6 +346,27 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_tok_attn(AttnKernelArgs a) {
     }
 }
 
+// Max and sum over lanes l and l ^ 16 (or l ^ 32) with the VALU lane swaps of gfx950:
+// each swap returns the pair (value of the lower, value of the upper 16- or 32-lane
+// group) in both lanes, so both lanes compute the same result in the same order.
+// (__shfl_xor goes through ds_bpermute, which queues behind the other wave's LDS reads.)
+__device__ __forceinline__ float pair16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Absorbed-MLA widths (Dqk = 576, Dv = 512, V = the key's first 512 columns): 16 query
 // heads per wave on 16x16x32 MFMAs, so that a wave's Q^T fragments (72 registers) and
 // output accumulators (128) fit in half a SIMD's register file and two waves share
@@ -488,8 +509,7 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void k_tok_attn16(Attn
     float mx = x[0];
 #pragma unroll
     for (int t = 1; t < 8; ++t) mx = fmaxf(mx, x[t]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * c;
+    mx = pair32_max(pair16_max(mx)) * c;
     const bool need = mx > m + kLazy || (m == -INFINITY && mx > -INFINITY);
     if (__any(need)) {  // (a late wave's O already holds the previous tile)
       const float mn = need ? mx : m;
@@ -509,9 +529,7 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void k_tok_attn16(Attn
       rs += p;
       pb[t] = (__bf16)p;
     }
-    rs += __shfl_xor(rs, 16, kWave);
-    rs += __shfl_xor(rs, 32, kWave);
-    l += rs;
+    l += pair32_sum(pair16_sum(rs));
     if (!late) pv(buf);
     if (kt + 2 < n_kt) store_key(kt + 2, key2);
     __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct loads have landed
