@@ -95,8 +95,26 @@ __global__ __launch_bounds__(kBwThreads) void k_bwd_delta(BwArgs a, int odt, int
   const int64_t pair = (int64_t)blockIdx.x * kBwWaves + threadIdx.x / kWave;
   if (pair >= (int64_t)a.L.n_q * a.q.h) return;
   const int i = (int)(pair / a.q.h), h = (int)(pair % a.q.h);
+  const int D = a.v.d;
   float acc = 0.f;
-  for (int d = lane; d < a.v.d; d += kWave) acc = fmaf(ld(a.dout, gdt, i, h, d), ld(a.o, odt, i, h, d), acc);
+  const void* gp = gdt == CSA_BF16 ? (const void*)elem_ptr<__bf16>(a.dout, i, h)
+                                   : (const void*)elem_ptr<float>(a.dout, i, h);
+  const void* op = odt == CSA_BF16 ? (const void*)elem_ptr<__bf16>(a.o, i, h)
+                                   : (const void*)elem_ptr<float>(a.o, i, h);
+  if (D % 8 == 0 && ((reinterpret_cast<uintptr_t>(gp) | reinterpret_cast<uintptr_t>(op)) & 15) == 0) {
+    // 8 consecutive elements a lane per step, 16-byte loads (wave-uniform branch)
+    for (int e = 8 * lane; e < D; e += 8 * kWave) {
+      float g[8], o[8];
+      if (gdt == CSA_BF16) load8(static_cast<const __bf16*>(gp) + e, g);
+      else load8(static_cast<const float*>(gp) + e, g);
+      if (odt == CSA_BF16) load8(static_cast<const __bf16*>(op) + e, o);
+      else load8(static_cast<const float*>(op) + e, o);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc = fmaf(g[t], o[t], acc);
+    }
+  } else {
+    for (int d = lane; d < D; d += kWave) acc = fmaf(ld(a.dout, gdt, i, h, d), ld(a.o, odt, i, h, d), acc);
+  }
   acc = wave_sum(acc);
   if (lane == 0) a.delta[pair] = acc;
 }
