@@ -180,6 +180,58 @@ def test_token_mode_per_head_index_and_pads():
     _check_out(w, idx, out, lse, list(range(w.n_q)), TOL["bf16"])
 
 
+def _mla_slots(rng, pos, n_kv, width, hot, hot_slot):
+    """Caller-made token selections: permitted keys, pads, future (masked) keys and
+    repeats of the previous slot; the hot key at hot_slot where the row may see it;
+    one row of pads only and one of future keys only."""
+    n_q = len(pos)
+    idx = np.full((n_q, width), -1, np.int32)
+    for i in range(n_q):
+        p = int(pos[i])
+        for s in range(width):
+            u = rng.random()
+            if u < 0.1:
+                continue
+            if u < 0.2 and p + 1 < n_kv:
+                idx[i, s] = rng.integers(p + 1, n_kv)
+            elif u < 0.3 and s > 0:
+                idx[i, s] = idx[i, s - 1]
+            else:
+                idx[i, s] = rng.integers(0, p + 1)
+        if p >= hot and width > hot_slot:
+            idx[i, hot_slot] = hot
+    idx[3] = -1
+    idx[11] = rng.integers(pos[11] + 1, n_kv, size=width)
+    return idx
+
+
+@pytest.mark.parametrize("hq", [64, 128])
+def test_token_mla_widths_edge_cases(hq):
+    """Absorbed-MLA widths (16 heads a wave; at 128 heads the second wave on each
+    SIMD forms P V one tile late): caller-made selections of 1, 5, 33 and 97 slots
+    with pads, repeats, future keys and rows without keys, and a key whose score
+    dwarfs the rest in the third tile, so that the running maximum moves after
+    the first tile; bf16 and f32 outputs, and the result repeats bit for bit."""
+    w = tiny_token_workload(seed=41, lengths=(300,), hq=hq, dqk=576, dv=512, hi=8, di=128,
+                            topk=16, dtype="bf16")
+    hot = 150
+    w.k[hot, :, 512:] *= 32.0  # rope columns only: scores grow, the value row does not
+    d = upload(w)
+    rng = np.random.default_rng(41)
+    for width in (1, 5, 33, 97):
+        idx_np = _mla_slots(rng, w.q_pos, w.n_kv, width, hot, hot_slot=70)
+        idx = torch.from_numpy(idx_np).cuda()
+        _say("token mla edges", hq, "width", width)
+        for out_dtype in (torch.float32, torch.bfloat16):
+            out, lse = _attn(w, d, idx, out_dtype=out_dtype)
+            for r in (3, 11):
+                assert not out[r].any() and (lse[r] == -np.inf).all()
+            tol = TOL["bf16"]
+            _check_out(w, idx_np[:, None, :], out, lse, list(range(w.n_q)), tol)
+            again = _attn(w, d, idx, out_dtype=out_dtype)
+            assert np.array_equal(out, again[0]) and np.array_equal(lse, again[1])
+
+
 def test_summary_merge_matches_oracle():
     _say("summary_merge")
     rng = np.random.default_rng(9)
