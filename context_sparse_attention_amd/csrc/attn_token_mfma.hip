@@ -479,20 +479,22 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void k_tok_attn16(Attn
     const char* kb = reinterpret_cast<const char*>(s_k[buf]);
     f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
     {
-      // each step's two key fragments are read one step ahead of their MFMAs
-      auto kf = [&](int off) { return *reinterpret_cast<const bf16x8*>(kb + off); };
-      bf16x8 f0[2], f1[2];
-      f0[0] = kf(ka0);
-      f1[0] = kf(ka1);
+      // MFMA j = 2 ks + half takes the key fragment of rows 16 half + c16 at step ks;
+      // fragments sit in a ring of four, read three MFMAs ahead of their use
+      auto kf = [&](int j) {
+        return *reinterpret_cast<const bf16x8*>(kb + ((j & 1) ? ka1 : ka0) + 64 * (j >> 1));
+      };
+      bf16x8 fr[4];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        if (ks + 1 < NKS) {
-          f0[(ks + 1) & 1] = kf(ka0 + 64 * (ks + 1));
-          f1[(ks + 1) & 1] = kf(ka1 + 64 * (ks + 1));
-        }
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f0[ks & 1], qf[ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f1[ks & 1], qf[ks], s1, 0, 0, 0);
-        if (ks == 1 && kt + 1 < n_kt) issue(kt + 1);
+      for (int j = 0; j < 3; ++j) fr[j] = kf(j);
+#pragma unroll
+      for (int j = 0; j < 2 * NKS; ++j) {
+        if (j + 3 < 2 * NKS) fr[(j + 3) & 3] = kf(j + 3);
+        if (j & 1)
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[j & 3], qf[j >> 1], s1, 0, 0, 0);
+        else
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[j & 3], qf[j >> 1], s0, 0, 0, 0);
+        if (j == 3 && kt + 1 < n_kt) issue(kt + 1);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
