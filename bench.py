@@ -69,6 +69,7 @@ KERNEL_SOURCES = {
     "k_bm_attn": ["attn_block_mfma.hip"],
     "k_tok_attn": ["attn_token_mfma.hip", "mfma.hpp"],
     "k_tok_attn16": ["attn_token_mfma.hip"],
+    "k_tok_attn16p": ["attn_token_mfma.hip"],
     "k_attn_generic": ["attn_generic.hip"],
 }
 COMMON_SOURCES = ["common.hpp", "attention.hpp"]
@@ -503,7 +504,7 @@ def measure(torch, csa, w, steps, warmup, cold=True, up_proj=False, timed_steps=
         bwd_res = backward_stage(torch, csa, w, q, k, v, lay, select(), mode, out_dtype)
 
     att_med, sel_med = _q(att_ms, 50), _q(sel_ms, 50)
-    for dom in ("k_bm_attn", "k_tok_attn16", "k_tok_attn", "k_attn_generic"):
+    for dom in ("k_bm_attn", "k_tok_attn16p", "k_tok_attn16", "k_tok_attn", "k_attn_generic"):
         if dom in kern:
             break
     dom_ms = float(np.mean(kern[dom])) if dom in kern else att_med

@@ -33,6 +33,7 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTK = 32;          // gathered keys per tile
@@ -372,7 +373,8 @@ __device__ __forceinline__ float pair32_sum(float v) {
 // output accumulators (128) fit in half a SIMD's register file and two waves share
 // each SIMD: one wave's gather issue and softmax then run under the other's MFMAs
 // (a single wave per SIMD, as with 32 heads a wave, leaves the matrix core idle
-// through both).  Per 32-key tile each wave forms S^T = K Q^T over 18 column steps
+// through both).  This kernel serves 32 and 64 heads a key head (two workgroups a CU
+// at 64); 128 heads take the paired form below.  Per 32-key tile each wave forms S^T = K Q^T over 18 column steps
 // for two 16-key halves, the softmax of its heads, and O^T += V^T P^T with the keys
 // in the order its score accumulators hold them: key k of step position 8 quad + t
 // is 4 quad + t (t < 4) or 16 + 4 quad + t - 4.
@@ -382,11 +384,7 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void k_tok_attn16(Attn
   constexpr int kPitch = DQK + 16;
   constexpr int NKS = DQK / 32;  // score steps
   constexpr int NDB = DV / 16;   // output blocks of 16 columns
-  // With eight waves, waves 4 .. 7 (the second wave on each SIMD) form O^T += V^T P^T
-  // of a tile at the start of the next one, so that one wave's softmax runs under the
-  // other's MFMAs; a tile then stays resident one tile longer (three buffers).
-  constexpr bool kStagger = NW == 8;
-  constexpr int NBUF = kStagger ? 3 : 2;
+  constexpr int NBUF = 2;
   __shared__ __bf16 s_k[NBUF][kTK * kPitch];
   __shared__ int s_keys[3][kTK];
   __shared__ int s_valid[3][kTK];
@@ -411,7 +409,6 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void k_tok_attn16(Attn
     for (int ks = 0; ks < NKS; ++ks)
       qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks + 8 * quad);
   }
-  typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
   f32x4 o[NDB];  // O^T: lane holds head c16, columns 16 db + 4 quad + 0 .. 3
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -447,8 +444,7 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void k_tok_attn16(Attn
   const int ka1 = tile_off<kPitch, 2>(16 + c16, 8 * quad);
   const int va0 = tile_off<kPitch, 2>(4 * quad + (c16 >> 2), 4 * (c16 & 3));
   const int va1 = tile_off<kPitch, 2>(16 + 4 * quad + (c16 >> 2), 4 * (c16 & 3));
-  const bool late = kStagger && wave >= NW / 2;  // wave-uniform
-  bf16x8 pb;  // P^T of the tile (a late wave's: of the previous tile, until its PV)
+  bf16x8 pb;  // P^T of the tile
   // O^T += V^T P^T over tile buffer b.  Value A operand of block db: columns
   // 16 db + c16 of the lane's two key groups, read transposed (lane c16 of a 16-lane
   // group addresses key base + c16 / 4 at column 16 db + 4 (c16 % 4) and receives
@@ -475,7 +471,6 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void k_tok_attn16(Attn
     const int buf = kt % NBUF;
     const int ks3 = kt % 3;
     const int key2 = kt + 2 < n_kt ? load_key(kt + 2) : -1;
-    if (late && kt > 0) pv((kt - 1) % NBUF);
     const char* kb = reinterpret_cast<const char*>(s_k[buf]);
     f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
     {
@@ -513,7 +508,7 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void k_tok_attn16(Attn
     for (int t = 1; t < 8; ++t) mx = fmaxf(mx, x[t]);
     mx = pair32_max(pair16_max(mx)) * c;
     const bool need = mx > m + kLazy || (m == -INFINITY && mx > -INFINITY);
-    if (__any(need)) {  // (a late wave's O already holds the previous tile)
+    if (__any(need)) {
       const float mn = need ? mx : m;
       const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mn);
       l *= alpha;
@@ -532,13 +527,11 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void k_tok_attn16(Attn
       pb[t] = (__bf16)p;
     }
     l += pair32_sum(pair16_sum(rs));
-    if (!late) pv(buf);
+    pv(buf);
     if (kt + 2 < n_kt) store_key(kt + 2, key2);
     __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct loads have landed
     __syncthreads();
   }
-  if (late && n_kt > 0) pv((n_kt - 1) % NBUF);
-  __syncthreads();  // every wave is done with the tiles before the output staging
 
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (a.lse && quad == 0)
@@ -575,20 +568,251 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void k_tok_attn16(Attn
   }
 }
 
+// 128 query heads a key head: waves w and w + 4 (one SIMD) form S^T and the softmax
+// of their own 16 heads as above and publish P (bf16) and their heads' running-maximum
+// factors in LDS; one tile later each of the two forms O^T += V^T P^T for all 32 heads
+// of the pair on 32x32x16 MFMAs, wave w over output columns 0 .. 255 and wave w + 4
+// over 256 .. 511, so that every transposing value read serves 32 heads (half the
+// value reads of 16 heads a wave).  Wave w forms S and the softmax of tile t before
+// the pair's P V of tile t - 1 and wave w + 4 after it, so one wave's softmax runs
+// under the other's MFMAs.
+//   Key order of the P V step st (keys 16 st .. 16 st + 15): lane half h takes keys
+// 16 st + h + 2 j (j < 4) and 16 st + h + 8 + 2 (j - 4): rows two apart start 16
+// banks apart at this pitch, so each 32-lane half of a transposing read covers the 64
+// banks once; P sits in LDS in that order (per step: even keys, then odd keys).
+template <typename TO>
+__global__ __launch_bounds__(512, 1) void k_tok_attn16p(AttnKernelArgs a) {
+  constexpr int DQK = 576, DV = 512, NW = 8;
+  constexpr int kPitch = DQK + 16;
+  constexpr int NKS = DQK / 32;  // score steps
+  constexpr int kPP = 40;        // P row pitch (bf16): 32 key positions + pad
+  __shared__ __bf16 s_k[3][kTK * kPitch];
+  __shared__ __bf16 s_p[2][4][32 * kPP];  // [tile parity][pair][pair head][key position]
+  __shared__ float s_al[2][4][32];        // [tile parity][pair][pair head]: factor
+  __shared__ float s_l[4][32];
+  __shared__ int s_keys[3][kTK];
+  __shared__ int s_valid[3][kTK];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int quad = lane >> 4, c16 = lane & 15, half = lane >> 5;
+  const int pr = wave & 3, side = wave >> 2;  // pair, and which half of the columns
+  const int hcol = 16 * side + c16;           // the lane's own head as a pair column
+  const int hkv = a.k.h;
+  const int i = blockIdx.x / hkv;
+  const int g = blockIdx.x % hkv;
+  const int G = a.q.h / hkv;
+  const int head = g * G + wave * 16 + c16;
+  const RowKeys r = row_keys(a.L, i);
+  const int W = a.idx_width;
+  const int32_t* slots = a.idx + (int64_t)i * W;
+  const float c = a.scale_log2;
+
+  bf16x8 qf[NKS];  // B operands Q^T [32 columns x 16 heads]
+  {
+    const __bf16* qp = elem_ptr<__bf16>(a.q, i, head);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks + 8 * quad);
+  }
+  // O^T of the pair: lane holds pair head lane % 32, columns 256 side + 32 db + 8 (j / 4)
+  // + 4 half + (j % 4)
+  f32x16 o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+
+  const int n_kt = r.valid ? (W + kTK - 1) / kTK : 0;
+  auto load_key = [&](int kt) {
+    const int j = kt * kTK + threadIdx.x;
+    return (threadIdx.x < kTK && j < W) ? slots[j] : -1;
+  };
+  auto store_key = [&](int kt, int key) {
+    if (threadIdx.x < kTK) {
+      const bool ok = key >= r.lo && key <= r.hi;
+      s_keys[kt % 3][threadIdx.x] = ok ? key : r.lo;  // masked slots read a valid row
+      s_valid[kt % 3][threadIdx.x] = ok;
+    }
+  };
+  auto issue = [&](int kt) { issue_tile<DQK, 2>(a.k, g, s_keys[kt % 3], s_k[kt % 3], wave, NW); };
+  if (n_kt > 0) {
+    store_key(0, load_key(0));
+    if (n_kt > 1) store_key(1, load_key(1));
+    __syncthreads();
+    issue(0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // on every path: no wait for the Q loads in the loop
+  __syncthreads();
+  const int ka0 = tile_off<kPitch, 2>(c16, 8 * quad);
+  const int ka1 = tile_off<kPitch, 2>(16 + c16, 8 * quad);
+  // value A operand (V^T [32 columns x 16 keys]) of step st and 32-column block db:
+  // lane c16 of a 16-lane group addresses key 16 st + half + 2 (c16 / 4) (+ 8) at
+  // column 256 side + 32 db + 16 (group % 2) + 4 (c16 % 4), and receives column
+  // ... + c16 of the 4 keys; steps add 16 rows, blocks 64 bytes (the row-bit-2 swap
+  // stays inside the unit's low bit)
+  const int vcol = 256 * side + 16 * ((lane >> 4) & 1) + 4 * (c16 & 3);
+  const int vb0 = tile_off<kPitch, 2>(half + 2 * (c16 >> 2), vcol);
+  const int vb1 = tile_off<kPitch, 2>(8 + half + 2 * (c16 >> 2), vcol);
+  auto pv_pair = [&](int b, int par) {
+    // the pair heads' factors for this tile (1 unless the running maximum moved)
+    const float al = s_al[par][pr][lane & 31];
+    if (__any(al != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[db][j] *= al;
+    }
+    const __bf16* pp = &s_p[par][pr][(lane & 31) * kPP + 8 * half];
+    const bf16x8 pb0 = *reinterpret_cast<const bf16x8*>(pp);
+    const bf16x8 pb1 = *reinterpret_cast<const bf16x8*>(pp + 16);
+    const __bf16* vt = s_k[b];
+    auto vf = [&](int u) {  // u = 8 st + db
+      const int off = (u >> 3) * 16 * kPitch * 2 + 64 * (u & 7);
+      const bf16x4 lo = read_tr(vt, vb0 + off);
+      const bf16x4 hi = read_tr(vt, vb1 + off);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8 vfr[3];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) vfr[u] = vf(u);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (u + 2 < 16) vfr[(u + 2) % 3] = vf(u + 2);
+      o[u & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[u % 3], u < 8 ? pb0 : pb1,
+                                                         o[u & 7], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt % 3;
+    const int par = kt & 1;
+    const int key2 = kt + 2 < n_kt ? load_key(kt + 2) : -1;
+    if (side == 1 && kt > 0) pv_pair((kt - 1) % 3, par ^ 1);
+    const char* kb = reinterpret_cast<const char*>(s_k[buf]);
+    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    {
+      auto kf = [&](int j) {
+        return *reinterpret_cast<const bf16x8*>(kb + ((j & 1) ? ka1 : ka0) + 64 * (j >> 1));
+      };
+      bf16x8 fr[4];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) fr[j] = kf(j);
+#pragma unroll
+      for (int j = 0; j < 2 * NKS; ++j) {
+        if (j + 3 < 2 * NKS) fr[(j + 3) & 3] = kf(j + 3);
+        if (j & 1)
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[j & 3], qf[j >> 1], s1, 0, 0, 0);
+        else
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[j & 3], qf[j >> 1], s0, 0, 0, 0);
+        if (j == 3 && kt + 1 < n_kt) issue(kt + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // softmax of the own heads: lane holds head c16, keys 4 quad + t (s0) and
+    // 16 + 4 quad + t (s1)
+    const uint32_t ok = (uint32_t)(__ballot(s_valid[kt % 3][lane & (kTK - 1)] != 0) >> (4 * quad));
+    float x[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      x[t] = (ok >> t) & 1 ? s0[t] : -INFINITY;
+      x[4 + t] = (ok >> (16 + t)) & 1 ? s1[t] : -INFINITY;
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int t = 1; t < 8; ++t) mx = fmaxf(mx, x[t]);
+    mx = pair32_max(pair16_max(mx)) * c;
+    float al = 1.f;
+    if (mx > m + kLazy || (m == -INFINITY && mx > -INFINITY)) {
+      al = (m == -INFINITY) ? 0.f : exp2f(m - mx);
+      l *= al;
+      m = mx;
+    }
+    const float mu = (m == -INFINITY) ? 0.f : m;
+    float pv[8], rs = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      pv[t] = __builtin_amdgcn_exp2f(fmaf(x[t], c, -mu));
+      rs += pv[t];
+    }
+    l += pair32_sum(pair16_sum(rs));
+    {
+      // key 4 quad + t of a step sits at position 2 quad + t / 2 (t even) or
+      // 8 + 2 quad + t / 2 (t odd)
+      typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+      __bf16* prow = &s_p[par][pr][hcol * kPP + 2 * quad];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const float* q4 = pv + 4 * st;
+        *reinterpret_cast<bf16x2*>(prow + 16 * st) = bf16x2{(__bf16)q4[0], (__bf16)q4[2]};
+        *reinterpret_cast<bf16x2*>(prow + 16 * st + 8) = bf16x2{(__bf16)q4[1], (__bf16)q4[3]};
+      }
+      if (quad == 0) s_al[par][pr][hcol] = al;
+    }
+    if (side == 0 && kt > 0) pv_pair((kt - 1) % 3, par ^ 1);
+    if (kt + 2 < n_kt) store_key(kt + 2, key2);
+    __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct loads have landed
+    __syncthreads();
+  }
+  if (n_kt > 0) pv_pair((n_kt - 1) % 3, (n_kt - 1) & 1);
+  if (quad == 0) s_l[pr][hcol] = l;
+  if (a.lse && quad == 0)
+    a.lse[(int64_t)i * a.q.h + head] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  __syncthreads();  // the pair's row sums; every wave is done with the tiles
+  const float lp = s_l[pr][lane & 31];
+  const float inv = lp > 0.f ? 1.f / lp : 0.f;
+  const int n = lane & 31;
+  const int hout = g * G + 16 * (pr + 4 * (n >> 4)) + (n & 15);  // pair column n's head
+  if constexpr (sizeof(TO) == 2) {
+    // the pair's 32 heads x 128 columns at a time through the (now free) key tiles,
+    // then out as whole 16-byte row pieces
+    constexpr int kPart = 128;
+    constexpr int kRowB = kPart * 2 + 16;
+    static_assert(NW * 32 * kRowB <= (int)sizeof(s_k), "staging fits the key tiles");
+    char* st = reinterpret_cast<char*>(&s_k[0][0]) + wave * 32 * kRowB;
+#pragma unroll
+    for (int pc = 0; pc < 2; ++pc) {
+#pragma unroll
+      for (int db = 4 * pc; db < 4 * pc + 4; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const bf16x4 x4 = {(__bf16)(o[db][4 * jj] * inv), (__bf16)(o[db][4 * jj + 1] * inv),
+                             (__bf16)(o[db][4 * jj + 2] * inv), (__bf16)(o[db][4 * jj + 3] * inv)};
+          *reinterpret_cast<bf16x4*>(st + n * kRowB + (32 * db + 8 * jj + 4 * half - kPart * pc) * 2) = x4;
+        }
+#pragma unroll
+      for (int e0 = 0; e0 < 32 * (kPart / 8); e0 += kWave) {
+        const int rr = (e0 + lane) / (kPart / 8), un = (e0 + lane) % (kPart / 8);
+        const int hr = g * G + 16 * (pr + 4 * (rr >> 4)) + (rr & 15);
+        *reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(a.out) + ((int64_t)i * a.q.h + hr) * DV +
+                                  256 * side + kPart * pc + un * 8) =
+            *reinterpret_cast<const uint4*>(st + rr * kRowB + un * 16);
+      }
+    }
+  } else {
+    float* out = reinterpret_cast<float*>(a.out) + ((int64_t)i * a.q.h + hout) * DV + 256 * side;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<float4*>(out + 32 * db + 8 * jj + 4 * half) =
+            make_float4(o[db][4 * jj] * inv, o[db][4 * jj + 1] * inv, o[db][4 * jj + 2] * inv,
+                        o[db][4 * jj + 3] * inv);
+  }
+}
+
 template <int DQK, int DV, bool ALIAS, typename TO>
 hipError_t launch_shape(const AttnKernelArgs& a, hipStream_t stream) {
   const int G = a.q.h / a.k.h;
   const dim3 grid((unsigned)a.L.n_q * a.k.h);
   int slot;
   constexpr bool k16 = DQK == 576 && DV == 512 && ALIAS;
-  trace_begin(stream, k16 ? "k_tok_attn16" : "k_tok_attn", &slot);
+  trace_begin(stream, !k16 ? "k_tok_attn" : G == 128 ? "k_tok_attn16p" : "k_tok_attn16", &slot);
   if constexpr (k16) {
     if (G == 32)
       hipLaunchKernelGGL((k_tok_attn16<2, TO>), grid, dim3(128), 0, stream, a);
     else if (G == 64)
       hipLaunchKernelGGL((k_tok_attn16<4, TO>), grid, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((k_tok_attn16<8, TO>), grid, dim3(512), 0, stream, a);
+      hipLaunchKernelGGL((k_tok_attn16p<TO>), grid, dim3(512), 0, stream, a);
     trace_end(stream, slot);
     return hipGetLastError();
   }
