@@ -314,15 +314,22 @@ __device__ __forceinline__ void sdp_role(const BwTokArgs& a, SdpLds& s, int i, i
     }
     if (t == n_t) break;
     // row r's piece 2 ks + half sits at (2 ks + half) ^ swq(r): for ks = 4 q + u that is
-    // base u plus 8 q pieces, so four per-lane bases and immediate offsets suffice
+    // base u plus 8 q pieces, so four per-lane bases and immediate offsets suffice.
+    // Fragments sit in a ring of four, read three MFMAs ahead of their use.
     const __bf16* kt = s.k[t & 1] + r * kTQ;
+    auto af = [&](int ks) {
+      return *reinterpret_cast<const bf16x8*>(kt + (((2 * (ks & 3) + half) ^ swq(r)) << 3) +
+                                              64 * (ks >> 2));
+    };
     f32x16 c0 = f32x16{}, c1 = f32x16{};
+    bf16x8 fr[4];
 #pragma unroll
-    for (int ks = 0; ks < NF; ks += 2) {
-      const __bf16* b0 = kt + (((2 * (ks & 3) + half) ^ swq(r)) << 3) + 64 * (ks >> 2);
-      const __bf16* b1 = kt + (((2 * ((ks + 1) & 3) + half) ^ swq(r)) << 3) + 64 * (ks >> 2);
-      c0 = mfma(*reinterpret_cast<const bf16x8*>(b0), f[ks], c0);
-      c1 = mfma(*reinterpret_cast<const bf16x8*>(b1), f[ks + 1], c1);
+    for (int ks = 0; ks < 3; ++ks) fr[ks] = af(ks);
+#pragma unroll
+    for (int ks = 0; ks < NF; ++ks) {
+      if (ks + 3 < NF) fr[(ks + 3) & 3] = af(ks + 3);
+      if (ks & 1) c1 = mfma(fr[ks & 3], f[ks], c1);
+      else c0 = mfma(fr[ks & 3], f[ks], c0);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (SW) {
