@@ -463,14 +463,11 @@ __device__ __forceinline__ int offs(int r, int e) {  // [head][128 slots], 256-b
   return r * kCS + ((((e >> 3) ^ sw256(r))) << 3) + (e & 7);
 }
 
-// dS' and P of the G heads for the 128 slots are staged once and read into each
-// wave's registers (the B operands of its 32 slots); their LDS then holds the
-// double-buffered q / dO chunks and the output tile
+// dS' and P of the G heads for the 128 slots are staged (one after the other) and read
+// into each wave's registers (the B operands of its 32 slots); their LDS then holds
+// the double-buffered q / dO chunks and the output tile
 union CkLds {
-  struct {
-    __bf16 ds[128 * kCS];  // dS' of the group's heads
-    __bf16 p[128 * kCS];   // P
-  } b;
+  __bf16 b[128 * kCS];  // dS', then P, of the group's heads for the 128 slots
   struct {
     __bf16 x[2][128 * kCC];  // a 64-column chunk of the heads' q (chunks 0 .. 8) or dO (9 .. 16)
     __bf16 out[kCS * kCC];   // the chunk's results, slot-major, on their way out
@@ -496,7 +493,7 @@ __device__ __forceinline__ bf16x8 trh(const __bf16* t, int ks, int c0, int lane)
 // one workgroup per (row, key head, 128 slots); wave w takes slots 32 w .. 32 w + 31
 // and both 32-column blocks of every chunk
 template <int G>
-__global__ __launch_bounds__(256, 2) void k_bwtm_ckv(BwTokArgs a) {
+__global__ __launch_bounds__(256, 3) void k_bwtm_ckv(BwTokArgs a) {
   __shared__ CkLds s;
   constexpr int KS = G / 16;  // k-steps over the heads
   const int lane = threadIdx.x & (kWave - 1);
@@ -513,23 +510,25 @@ __global__ __launch_bounds__(256, 2) void k_bwtm_ckv(BwTokArgs a) {
   const __bf16* qb = static_cast<const __bf16*>(a.q.data);
   const __bf16* gb = static_cast<const __bf16*>(a.g16.data);
 
-  // dS' and P of the G heads for the 128 slots: 4 heads per 1 KiB copy
-  for (int c = wave; c < 2 * (G / 4); c += 4) {
-    const int tn = c / (G / 4), m = c % (G / 4);
-    const int hh = 4 * m + lane / 16, pp = lane % 16;
-    const __bf16* src = (tn == 0 ? a.ds : a.pb) + ((int64_t)i * hq + h0 + hh) * a.wpad + kCS * st +
-                        8 * (pp ^ sw256(hh));
-    gather16_addr(src,
-                  __builtin_amdgcn_readfirstlane(lds_addr(tn == 0 ? s.b.ds : s.b.p) + 1024 * m));
-  }
-  wait_gathers();
-  __syncthreads();
+  // dS', then P, of the G heads for the 128 slots (4 heads per 1 KiB copy) through one
+  // 32 KiB area, so that the workgroup's LDS stays at 48 KiB (three workgroups a CU)
+  auto stage = [&](const __bf16* src0) {
+    for (int m = wave; m < G / 4; m += 4) {
+      const int hh = 4 * m + lane / 16, pp = lane % 16;
+      const __bf16* src = src0 + ((int64_t)i * hq + h0 + hh) * a.wpad + kCS * st + 8 * (pp ^ sw256(hh));
+      gather16_addr(src, __builtin_amdgcn_readfirstlane(lds_addr(s.b) + 1024 * m));
+    }
+    wait_gathers();
+    __syncthreads();
+  };
   bf16x8 bd[KS], bp[KS];  // B operands [heads 16 ks .. x the wave's 32 slots]
+  stage(a.ds);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    bd[ks] = trh<true>(s.b.ds, ks, 32 * wave, lane);
-    bp[ks] = trh<true>(s.b.p, ks, 32 * wave, lane);
-  }
+  for (int ks = 0; ks < KS; ++ks) bd[ks] = trh<true>(s.b, ks, 32 * wave, lane);
+  __syncthreads();
+  stage(a.pb);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) bp[ks] = trh<true>(s.b, ks, 32 * wave, lane);
   __syncthreads();
   // chunk c of the heads' q (c < 9) or dO rows: 8 heads per 1 KiB copy
   auto copy_chunk = [&](int c) {
