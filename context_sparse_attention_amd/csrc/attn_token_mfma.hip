@@ -387,7 +387,7 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void k_tok_attn16(Attn
   constexpr int NBUF = 2;
   __shared__ __bf16 s_k[NBUF][kTK * kPitch];
   __shared__ int s_keys[3][kTK];
-  __shared__ int s_valid[3][kTK];
+  __shared__ __align__(16) float s_bias[3][kTK];  // 0: permitted key; -inf: masked slot
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int quad = lane >> 4, c16 = lane & 15;
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void k_tok_attn16(Attn
     if (threadIdx.x < kTK) {
       const bool ok = key >= r.lo && key <= r.hi;
       s_keys[kt % 3][threadIdx.x] = ok ? key : r.lo;  // masked slots read a valid row
-      s_valid[kt % 3][threadIdx.x] = ok;
+      s_bias[kt % 3][threadIdx.x] = ok ? 0.f : -INFINITY;
     }
   };
   auto issue = [&](int kt) { issue_tile<DQK, 2>(a.k, g, s_keys[kt % 3], s_k[kt % NBUF], wave, NW); };
@@ -472,7 +472,10 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void k_tok_attn16(Attn
     const int ks3 = kt % 3;
     const int key2 = kt + 2 < n_kt ? load_key(kt + 2) : -1;
     const char* kb = reinterpret_cast<const char*>(s_k[buf]);
-    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    // the scores start from the slots' bias: a masked slot's score is -inf exactly
+    // (its key row is a valid one, so every product is finite)
+    f32x4 s0 = *reinterpret_cast<const f32x4*>(&s_bias[ks3][4 * quad]);
+    f32x4 s1 = *reinterpret_cast<const f32x4*>(&s_bias[ks3][16 + 4 * quad]);
     {
       // MFMA j = 2 ks + half takes the key fragment of rows 16 half + c16 at step ks;
       // fragments sit in a ring of four, read three MFMAs ahead of their use
@@ -493,15 +496,12 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void k_tok_attn16(Attn
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // lane: head c16, keys 4 quad + t (s0) and 16 + 4 quad + t (s1).  Bit k of the
-    // ballot: slot k of the tile selects a permitted key; shifted so that bit t is
-    // key 4 quad + t
-    const uint32_t ok = (uint32_t)(__ballot(s_valid[ks3][lane & (kTK - 1)] != 0) >> (4 * quad));
+    // lane: head c16, keys 4 quad + t (s0) and 16 + 4 quad + t (s1)
     float x[8];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      x[t] = (ok >> t) & 1 ? s0[t] : -INFINITY;
-      x[4 + t] = (ok >> (16 + t)) & 1 ? s1[t] : -INFINITY;
+      x[t] = s0[t];
+      x[4 + t] = s1[t];
     }
     float mx = x[0];
 #pragma unroll
@@ -591,7 +591,7 @@ __global__ __launch_bounds__(512, 1) void k_tok_attn16p(AttnKernelArgs a) {
   __shared__ float s_al[2][4][32];        // [tile parity][pair][pair head]: factor
   __shared__ float s_l[4][32];
   __shared__ int s_keys[3][kTK];
-  __shared__ int s_valid[3][kTK];
+  __shared__ __align__(16) float s_bias[3][kTK];  // 0: permitted key; -inf: masked slot
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int quad = lane >> 4, c16 = lane & 15, half = lane >> 5;
@@ -630,7 +630,7 @@ __global__ __launch_bounds__(512, 1) void k_tok_attn16p(AttnKernelArgs a) {
     if (threadIdx.x < kTK) {
       const bool ok = key >= r.lo && key <= r.hi;
       s_keys[kt % 3][threadIdx.x] = ok ? key : r.lo;  // masked slots read a valid row
-      s_valid[kt % 3][threadIdx.x] = ok;
+      s_bias[kt % 3][threadIdx.x] = ok ? 0.f : -INFINITY;
     }
   };
   auto issue = [&](int kt) { issue_tile<DQK, 2>(a.k, g, s_keys[kt % 3], s_k[kt % 3], wave, NW); };
@@ -688,7 +688,9 @@ __global__ __launch_bounds__(512, 1) void k_tok_attn16p(AttnKernelArgs a) {
     const int key2 = kt + 2 < n_kt ? load_key(kt + 2) : -1;
     if (side == 1 && kt > 0) pv_pair((kt - 1) % 3, par ^ 1);
     const char* kb = reinterpret_cast<const char*>(s_k[buf]);
-    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    // scores start from the slots' bias (masked slot: -inf)
+    f32x4 s0 = *reinterpret_cast<const f32x4*>(&s_bias[buf][4 * quad]);
+    f32x4 s1 = *reinterpret_cast<const f32x4*>(&s_bias[buf][16 + 4 * quad]);
     {
       auto kf = [&](int j) {
         return *reinterpret_cast<const bf16x8*>(kb + ((j & 1) ? ka1 : ka0) + 64 * (j >> 1));
@@ -709,12 +711,11 @@ __global__ __launch_bounds__(512, 1) void k_tok_attn16p(AttnKernelArgs a) {
     }
     // softmax of the own heads: lane holds head c16, keys 4 quad + t (s0) and
     // 16 + 4 quad + t (s1)
-    const uint32_t ok = (uint32_t)(__ballot(s_valid[kt % 3][lane & (kTK - 1)] != 0) >> (4 * quad));
     float x[8];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      x[t] = (ok >> t) & 1 ? s0[t] : -INFINITY;
-      x[4 + t] = (ok >> (16 + t)) & 1 ? s1[t] : -INFINITY;
+      x[t] = s0[t];
+      x[4 + t] = s1[t];
     }
     float mx = x[0];
 #pragma unroll
