@@ -22,6 +22,8 @@
 // stay bounded by 2^8 in between), so the 16 x Dv/32 accumulators are rarely
 // rescaled.  Chunk summaries merge exactly as in "Context parallel attention:
 // exchange keys and merge softmax globally" (chunk summary paragraph).
+#include <type_traits>
+
 #include "attention.hpp"
 #include "gather.hpp"
 #include "mfma.hpp"
@@ -573,9 +575,10 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void k_tok_attn16(Attn
 // factors in LDS; one tile later each of the two forms O^T += V^T P^T for all 32 heads
 // of the pair on 32x32x16 MFMAs, wave w over output columns 0 .. 255 and wave w + 4
 // over 256 .. 511, so that every transposing value read serves 32 heads (half the
-// value reads of 16 heads a wave).  Wave w forms S and the softmax of tile t before
-// the pair's P V of tile t - 1 and wave w + 4 after it, so one wave's softmax runs
-// under the other's MFMAs.
+// value reads of 16 heads a wave).  Both waves form S and the softmax of tile t and
+// then the pair's P V of tile t - 1, except that wave w + 4 runs the first kPre of
+// the 16 P V steps before its scores: the small offset keeps the two waves' softmaxes
+// apart (a whole P V ahead, or none, measured slower).
 //   Key order of the P V step st (keys 16 st .. 16 st + 15): lane half h takes keys
 // 16 st + h + 2 j (j < 4) and 16 st + h + 8 + 2 (j - 4): rows two apart start 16
 // banks apart at this pitch, so each 32-lane half of a transposing read covers the 64
@@ -586,6 +589,7 @@ __global__ __launch_bounds__(512, 1) void k_tok_attn16p(AttnKernelArgs a) {
   constexpr int kPitch = DQK + 16;
   constexpr int NKS = DQK / 32;  // score steps
   constexpr int kPP = 40;        // P row pitch (bf16): 32 key positions + pad
+  constexpr int kPre = 4;        // P V steps wave w + 4 runs before its scores
   __shared__ __bf16 s_k[3][kTK * kPitch];
   __shared__ __bf16 s_p[2][4][32 * kPP];  // [tile parity][pair][pair head][key position]
   __shared__ float s_al[2][4][32];        // [tile parity][pair][pair head]: factor
@@ -652,10 +656,13 @@ __global__ __launch_bounds__(512, 1) void k_tok_attn16p(AttnKernelArgs a) {
   const int vcol = 256 * side + 16 * ((lane >> 4) & 1) + 4 * (c16 & 3);
   const int vb0 = tile_off<kPitch, 2>(half + 2 * (c16 >> 2), vcol);
   const int vb1 = tile_off<kPitch, 2>(8 + half + 2 * (c16 >> 2), vcol);
-  auto pv_pair = [&](int b, int par) {
+  // P V steps [U0, U1) of the 16 (step u: keys 16 (u / 8) .., output block u % 8); the
+  // accumulators are rescaled by the part that starts at step 0
+  auto pv_steps = [&](int b, int par, auto U0c, auto U1c) {
+    constexpr int U0 = decltype(U0c)::value, U1 = decltype(U1c)::value;
     // the pair heads' factors for this tile (1 unless the running maximum moved)
     const float al = s_al[par][pr][lane & 31];
-    if (__any(al != 1.f)) {
+    if (U0 == 0 && __any(al != 1.f)) {
 #pragma unroll
       for (int db = 0; db < 8; ++db)
 #pragma unroll
@@ -673,20 +680,23 @@ __global__ __launch_bounds__(512, 1) void k_tok_attn16p(AttnKernelArgs a) {
     };
     bf16x8 vfr[3];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) vfr[u] = vf(u);
+    for (int u = U0; u < U0 + 2 && u < U1; ++u) vfr[u % 3] = vf(u);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      if (u + 2 < 16) vfr[(u + 2) % 3] = vf(u + 2);
+    for (int u = U0; u < U1; ++u) {
+      if (u + 2 < U1) vfr[(u + 2) % 3] = vf(u + 2);
       o[u & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[u % 3], u < 8 ? pb0 : pb1,
                                                          o[u & 7], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  const std::integral_constant<int, 0> first;
+  const std::integral_constant<int, kPre> pre;
+  const std::integral_constant<int, 16> all;
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt % 3;
     const int par = kt & 1;
     const int key2 = kt + 2 < n_kt ? load_key(kt + 2) : -1;
-    if (side == 1 && kt > 0) pv_pair((kt - 1) % 3, par ^ 1);
+    if (side == 1 && kt > 0) pv_steps((kt - 1) % 3, par ^ 1, first, pre);
     const char* kb = reinterpret_cast<const char*>(s_k[buf]);
     // scores start from the slots' bias (masked slot: -inf)
     f32x4 s0 = *reinterpret_cast<const f32x4*>(&s_bias[buf][4 * quad]);
@@ -748,12 +758,13 @@ __global__ __launch_bounds__(512, 1) void k_tok_attn16p(AttnKernelArgs a) {
       }
       if (quad == 0) s_al[par][pr][hcol] = al;
     }
-    if (side == 0 && kt > 0) pv_pair((kt - 1) % 3, par ^ 1);
+    if (side == 0 && kt > 0) pv_steps((kt - 1) % 3, par ^ 1, first, all);
+    if (side == 1 && kt > 0) pv_steps((kt - 1) % 3, par ^ 1, pre, all);
     if (kt + 2 < n_kt) store_key(kt + 2, key2);
     __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct loads have landed
     __syncthreads();
   }
-  if (n_kt > 0) pv_pair((n_kt - 1) % 3, (n_kt - 1) & 1);
+  if (n_kt > 0) pv_steps((n_kt - 1) % 3, (n_kt - 1) & 1, first, all);
   if (quad == 0) s_l[pr][hcol] = l;
   if (a.lse && quad == 0)
     a.lse[(int64_t)i * a.q.h + head] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
