@@ -701,6 +701,9 @@ __global__ __launch_bounds__(512, 1) void k_tok_attn16p(AttnKernelArgs a) {
     // scores start from the slots' bias (masked slot: -inf)
     f32x4 s0 = *reinterpret_cast<const f32x4*>(&s_bias[buf][4 * quad]);
     f32x4 s1 = *reinterpret_cast<const f32x4*>(&s_bias[buf][16 + 4 * quad]);
+    // the score loop runs at a raised wave priority: where both waves of a SIMD can
+    // issue, the one feeding score MFMAs goes first (~1% faster than equal priority)
+    __builtin_amdgcn_s_setprio(1);
     {
       auto kf = [&](int j) {
         return *reinterpret_cast<const bf16x8*>(kb + ((j & 1) ? ka1 : ka0) + 64 * (j >> 1));
@@ -719,6 +722,7 @@ __global__ __launch_bounds__(512, 1) void k_tok_attn16p(AttnKernelArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // softmax of the own heads: lane holds head c16, keys 4 quad + t (s0) and
     // 16 + 4 quad + t (s1)
     float x[8];
