@@ -207,8 +207,10 @@ def _mla_slots(rng, pos, n_kv, width, hot, hot_slot):
 
 @pytest.mark.parametrize("hq", [64, 128])
 def test_token_mla_widths_edge_cases(hq):
-    """Absorbed-MLA widths (16 heads a wave; at 128 heads the second wave on each
-    SIMD forms P V one tile late): caller-made selections of 1, 5, 33 and 97 slots
+    """Absorbed-MLA widths (16 heads a wave; at 128 heads the two waves of a SIMD
+    share P and form P V one tile late, one of them starting a few steps of it
+    before its scores): caller-made selections of 1, 5, 33 and 97 slots (one to
+    four 32-key tiles)
     with pads, repeats, future keys and rows without keys, and a key whose score
     dwarfs the rest in the third tile, so that the running maximum moves after
     the first tile; bf16 and f32 outputs, and the result repeats bit for bit."""
