@@ -25,6 +25,10 @@
 //   k_bwd_fill   each wave places its index rows one at a time, in order (a
 //                row's entries in one list are its repeated slots, whose order
 //                does not change any sum)
+// Wide index rows (token mode) with at most kLdsLists lists take one workgroup
+// per range instead, with the counts and cursors in LDS (k_bwd_hist_lds,
+// k_bwd_fill_lds): the same counts, offsets and list order without a global
+// atomic per entry.
 // bf16 block mode with D in {64, 128} and one index row per query head runs the
 // matrix-core kernels of attn_backward_mfma.hip over these lists; every other
 // case runs k_bwd_dq / k_bwd_dkdv below, fp32 on the vector ALUs (exact bf16
@@ -163,6 +167,74 @@ __global__ __launch_bounds__(kBwThreads) void k_bwd_fill(BwArgs a) {
     // every cursor update of this index row has returned before the next row's
     // are issued (and the compiler moves no memory access across this point)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+}
+
+// Lists whose counts and cursors one workgroup keeps in LDS (64 KiB), and the
+// number of ranges (workgroups) the index rows are cut into on that path.
+constexpr int kLdsLists = 16384;
+constexpr int kLdsRanges = 512;
+
+// One workgroup per range: its index rows' entry counts per list, counted in
+// LDS, then stored into the (zeroed) count table where not zero.
+__global__ __launch_bounds__(kBwThreads) void k_bwd_hist_lds(BwArgs a) {
+  extern __shared__ int s_cnt[];
+  const int r = blockIdx.x;
+  for (int c = threadIdx.x; c < a.n_lists; c += kBwThreads) s_cnt[c] = 0;
+  __syncthreads();
+  const int64_t n_rows = (int64_t)a.L.n_q * a.idx_heads;
+  const int64_t e0 = (int64_t)r * a.rows_per_range;
+  const int64_t e1 = min(n_rows, e0 + a.rows_per_range);
+  for (int64_t e = e0; e < e1; ++e) {
+    const int i = (int)(e / a.idx_heads), hi = (int)(e % a.idx_heads);
+    const RowKeys rk = row_keys(a.L, i);
+    const int32_t* slots = a.idx + e * a.idx_width;
+    for (int s = threadIdx.x; s < a.idx_width; s += kBwThreads) {
+      const int c = slot_list(a, rk, hi, slots[s]);
+      if (c >= 0) atomicAdd(&s_cnt[c], 1);
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < a.n_lists; c += kBwThreads) {
+    const int v = s_cnt[c];
+    if (v) a.hist[(int64_t)c * a.R + r] = v;
+  }
+}
+
+// One workgroup per range: the cursors of the lists its rows touch come from
+// the scanned table into LDS; then its index rows are placed one at a time,
+// with a barrier between rows, so every list holds ascending index-row ids
+// (within a row, a list's entries are its repeated slots).
+__global__ __launch_bounds__(kBwThreads) void k_bwd_fill_lds(BwArgs a) {
+  extern __shared__ int s_cur[];
+  const int r = blockIdx.x;
+  for (int c = threadIdx.x; c < a.n_lists; c += kBwThreads) s_cur[c] = -1;
+  __syncthreads();
+  const int64_t n_rows = (int64_t)a.L.n_q * a.idx_heads;
+  const int64_t e0 = (int64_t)r * a.rows_per_range;
+  const int64_t e1 = min(n_rows, e0 + a.rows_per_range);
+  for (int64_t e = e0; e < e1; ++e) {  // mark the lists this range touches
+    const int i = (int)(e / a.idx_heads), hi = (int)(e % a.idx_heads);
+    const RowKeys rk = row_keys(a.L, i);
+    const int32_t* slots = a.idx + e * a.idx_width;
+    for (int s = threadIdx.x; s < a.idx_width; s += kBwThreads) {
+      const int c = slot_list(a, rk, hi, slots[s]);
+      if (c >= 0) s_cur[c] = 0;
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < a.n_lists; c += kBwThreads)
+    if (s_cur[c] == 0) s_cur[c] = a.hist[(int64_t)c * a.R + r];
+  __syncthreads();
+  for (int64_t e = e0; e < e1; ++e) {
+    const int i = (int)(e / a.idx_heads), hi = (int)(e % a.idx_heads);
+    const RowKeys rk = row_keys(a.L, i);
+    const int32_t* slots = a.idx + e * a.idx_width;
+    for (int s = threadIdx.x; s < a.idx_width; s += kBwThreads) {
+      const int c = slot_list(a, rk, hi, slots[s]);
+      if (c >= 0) a.entries[atomicAdd(&s_cur[c], 1)] = (int32_t)(e * a.idx_width + s);
+    }
+    __syncthreads();  // this row's positions are taken before the next row's
   }
 }
 
@@ -462,6 +534,7 @@ __global__ __launch_bounds__(kBwThreads) void k_bwd_dkdv(BwArgs a, int gdt) {
 struct BwLayout {
   int n_lists, R, rows_per_range, n_tiles;
   int64_t n_hist, n_entries;
+  bool lds_lists;      // counts and cursors in LDS, one workgroup per range
   bool mfma;           // block mode on the matrix cores
   int64_t max_tiles;   // its dQ chunks
   int64_t n_part;      // its dQ partials (floats)
@@ -479,10 +552,13 @@ BwLayout bw_layout(int n_q, int n_kv, int n_blocks, int mode, int dtype, int hq,
   const int64_t chunks = mode == CSA_SEL_TOKEN ? n_kv : n_blocks;
   b.n_lists = (int)((idx_heads == 1 ? 1 : hkv) * chunks);
   const int64_t n_rows = (int64_t)n_q * idx_heads;
-  // ranges (one per wave): enough to fill the chip, the count table within 2^24
+  // ranges: one per wave, enough to fill the chip, the count table within 2^24; or,
+  // with the counts in LDS, one per workgroup, kLdsRanges of them
+  b.lds_lists = b.n_lists <= kLdsLists && idx_width >= kBwThreads;
   int64_t R = std::max<int64_t>(1, std::min<int64_t>((1 << 24) / std::max(1, b.n_lists),
                                                      (n_rows + 3) / 4));
   R = std::min<int64_t>(R, 1 << 16);
+  if (b.lds_lists) R = std::max<int64_t>(1, std::min<int64_t>(kLdsRanges, n_rows));
   b.rows_per_range = (int)std::max<int64_t>(1, (n_rows + R - 1) / R);
   b.R = (int)std::max<int64_t>(1, (n_rows + b.rows_per_range - 1) / b.rows_per_range);
   b.n_hist = (int64_t)b.n_lists * b.R;
@@ -613,9 +689,15 @@ hipError_t launch_attn_backward(const AttnBwdArgs& x, hipStream_t stream) {
                        stream, a, x.o_dtype, x.dout_dtype);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  // wide index rows: counts and cursors in LDS, one workgroup per range
+  const bool lds_lists = b.lds_lists;
+  const size_t lds_bytes = (size_t)b.n_lists * sizeof(int);
   if (pairs > 0) {
-    hipLaunchKernelGGL(k_bwd_hist, dim3(grid_for(b.R, kBwWaves)), dim3(kBwThreads), 0, stream,
-                       a);
+    if (lds_lists)
+      hipLaunchKernelGGL(k_bwd_hist_lds, dim3(b.R), dim3(kBwThreads), lds_bytes, stream, a);
+    else
+      hipLaunchKernelGGL(k_bwd_hist, dim3(grid_for(b.R, kBwWaves)), dim3(kBwThreads), 0,
+                         stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (b.n_tiles > 0) {
@@ -629,8 +711,11 @@ hipError_t launch_attn_backward(const AttnBwdArgs& x, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (pairs > 0) {
-    hipLaunchKernelGGL(k_bwd_fill, dim3(grid_for(b.R, kBwWaves)), dim3(kBwThreads), 0, stream,
-                       a);
+    if (lds_lists)
+      hipLaunchKernelGGL(k_bwd_fill_lds, dim3(b.R), dim3(kBwThreads), lds_bytes, stream, a);
+    else
+      hipLaunchKernelGGL(k_bwd_fill, dim3(grid_for(b.R, kBwWaves)), dim3(kBwThreads), 0,
+                         stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (b.tok) {
