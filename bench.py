@@ -537,7 +537,12 @@ def measure(torch, csa, w, steps, warmup, cold=True, up_proj=False, timed_steps=
                              "traffic": measured_traffic(dom, w.name)},
         "select_call": {"ms_median": sel_med, "ms_p10": _q(sel_ms, 10),
                         "ms_p90": _q(sel_ms, 90), "alg_bytes": sel_bytes["total"],
-                        "GBs": sel_gbs, "frac_hbm": sel_gbs / PEAK_HBM_GBS},
+                        "GBs": sel_gbs, "frac_hbm": sel_gbs / PEAK_HBM_GBS,
+                        # the block selection is bound by HBM; the token indexer's
+                        # call by its MFMA logits (flops / call time / bf16 peak)
+                        "bound": "hbm" if w.mode == "block" else "mfma",
+                        "frac": (sel_gbs / PEAK_HBM_GBS if w.mode == "block" else
+                                 sel_bytes["indexer_flops"] / (sel_med * 1e-3) / 1e12 / peak)},
         "select_kernel": {"kernel": sk, "ms": sk_ms, "rate": sk_rate, "unit": sk_unit,
                           "frac": sk_rate / sk_peak},
         "kernels_ms": {k_: float(np.mean(v_)) for k_, v_ in kern.items()},
