@@ -194,6 +194,39 @@ def test_token_backward_per_head_index_with_pads_and_repeats():
     _compare(w, idx_np, got[3], got[:3], TOL["bf16"], "token per-head")
 
 
+@pytest.mark.parametrize("per_head", [False, True])
+def test_token_backward_wide_rows(per_head):
+    """Index rows of 256 slots or more build the key lists with their counts and
+    cursors in LDS (one workgroup per range of rows): the absorbed-MLA shape on the
+    matrix cores with a shared index row, and per-head rows with pads, future keys
+    and repeated slots on the general kernels; gradients against the oracle, and a
+    second call repeats them bit for bit."""
+    if per_head:
+        w = tiny_token_workload(seed=69, hq=8, dqk=64, dv=64, lengths=(600,), dtype="bf16")
+        rng = np.random.default_rng(69)
+        idx_np = rng.integers(-5, w.n_kv + 5, size=(w.n_q, w.hq, 300)).astype(np.int32)
+        idx_np[:, :, 7] = idx_np[:, :, 3]
+        idx = torch.from_numpy(idx_np).cuda()
+        family = "generic"
+    else:
+        w = tiny_token_workload(seed=70, hq=32, dqk=576, dv=512, hi=8, di=128, topk=280,
+                                lengths=(400,), dtype="bf16")
+        rng = np.random.default_rng(70)
+        d0 = upload(w)
+        idx = csa.dsa_indexer_topk(d0["iq"], d0["ik"], d0["w"], d0["layout"], w.topk)
+        idx_np = idx.cpu().numpy()[:, None, :]
+        family = "token_mfma"
+    _say("token backward wide rows", "per-head" if per_head else "shared")
+    d = upload(w)
+    assert _family(w, d, idx) == family
+    dout = rng.standard_normal((w.n_q, w.hq, w.dv))
+    got = _fwd_bwd(w, d, idx, dout)
+    again = _fwd_bwd(w, d, idx, dout)
+    for name, a, b in zip(("dq", "dk", "dv"), got[:3], again[:3]):
+        assert np.array_equal(a, b), f"{name} differs between two calls"
+    _compare(w, idx_np, got[3], got[:3], TOL["bf16"], "token wide rows")
+
+
 def test_backward_is_bitwise_reproducible():
     w = tiny_block_workload(seed=68, layout="all", lengths=(1000, 537), hq=8, hkv=2, d=128,
                             block=64, topk=3, dtype="bf16")
