@@ -25,10 +25,11 @@
 //   k_bwd_fill   each wave places its index rows one at a time, in order (a
 //                row's entries in one list are its repeated slots, whose order
 //                does not change any sum)
-// Wide index rows (token mode) with at most kLdsLists lists take one workgroup
-// per range instead, with the counts and cursors in LDS (k_bwd_hist_lds,
-// k_bwd_fill_lds): the same counts, offsets and list order without a global
-// atomic per entry.
+// With at most kLdsLists lists, one workgroup per range takes the place of the
+// waves, with the counts and cursors in LDS: the same counts, offsets and list
+// order without a global atomic per entry.  Wide index rows (token mode) go row by
+// row (k_bwd_hist_lds, k_bwd_fill_lds), narrow ones (block mode) in flat batches
+// of entries (k_bwd_hist_flat, k_bwd_fill_flat).
 // bf16 block mode with D in {64, 128} and one index row per query head runs the
 // matrix-core kernels of attn_backward_mfma.hip over these lists; every other
 // case runs k_bwd_dq / k_bwd_dkdv below, fp32 on the vector ALUs (exact bf16
@@ -235,6 +236,74 @@ __global__ __launch_bounds__(kBwThreads) void k_bwd_fill_lds(BwArgs a) {
       if (c >= 0) a.entries[atomicAdd(&s_cur[c], 1)] = (int32_t)(e * a.idx_width + s);
     }
     __syncthreads();  // this row's positions are taken before the next row's
+  }
+}
+
+// The range's entries in flat order (index row * width + slot): entry f of row
+// e = f / width, slot f % width, and its list (-1 when it selects no permitted
+// key).
+__device__ __forceinline__ int entry_list(const BwArgs& a, int64_t f) {
+  const int64_t e = f / a.idx_width;
+  const int i = (int)(e / a.idx_heads), hi = (int)(e % a.idx_heads);
+  return slot_list(a, row_keys(a.L, i), hi, a.idx[f]);
+}
+
+// Narrow index rows: one workgroup per range over its entries in flat order,
+// counted in LDS, then stored into the (zeroed) count table where not zero.
+__global__ __launch_bounds__(kBwThreads) void k_bwd_hist_flat(BwArgs a) {
+  extern __shared__ int s_cnt[];
+  const int r = blockIdx.x;
+  for (int c = threadIdx.x; c < a.n_lists; c += kBwThreads) s_cnt[c] = 0;
+  __syncthreads();
+  const int64_t n_rows = (int64_t)a.L.n_q * a.idx_heads;
+  const int64_t f0 = (int64_t)r * a.rows_per_range * a.idx_width;
+  const int64_t f1 = min(n_rows, (int64_t)(r + 1) * a.rows_per_range) * a.idx_width;
+  for (int64_t f = f0 + threadIdx.x; f < f1; f += kBwThreads) {
+    const int c = entry_list(a, f);
+    if (c >= 0) atomicAdd(&s_cnt[c], 1);
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < a.n_lists; c += kBwThreads) {
+    const int v = s_cnt[c];
+    if (v) a.hist[(int64_t)c * a.R + r] = v;
+  }
+}
+
+// One workgroup per range: the cursors of the lists its entries touch come from
+// the scanned table into LDS; then the entries are placed kBwThreads at a time in
+// flat order. Within a batch an entry's place is its list's cursor plus the number
+// of earlier entries of the batch in the same list, so every list holds ascending
+// flat slot ids; the cursors then advance by the batch's counts.
+__global__ __launch_bounds__(kBwThreads) void k_bwd_fill_flat(BwArgs a) {
+  extern __shared__ int s_cur[];
+  __shared__ int s_c[kBwThreads];
+  const int r = blockIdx.x;
+  for (int c = threadIdx.x; c < a.n_lists; c += kBwThreads) s_cur[c] = -1;
+  __syncthreads();
+  const int64_t n_rows = (int64_t)a.L.n_q * a.idx_heads;
+  const int64_t f0 = (int64_t)r * a.rows_per_range * a.idx_width;
+  const int64_t f1 = min(n_rows, (int64_t)(r + 1) * a.rows_per_range) * a.idx_width;
+  for (int64_t f = f0 + threadIdx.x; f < f1; f += kBwThreads) {  // mark the touched lists
+    const int c = entry_list(a, f);
+    if (c >= 0) s_cur[c] = 0;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < a.n_lists; c += kBwThreads)
+    if (s_cur[c] == 0) s_cur[c] = a.hist[(int64_t)c * a.R + r];
+  __syncthreads();
+  for (int64_t fb = f0; fb < f1; fb += kBwThreads) {
+    const int64_t f = fb + threadIdx.x;
+    const int c = f < f1 ? entry_list(a, f) : -1;
+    s_c[threadIdx.x] = c;
+    __syncthreads();
+    if (c >= 0) {
+      int rank = 0;
+      for (int t = 0; t < (int)threadIdx.x; ++t) rank += s_c[t] == c;
+      a.entries[s_cur[c] + rank] = (int32_t)f;
+    }
+    __syncthreads();  // every cursor read before any advance
+    if (c >= 0) atomicAdd(&s_cur[c], 1);
+    __syncthreads();
   }
 }
 
@@ -554,7 +623,7 @@ BwLayout bw_layout(int n_q, int n_kv, int n_blocks, int mode, int dtype, int hq,
   const int64_t n_rows = (int64_t)n_q * idx_heads;
   // ranges: one per wave, enough to fill the chip, the count table within 2^24; or,
   // with the counts in LDS, one per workgroup, kLdsRanges of them
-  b.lds_lists = b.n_lists <= kLdsLists && idx_width >= kBwThreads;
+  b.lds_lists = b.n_lists <= kLdsLists;
   int64_t R = std::max<int64_t>(1, std::min<int64_t>((1 << 24) / std::max(1, b.n_lists),
                                                      (n_rows + 3) / 4));
   R = std::min<int64_t>(R, 1 << 16);
@@ -693,8 +762,10 @@ hipError_t launch_attn_backward(const AttnBwdArgs& x, hipStream_t stream) {
   const bool lds_lists = b.lds_lists;
   const size_t lds_bytes = (size_t)b.n_lists * sizeof(int);
   if (pairs > 0) {
-    if (lds_lists)
+    if (lds_lists && x.idx_width >= kBwThreads)
       hipLaunchKernelGGL(k_bwd_hist_lds, dim3(b.R), dim3(kBwThreads), lds_bytes, stream, a);
+    else if (lds_lists)
+      hipLaunchKernelGGL(k_bwd_hist_flat, dim3(b.R), dim3(kBwThreads), lds_bytes, stream, a);
     else
       hipLaunchKernelGGL(k_bwd_hist, dim3(grid_for(b.R, kBwWaves)), dim3(kBwThreads), 0,
                          stream, a);
@@ -711,8 +782,10 @@ hipError_t launch_attn_backward(const AttnBwdArgs& x, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (pairs > 0) {
-    if (lds_lists)
+    if (lds_lists && x.idx_width >= kBwThreads)
       hipLaunchKernelGGL(k_bwd_fill_lds, dim3(b.R), dim3(kBwThreads), lds_bytes, stream, a);
+    else if (lds_lists)
+      hipLaunchKernelGGL(k_bwd_fill_flat, dim3(b.R), dim3(kBwThreads), lds_bytes, stream, a);
     else
       hipLaunchKernelGGL(k_bwd_fill, dim3(grid_for(b.R, kBwWaves)), dim3(kBwThreads), 0,
                          stream, a);
