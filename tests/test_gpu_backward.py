@@ -227,6 +227,25 @@ def test_token_backward_wide_rows(per_head):
     _compare(w, idx_np, got[3], got[:3], TOL["bf16"], "token wide rows")
 
 
+def test_token_backward_many_keys_global_lists():
+    """More keys than one workgroup's LDS holds counts for (17000 > 16384 lists): the
+    key lists are built by the wave-per-range kernels with global atomics, and the
+    gradients still match the oracle and repeat bit for bit."""
+    pos = np.arange(17000 - 64, 17000, dtype=np.int32)
+    w = tiny_token_workload(seed=71, lengths=(17000,), positions=pos, hq=4, dqk=64, dv=64,
+                            hi=4, di=32, topk=37, dtype="bf16")
+    _say("token backward global lists")
+    d = upload(w)
+    idx = csa.dsa_indexer_topk(d["iq"], d["ik"], d["w"], d["layout"], w.topk)
+    assert _family(w, d, idx) == "generic"
+    dout = np.random.default_rng(71).standard_normal((w.n_q, w.hq, w.dv))
+    got = _fwd_bwd(w, d, idx, dout)
+    again = _fwd_bwd(w, d, idx, dout)
+    for name, a, b in zip(("dq", "dk", "dv"), got[:3], again[:3]):
+        assert np.array_equal(a, b), f"{name} differs between two calls"
+    _compare(w, idx.cpu().numpy()[:, None, :], got[3], got[:3], TOL["bf16"], "global lists")
+
+
 def test_backward_is_bitwise_reproducible():
     w = tiny_block_workload(seed=68, layout="all", lengths=(1000, 537), hq=8, hkv=2, d=128,
                             block=64, topk=3, dtype="bf16")
