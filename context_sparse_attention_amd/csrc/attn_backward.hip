@@ -27,9 +27,9 @@
 //                does not change any sum)
 // With at most kLdsLists lists, one workgroup per range takes the place of the
 // waves, with the counts and cursors in LDS: the same counts, offsets and list
-// order without a global atomic per entry.  Wide index rows (token mode) go row by
-// row (k_bwd_hist_lds, k_bwd_fill_lds), narrow ones (block mode) in flat batches
-// of entries (k_bwd_hist_flat, k_bwd_fill_flat).
+// order (up to a row's repeated slots) without a global atomic per entry.  Index
+// rows of at least kBwThreads slots go row by row (k_bwd_hist_lds, k_bwd_fill_lds),
+// shorter ones in flat batches of entries (k_bwd_hist_flat, k_bwd_fill_flat).
 // bf16 block mode with D in {64, 128} and one index row per query head runs the
 // matrix-core kernels of attn_backward_mfma.hip over these lists; every other
 // case runs k_bwd_dq / k_bwd_dkdv below, fp32 on the vector ALUs (exact bf16
